@@ -1,0 +1,128 @@
+"""Byte formula of the packed int4 weight layout (the specification).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+"Enabling Dynamic Sparsity in Quantized LLM Inference" (Abstract) calls for
+a quantization layout that is consistent with activation sparsity and
+improves GPU memory locality, but does not give the pattern.  This layout is
+our own reading of that requirement: the output dimension is cut into tiles
+of ``tile_n`` rows, and for every tile and every input index k the
+``tile_n`` 4-bit codes of that column are one contiguous run of tile_n/2
+bytes, so a single active input index costs exactly one contiguous read per
+tile and an inactive one costs nothing.  Scales and zero-points live in a
+separate region, one contiguous run of tile_n (scale, zero) pairs per tile
+and group.
+
+Blob = header (256 bytes) | weight region | metadata region, little-endian:
+
+  header  0: b"SGV1"           4: u32 version = 1
+          8: i32 N            12: i32 K        16: i32 group = 128
+         20: i32 tile_n       24: u64 w_off    32: u64 w_bytes
+         40: u64 m_off        48: u64 m_bytes  56: u64 total_bytes
+         64..255: zero
+  w_off = 256, w_bytes = N*K/2,   m_off = w_off + roundup(w_bytes, 256),
+  m_bytes = (K/128)*N*4,          total = m_off + roundup(m_bytes, 256)
+
+  weight byte  w_off + (t*K + k)*(tile_n/2) + j
+               = q[t*tile_n + 2j][k] | q[t*tile_n + 2j + 1][k] << 4
+  metadata     m_off + ((t*(K/128) + g)*tile_n + i)*4 : fp16 bits of
+               s[t*tile_n + i][g], then fp16 bits of z[t*tile_n + i][g]
+
+for tiles t < N/tile_n, columns k < K, bytes j < tile_n/2, groups g < K/128
+and rows i < tile_n.  Padding bytes are zero.
+"""
+from __future__ import annotations
+
+import struct
+
+import numpy as np
+
+GROUP = 128
+HEADER_BYTES = 256
+MAGIC = b"SGV1"
+VERSION = 1
+
+
+def _roundup(v: int, a: int) -> int:
+    return (v + a - 1) // a * a
+
+
+def header_fields(N: int, K: int, tile_n: int) -> dict:
+    w_off = HEADER_BYTES
+    w_bytes = N * K // 2
+    m_off = w_off + _roundup(w_bytes, 256)
+    m_bytes = (K // GROUP) * N * 4
+    total = m_off + _roundup(m_bytes, 256)
+    return dict(N=N, K=K, group=GROUP, tile_n=tile_n, w_off=w_off,
+                w_bytes=w_bytes, m_off=m_off, m_bytes=m_bytes, total_bytes=total)
+
+
+def _check(q, s_bits, z_bits, tile_n):
+    q = np.asarray(q, dtype=np.uint8)
+    N, K = q.shape
+    if K % GROUP or K <= 0 or N <= 0:
+        raise ValueError("K must be a positive multiple of 128")
+    if tile_n < 64 or tile_n > 1024 or tile_n & (tile_n - 1) or N % tile_n:
+        raise ValueError("tile_n must be a power of two in [64, 1024] dividing N")
+    if q.max(initial=0) > 15:
+        raise ValueError("codes must be 4-bit")
+    s_bits = np.asarray(s_bits, dtype=np.uint16)
+    z_bits = np.asarray(z_bits, dtype=np.uint16)
+    if s_bits.shape != (N, K // GROUP) or z_bits.shape != (N, K // GROUP):
+        raise ValueError("scale/zero shape must be [N][K/128]")
+    return q, s_bits, z_bits, N, K
+
+
+def pack_spec(q, s_bits, z_bits, tile_n: int) -> np.ndarray:
+    """Return the blob (uint8 array) for codes ``q`` [N][K] and fp16 bit
+    patterns ``s_bits``, ``z_bits`` [N][K/128]."""
+    q, s_bits, z_bits, N, K = _check(q, s_bits, z_bits, tile_n)
+    h = header_fields(N, K, tile_n)
+    blob = np.zeros(h["total_bytes"], dtype=np.uint8)
+    head = (MAGIC + struct.pack("<I", VERSION)
+            + struct.pack("<iiii", N, K, GROUP, tile_n)
+            + struct.pack("<QQQQQ", h["w_off"], h["w_bytes"], h["m_off"],
+                          h["m_bytes"], h["total_bytes"]))
+    blob[:len(head)] = np.frombuffer(head, dtype=np.uint8)
+
+    T = N // tile_n
+    # q[t*tile_n + i][k] viewed as [t][k][i]
+    qt = q.reshape(T, tile_n, K).transpose(0, 2, 1)
+    byte = qt[:, :, 0::2] | (qt[:, :, 1::2] << 4)          # [t][k][j]
+    blob[h["w_off"]:h["w_off"] + h["w_bytes"]] = byte.reshape(-1)
+
+    Gk = K // GROUP
+    pair = np.empty((T, Gk, tile_n, 2), dtype=np.uint16)     # [t][g][i][s|z]
+    pair[..., 0] = s_bits.reshape(T, tile_n, Gk).transpose(0, 2, 1)
+    pair[..., 1] = z_bits.reshape(T, tile_n, Gk).transpose(0, 2, 1)
+    blob[h["m_off"]:h["m_off"] + h["m_bytes"]] = \
+        pair.astype("<u2").reshape(-1).view(np.uint8)
+    return blob
+
+
+def read_header(blob) -> dict:
+    b = bytes(np.asarray(blob, dtype=np.uint8)[:64])
+    if b[:4] != MAGIC:
+        raise ValueError("bad magic")
+    version, = struct.unpack_from("<I", b, 4)
+    N, K, G, tile_n = struct.unpack_from("<iiii", b, 8)
+    w_off, w_bytes, m_off, m_bytes, total = struct.unpack_from("<QQQQQ", b, 24)
+    return dict(version=version, N=N, K=K, group=G, tile_n=tile_n, w_off=w_off,
+                w_bytes=w_bytes, m_off=m_off, m_bytes=m_bytes, total_bytes=total)
+
+
+def unpack_spec(blob):
+    """Inverse of ``pack_spec``: returns (q, s_bits, z_bits, header)."""
+    blob = np.asarray(blob, dtype=np.uint8)
+    h = read_header(blob)
+    N, K, tile_n = h["N"], h["K"], h["tile_n"]
+    T, Gk = N // tile_n, K // GROUP
+    byte = blob[h["w_off"]:h["w_off"] + h["w_bytes"]].reshape(T, K, tile_n // 2)
+    qt = np.empty((T, K, tile_n), dtype=np.uint8)
+    qt[:, :, 0::2] = byte & 0x0F
+    qt[:, :, 1::2] = byte >> 4
+    q = qt.transpose(0, 2, 1).reshape(N, K)
+    pair = blob[h["m_off"]:h["m_off"] + h["m_bytes"]].view("<u2").reshape(T, Gk, tile_n, 2)
+    s_bits = pair[..., 0].transpose(0, 2, 1).reshape(N, Gk).astype(np.uint16)
+    z_bits = pair[..., 1].transpose(0, 2, 1).reshape(N, Gk).astype(np.uint16)
+    return np.ascontiguousarray(q), s_bits, z_bits, h

@@ -1,0 +1,49 @@
+"""Input generator checks (CPU): quantizer error bound, code ranges, seeds,
+thresholds that realise the requested sparsity."""
+import numpy as np
+
+import synth
+from tests.oracle_pins import f16_table
+
+
+def test_quantizer_bounds():
+    W = synth.normal_f32(1, (64, 1024), 0.02)
+    W[3, :128] = 0.0                      # a zero group
+    W[5, 128:256] = 0.01                  # a constant positive group
+    q, s, z = synth.quantize_int4_g128(W)
+    F = f16_table()
+    assert q.dtype == np.uint8 and q.max() <= 15
+    zf = F[z]
+    assert np.all(zf == np.rint(zf)) and zf.min() >= 0 and zf.max() <= 15
+    sf = F[s]
+    assert np.all(sf > 0)
+    g = np.arange(1024) // 128
+    What = sf[:, g] * (q.astype(np.float64) - zf[:, g])
+    err = np.abs(W.astype(np.float64) - What)
+    assert np.all(err <= sf[:, g] * (0.5 + 2 ** -9) + 1e-12)
+    assert np.all(What[3, :128] == 0.0)
+
+
+def test_seeds_reproducible():
+    a = synth.glu_activation(0, 2048)
+    b = synth.glu_activation(0, 2048)
+    assert a.dtype == np.float16 and np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    assert not np.array_equal(synth.glu_activation(1, 2048), a)
+
+
+def test_percentile_threshold_sparsity():
+    x = synth.glu_activation(0, 14336)
+    for p in (0.5, 0.7, 0.9):
+        t = synth.percentile_threshold(x, p)
+        kept = np.count_nonzero(np.abs(x.astype(np.float32)) >= np.float32(t))
+        realised = 1 - kept / x.size
+        assert realised <= p + 1e-12 and realised >= p - 0.01
+    assert synth.percentile_threshold(x, 0.0) == 0.0
+
+
+def test_workloads():
+    for name in ("single-2048", "down-14336", "layer-8b", "mlp-70b", "batched-14336"):
+        wl = synth.workload(name)
+        for p in wl.projections:
+            assert p.K % 128 == 0 and p.N % 512 == 0
+            assert p.input_name in wl.inputs
