@@ -1,0 +1,144 @@
+// Host packer for the sparsity-aware int4 layout (no HIP calls).
+//
+// The layout answers the page's call ("Enabling Dynamic Sparsity in
+// Quantized LLM Inference", Abstract) for a quantized-weight arrangement
+// that agrees with activation sparsity and keeps GPU reads local.  For each
+// tile of tile_n outputs, the tile_n codes of one input column k sit in one
+// contiguous run of tile_n/2 bytes (even row in the low nibble), so a GEMV
+// that skips inactive inputs reads whole 256-byte runs and nothing else.
+// Scales and zero-points of one (tile, group) pair are one contiguous run
+// of tile_n (s, z) fp16 pairs.  The byte formula is documented in sgemv.h.
+#include "sgemv.h"
+
+#include <cstring>
+
+namespace {
+
+constexpr uint64_t kHeader = 256;
+
+uint64_t roundup(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+bool fp16_is_finite(uint16_t b) { return (b & 0x7C00u) != 0x7C00u; }
+
+// Value of an fp16 bit pattern when it is an integer in 0..15, else -1.
+int fp16_small_int(uint16_t b) {
+    if (b == 0x0000u || b == 0x8000u) return 0;
+    if (b & 0x8000u) return -1;
+    const int e = (b >> 10) & 0x1F;  // biased exponent
+    const int m = b & 0x3FF;
+    if (e < 15 || e > 18) return -1;  // value outside [1, 16)
+    const int shift = 10 - (e - 15);  // mantissa bits below the binary point
+    if (m & ((1 << shift) - 1)) return -1;
+    return (1 << (e - 15)) | (m >> shift);
+}
+
+}  // namespace
+
+extern "C" int sgemv_layout_fill_desc(int32_t N, int32_t K, int32_t tile_n, sgemv_desc* d) {
+    d->N = N;
+    d->K = K;
+    d->group = SGEMV_GROUP;
+    d->tile_n = tile_n;
+    d->w_off = kHeader;
+    d->w_bytes = (uint64_t)N * (uint64_t)K / 2;
+    d->m_off = d->w_off + roundup(d->w_bytes, 256);
+    d->m_bytes = (uint64_t)(K / SGEMV_GROUP) * (uint64_t)N * 4;
+    d->total_bytes = d->m_off + roundup(d->m_bytes, 256);
+    return SGEMV_OK;
+}
+
+static int check_shape(int32_t N, int32_t K, int32_t group, int32_t tile_n) {
+    if (group != SGEMV_GROUP) return SGEMV_EINVAL;
+    if (N <= 0 || K <= 0 || K % SGEMV_GROUP || K > SGEMV_MAX_K || N > SGEMV_MAX_N)
+        return SGEMV_ESIZE;
+    if (tile_n < 64 || tile_n > 1024 || (tile_n & (tile_n - 1)) || N % tile_n)
+        return SGEMV_ESIZE;
+    return SGEMV_OK;
+}
+
+extern "C" int sgemv_pack_layout(const uint8_t* q, const uint16_t* scales_f16,
+                                 const uint16_t* zeros_f16, int32_t N, int32_t K,
+                                 int32_t group, int32_t tile_n, void* out,
+                                 size_t out_capacity, sgemv_desc* desc_out) {
+    int st = check_shape(N, K, group, tile_n);
+    if (st) return st;
+    sgemv_desc d;
+    sgemv_layout_fill_desc(N, K, tile_n, &d);
+    if (!out) {  // size query
+        if (desc_out) *desc_out = d;
+        return SGEMV_OK;
+    }
+    if (!q || !scales_f16 || !zeros_f16) return SGEMV_EINVAL;
+    if (out_capacity < d.total_bytes) return SGEMV_ESIZE;
+
+    const int32_t Gk = K / SGEMV_GROUP;
+    // Validate every input before writing anything.
+    for (uint64_t i = 0, e = (uint64_t)N * K; i < e; ++i)
+        if (q[i] > 15) return SGEMV_EINVAL;
+    for (uint64_t i = 0, e = (uint64_t)N * Gk; i < e; ++i) {
+        if (!fp16_is_finite(scales_f16[i])) return SGEMV_EINVAL;
+        if (fp16_small_int(zeros_f16[i]) < 0) return SGEMV_EINVAL;
+    }
+
+    uint8_t* blob = static_cast<uint8_t*>(out);
+    std::memset(blob, 0, d.total_bytes);
+    // header (little-endian host assumed: x86-64 and the GPU are both LE)
+    std::memcpy(blob + 0, "SGV1", 4);
+    const uint32_t version = 1;
+    std::memcpy(blob + 4, &version, 4);
+    const int32_t hv[4] = {N, K, SGEMV_GROUP, tile_n};
+    std::memcpy(blob + 8, hv, 16);
+    const uint64_t ho[5] = {d.w_off, d.w_bytes, d.m_off, d.m_bytes, d.total_bytes};
+    std::memcpy(blob + 24, ho, 40);
+
+    // weights: tile t, column k -> tile_n/2 contiguous bytes
+    const int32_t T = N / tile_n;
+    const int32_t half = tile_n / 2;
+    uint8_t* wr = blob + d.w_off;
+    for (int32_t t = 0; t < T; ++t) {
+        const uint8_t* qt = q + (uint64_t)t * tile_n * K;
+        for (int32_t j = 0; j < half; ++j) {
+            const uint8_t* r0 = qt + (uint64_t)(2 * j) * K;      // even row
+            const uint8_t* r1 = r0 + K;                          // odd row
+            uint8_t* dst = wr + (uint64_t)t * K * half + j;
+            for (int32_t k = 0; k < K; ++k)
+                dst[(uint64_t)k * half] = (uint8_t)(r0[k] | (r1[k] << 4));
+        }
+    }
+    // metadata: tile t, group g -> tile_n (s, z) pairs
+    uint16_t* md = reinterpret_cast<uint16_t*>(blob + d.m_off);
+    for (int32_t t = 0; t < T; ++t)
+        for (int32_t i = 0; i < tile_n; ++i) {
+            const uint64_t n = (uint64_t)t * tile_n + i;
+            for (int32_t g = 0; g < Gk; ++g) {
+                const uint64_t o = (((uint64_t)t * Gk + g) * tile_n + i) * 2;
+                md[o] = scales_f16[n * Gk + g];
+                md[o + 1] = zeros_f16[n * Gk + g];
+            }
+        }
+    if (desc_out) *desc_out = d;
+    return SGEMV_OK;
+}
+
+extern "C" int sgemv_desc_from_header(const void* header, size_t bytes, sgemv_desc* desc_out) {
+    if (!header || !desc_out) return SGEMV_EINVAL;
+    if (bytes < 64) return SGEMV_ESIZE;
+    const uint8_t* h = static_cast<const uint8_t*>(header);
+    if (std::memcmp(h, "SGV1", 4) != 0) return SGEMV_EINVAL;
+    uint32_t version;
+    std::memcpy(&version, h + 4, 4);
+    if (version != 1) return SGEMV_EINVAL;
+    int32_t hv[4];
+    std::memcpy(hv, h + 8, 16);
+    int st = check_shape(hv[0], hv[1], hv[2], hv[3]);
+    if (st) return SGEMV_EINVAL;
+    uint64_t ho[5];
+    std::memcpy(ho, h + 24, 40);
+    sgemv_desc d;
+    sgemv_layout_fill_desc(hv[0], hv[1], hv[3], &d);
+    if (ho[0] != d.w_off || ho[1] != d.w_bytes || ho[2] != d.m_off ||
+        ho[3] != d.m_bytes || ho[4] != d.total_bytes)
+        return SGEMV_EINVAL;
+    *desc_out = d;
+    return SGEMV_OK;
+}

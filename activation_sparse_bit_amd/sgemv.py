@@ -1,0 +1,214 @@
+"""Python binding of libsgemv.so: argument marshalling only.
+
+Every step of the GEMV runs in the HIP library; this module converts torch
+tensors and NumPy arrays to pointers and sizes, passes the current HIP
+stream, and turns status codes into exceptions.  PyTorch is used for device
+memory and streams only.  The names match the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libsgemv.so")
+
+SGEMV_OK = 0
+SGEMV_EINVAL = -1
+SGEMV_ESIZE = -2
+SGEMV_EALIGN = -3
+SGEMV_EUNSUPPORTED = -4
+SGEMV_EHIP = -5
+SGEMV_OUT_F32 = 1
+SGEMV_GROUP = 128
+SGEMV_TILE_N = 512
+SGEMV_MAX_BATCH = 16
+
+EXPORTED = ["sgemv_pack_layout", "sgemv_desc_from_header", "sgemv_gather_indices",
+            "sgemv_run", "sgemv_run_batched", "sgemv_workspace_bytes",
+            "sgemv_strerror", "sgemv_last_hip_error"]
+
+
+class SgemvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {strerror(status)} ({status})")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("K", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("tile_n", ctypes.c_int32), ("w_off", ctypes.c_uint64),
+                ("w_bytes", ctypes.c_uint64), ("m_off", ctypes.c_uint64),
+                ("m_bytes", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64)]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib():
+    """Load libsgemv.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    pd = ctypes.POINTER(Desc)
+    L.sgemv_pack_layout.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, sz, pd]
+    L.sgemv_pack_layout.restype = ctypes.c_int
+    L.sgemv_desc_from_header.argtypes = [vp, sz, pd]
+    L.sgemv_desc_from_header.restype = ctypes.c_int
+    L.sgemv_gather_indices.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
+    L.sgemv_gather_indices.restype = ctypes.c_int
+    L.sgemv_run.argtypes = [pd, vp, vp, vp, vp, vp, u32, vp, vp]
+    L.sgemv_run.restype = ctypes.c_int
+    L.sgemv_run_batched.argtypes = [pd, vp, vp, i32, i32, vp, vp, vp, vp, i32, u32, vp, vp]
+    L.sgemv_run_batched.restype = ctypes.c_int
+    L.sgemv_workspace_bytes.argtypes = [pd, i32]
+    L.sgemv_workspace_bytes.restype = sz
+    L.sgemv_strerror.argtypes = [ctypes.c_int]
+    L.sgemv_strerror.restype = ctypes.c_char_p
+    L.sgemv_last_hip_error.argtypes = []
+    L.sgemv_last_hip_error.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().sgemv_strerror(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != SGEMV_OK:
+        raise SgemvError(status, what)
+
+
+def _ptr(t):
+    """Address of a torch tensor, a NumPy array, or None."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _thresholds(t, M):
+    if t is None:
+        return None
+    arr = np.ascontiguousarray(np.asarray(t, dtype=np.float32).reshape(-1))
+    if arr.size == 1 and M > 1:
+        arr = np.repeat(arr, M)
+    if arr.size != M:
+        raise ValueError("one threshold per row")
+    return arr
+
+
+# ---------------------------------------------------------------------------
+# the four calls
+# ---------------------------------------------------------------------------
+def sgemv_pack_layout(q, scales_f16, zeros_f16, tile_n: int = SGEMV_TILE_N):
+    """Pack int4 codes q (uint8 [N][K]) and fp16 bit patterns of scales and
+    zero-points (uint16 [N][K/128]) into a blob.  Returns (Desc, uint8 blob)."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(scales_f16)
+    z = np.ascontiguousarray(zeros_f16)
+    if s.dtype == np.float16:
+        s = s.view(np.uint16)
+    if z.dtype == np.float16:
+        z = z.view(np.uint16)
+    s = np.ascontiguousarray(s, dtype=np.uint16)
+    z = np.ascontiguousarray(z, dtype=np.uint16)
+    N, K = q.shape
+    if s.shape != (N, K // SGEMV_GROUP) or z.shape != (N, K // SGEMV_GROUP):
+        raise ValueError("scales/zeros must be [N][K/128]")
+    d = Desc()
+    _check(lib().sgemv_pack_layout(None, None, None, N, K, SGEMV_GROUP, tile_n, None, 0,
+                                   ctypes.byref(d)), "sgemv_pack_layout(size)")
+    blob = np.empty(d.total_bytes, dtype=np.uint8)
+    _check(lib().sgemv_pack_layout(_ptr(q), _ptr(s), _ptr(z), N, K, SGEMV_GROUP, tile_n,
+                                   _ptr(blob), blob.nbytes, ctypes.byref(d)),
+           "sgemv_pack_layout")
+    return d, blob
+
+
+def sgemv_desc_from_header(blob) -> Desc:
+    b = np.ascontiguousarray(np.asarray(blob, dtype=np.uint8)[:64])
+    d = Desc()
+    _check(lib().sgemv_desc_from_header(_ptr(b), b.nbytes, ctypes.byref(d)),
+           "sgemv_desc_from_header")
+    return d
+
+
+def sgemv_gather_indices(x, thresholds, idx, count, K: int | None = None, stream=None):
+    """x: fp16 device tensor [K] or [M][ldx]; writes idx (int32 [K]) and
+    count (int32 [1]) on the device."""
+    M = 1 if x.dim() == 1 else x.shape[0]
+    ldx = x.shape[-1] if x.dim() == 1 else x.stride(0)
+    K = x.shape[-1] if K is None else K
+    t = _thresholds(thresholds, M)
+    _check(lib().sgemv_gather_indices(_ptr(x), M, K, ldx, _ptr(t), _ptr(idx), _ptr(count),
+                                      _stream(stream)), "sgemv_gather_indices")
+
+
+def _flags(y):
+    import torch
+    if y.dtype == torch.float32:
+        return SGEMV_OUT_F32
+    if y.dtype == torch.float16:
+        return 0
+    raise TypeError("y must be float16 or float32")
+
+
+def sgemv_run(desc: Desc, packed, x, idx, count, y, workspace, stream=None):
+    """y = W . x over idx[:count] (idx None: all columns)."""
+    _check(lib().sgemv_run(ctypes.byref(desc), _ptr(packed), _ptr(x), _ptr(idx), _ptr(count),
+                           _ptr(y), _flags(y), _ptr(workspace), _stream(stream)), "sgemv_run")
+
+
+def sgemv_run_batched(desc: Desc, packed, x, thresholds, idx, count, y, workspace, stream=None):
+    """y[m] = W . xe[m] over the union list; x is [M][ldx], y is [M][ldy]."""
+    M = x.shape[0]
+    t = _thresholds(thresholds, M)
+    _check(lib().sgemv_run_batched(ctypes.byref(desc), _ptr(packed), _ptr(x), M, x.stride(0),
+                                   _ptr(t), _ptr(idx), _ptr(count), _ptr(y), y.stride(0),
+                                   _flags(y), _ptr(workspace), _stream(stream)),
+           "sgemv_run_batched")
+
+
+def sgemv_workspace_bytes(desc: Desc, M: int = 1) -> int:
+    return int(lib().sgemv_workspace_bytes(ctypes.byref(desc), M))
+
+
+def sgemv_last_hip_error() -> int:
+    return int(lib().sgemv_last_hip_error())
+
+
+# ---------------------------------------------------------------------------
+# convenience: device buffers for one matrix
+# ---------------------------------------------------------------------------
+class PackedMatrix:
+    """A packed matrix on the device with its workspace (torch tensors)."""
+
+    def __init__(self, q, scales_f16, zeros_f16, device="cuda", max_batch: int = SGEMV_MAX_BATCH):
+        import torch
+        self.desc, blob = sgemv_pack_layout(q, scales_f16, zeros_f16)
+        self.blob = torch.from_numpy(blob).to(device)
+        self.workspace = torch.zeros(max(sgemv_workspace_bytes(self.desc, max_batch), 256),
+                                     dtype=torch.uint8, device=device)
+        self.N, self.K = self.desc.N, self.desc.K

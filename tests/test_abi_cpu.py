@@ -1,0 +1,190 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+the host packer matches the layout specification byte for byte, and every
+argument check fires before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from activation_sparse_bit_amd import sgemv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "sgemv.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(sgemv_[a-z_]+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    L = sgemv.lib()
+    names = declared_functions()
+    assert set(names) == set(sgemv.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+@pytest.mark.parametrize("N,K,tile", [(512, 128, 512), (1024, 384, 512), (512, 256, 64),
+                                      (2048, 256, 1024), (256, 512, 256), (4096, 1024, 512)])
+def test_packer_matches_spec(N, K, tile):
+    q, s, z = synth.random_int4_problem(N * 7 + K, N, K)
+    d, blob = sgemv.sgemv_pack_layout(q, s, z, tile)
+    ref = oracle.pack_spec(q, s, z, tile)
+    assert blob.shape == ref.shape and np.array_equal(blob, ref)
+    h = oracle.header_fields(N, K, tile)
+    for k, v in h.items():
+        assert getattr(d, k) == v, k
+    d2 = sgemv.sgemv_desc_from_header(blob)
+    assert d2.as_dict() == d.as_dict()
+
+
+def test_packer_quantized_weights():
+    q, s, z = synth.quantized_weights(3, 1024, 2048, 0.02)
+    d, blob = sgemv.sgemv_pack_layout(q, s, z)
+    assert np.array_equal(blob, oracle.pack_spec(q, s, z, 512))
+
+
+def _pack_raw(q, s, z, N, K, group=128, tile=512, cap=None):
+    L = sgemv.lib()
+    d = sgemv.Desc()
+    if cap is None:
+        cap = oracle.header_fields(N, K, tile)["total_bytes"] if K % 128 == 0 and N % tile == 0 else 0
+    out = np.zeros(max(cap, 1), dtype=np.uint8)
+    return L.sgemv_pack_layout(q.ctypes.data if q is not None else None,
+                               s.ctypes.data if s is not None else None,
+                               z.ctypes.data if z is not None else None,
+                               N, K, group, tile, out.ctypes.data, cap, ctypes.byref(d))
+
+
+def test_packer_errors():
+    N, K = 512, 256
+    q, s, z = synth.random_int4_problem(1, N, K)
+    assert _pack_raw(q, s, z, N, K) == sgemv.SGEMV_OK
+    assert _pack_raw(None, s, z, N, K) == sgemv.SGEMV_EINVAL
+    assert _pack_raw(q, s, z, N, K, group=64) == sgemv.SGEMV_EINVAL
+    assert _pack_raw(q, s, z, N, 200) == sgemv.SGEMV_ESIZE
+    assert _pack_raw(q, s, z, N, K, tile=384) == sgemv.SGEMV_ESIZE
+    assert _pack_raw(q, s, z, N, K, tile=2048) == sgemv.SGEMV_ESIZE
+    assert _pack_raw(q, s, z, 300, K, tile=64) == sgemv.SGEMV_ESIZE
+    assert _pack_raw(q, s, z, N, K, cap=1000) == sgemv.SGEMV_ESIZE
+    bad = q.copy(); bad[5, 7] = 16
+    assert _pack_raw(bad, s, z, N, K) == sgemv.SGEMV_EINVAL
+    badz = z.copy(); badz[1, 1] = np.float16(2.5).view(np.uint16)
+    assert _pack_raw(q, s, badz, N, K) == sgemv.SGEMV_EINVAL
+    badz[1, 1] = np.float16(16.0).view(np.uint16)
+    assert _pack_raw(q, s, badz, N, K) == sgemv.SGEMV_EINVAL
+    badz[1, 1] = np.float16(-1.0).view(np.uint16)
+    assert _pack_raw(q, s, badz, N, K) == sgemv.SGEMV_EINVAL
+    bads = s.copy(); bads[0, 0] = 0x7C00
+    assert _pack_raw(q, bads, z, N, K) == sgemv.SGEMV_EINVAL
+    # every integer zero-point 0..15, including -0, is accepted
+    okz = np.tile(np.arange(16, dtype=np.float16).view(np.uint16), (N * (K // 128)) // 16 + 1)[:N * (K // 128)].reshape(N, K // 128).copy()
+    okz[0, 0] = 0x8000
+    assert _pack_raw(q, s, okz, N, K) == sgemv.SGEMV_OK
+
+
+def test_desc_from_header_rejects():
+    q, s, z = synth.random_int4_problem(2, 512, 128)
+    d, blob = sgemv.sgemv_pack_layout(q, s, z)
+    for off, val in ((0, 0x58), (4, 2), (24, 0x10)):
+        b = blob.copy(); b[off] = val
+        with pytest.raises(sgemv.SgemvError):
+            sgemv.sgemv_desc_from_header(b)
+
+
+def _desc(N=4096, K=14336, tile=512):
+    d = sgemv.Desc()
+    L = sgemv.lib()
+    assert L.sgemv_pack_layout(None, None, None, N, K, 128, tile, None, 0, ctypes.byref(d)) == 0
+    return d
+
+
+FAKE = 1 << 20  # a well-aligned address that is never dereferenced: every call below fails validation
+
+
+def test_gather_validation():
+    L = sgemv.lib()
+    t = np.array([0.5] * 16, dtype=np.float32)
+    tp = t.ctypes.data
+    E = sgemv
+    assert L.sgemv_gather_indices(None, 1, 2048, 2048, tp, FAKE, FAKE, None) == E.SGEMV_EINVAL
+    assert L.sgemv_gather_indices(FAKE, 1, 2048, 2048, None, FAKE, FAKE, None) == E.SGEMV_EINVAL
+    assert L.sgemv_gather_indices(FAKE, 0, 2048, 2048, tp, FAKE, FAKE, None) == E.SGEMV_ESIZE
+    assert L.sgemv_gather_indices(FAKE, 17, 2048, 2048, tp, FAKE, FAKE, None) == E.SGEMV_ESIZE
+    assert L.sgemv_gather_indices(FAKE, 1, 2000, 2048, tp, FAKE, FAKE, None) == E.SGEMV_ESIZE
+    assert L.sgemv_gather_indices(FAKE, 1, 131072, 131072, tp, FAKE, FAKE, None) == E.SGEMV_ESIZE
+    assert L.sgemv_gather_indices(FAKE, 2, 2048, 2000, tp, FAKE, FAKE, None) == E.SGEMV_ESIZE
+    assert L.sgemv_gather_indices(FAKE, 2, 2048, 2052, tp, FAKE, FAKE, None) == E.SGEMV_EALIGN
+    assert L.sgemv_gather_indices(FAKE + 2, 1, 2048, 2048, tp, FAKE, FAKE, None) == E.SGEMV_EALIGN
+    for bad in (np.nan, -0.25, np.inf):
+        tb = np.array([bad], dtype=np.float32)
+        assert L.sgemv_gather_indices(FAKE, 1, 2048, 2048, tb.ctypes.data, FAKE, FAKE, None) == E.SGEMV_EINVAL
+
+
+def test_run_validation():
+    L = sgemv.lib()
+    E = sgemv
+    d = _desc()
+    pd = ctypes.byref(d)
+    assert L.sgemv_run(None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == E.SGEMV_EINVAL
+    assert L.sgemv_run(pd, None, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == E.SGEMV_EINVAL
+    assert L.sgemv_run(pd, FAKE, None, FAKE, FAKE, FAKE, 0, FAKE, None) == E.SGEMV_EINVAL
+    assert L.sgemv_run(pd, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, None) == E.SGEMV_EINVAL
+    assert L.sgemv_run(pd, FAKE, FAKE, FAKE, None, FAKE, 0, FAKE, None) == E.SGEMV_EINVAL
+    assert L.sgemv_run(pd, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, None) == E.SGEMV_EINVAL
+    assert L.sgemv_run(pd, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, None) == E.SGEMV_EINVAL
+    assert L.sgemv_run(pd, FAKE + 16, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == E.SGEMV_EALIGN
+    assert L.sgemv_run(pd, FAKE, FAKE + 2, FAKE, FAKE, FAKE, 0, FAKE, None) == E.SGEMV_EALIGN
+    assert L.sgemv_run(pd, FAKE, FAKE, FAKE, FAKE, FAKE + 4, 0, FAKE, None) == E.SGEMV_EALIGN
+    assert L.sgemv_run(pd, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE + 64, None) == E.SGEMV_EALIGN
+    # a description the kernels do not run, and inconsistent ones
+    d2 = _desc(N=4096, K=14336, tile=256)
+    assert L.sgemv_run(ctypes.byref(d2), FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == E.SGEMV_EUNSUPPORTED
+    d3 = _desc(); d3.m_off += 256
+    assert L.sgemv_run(ctypes.byref(d3), FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == E.SGEMV_EINVAL
+    d4 = _desc(); d4.group = 64
+    assert L.sgemv_run(ctypes.byref(d4), FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == E.SGEMV_EINVAL
+
+
+def test_run_batched_validation():
+    L = sgemv.lib()
+    E = sgemv
+    d = _desc()
+    pd = ctypes.byref(d)
+    t = np.array([0.5] * 16, dtype=np.float32)
+    tp = t.ctypes.data
+    K, N = d.K, d.N
+    assert L.sgemv_run_batched(pd, FAKE, FAKE, 0, K, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_ESIZE
+    assert L.sgemv_run_batched(pd, FAKE, FAKE, 17, K, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_ESIZE
+    assert L.sgemv_run_batched(pd, FAKE, FAKE, 4, K - 8, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_ESIZE
+    assert L.sgemv_run_batched(pd, FAKE, FAKE, 4, K, tp, FAKE, FAKE, FAKE, N - 8, 0, FAKE, None) == E.SGEMV_ESIZE
+    assert L.sgemv_run_batched(pd, FAKE, FAKE, 4, K + 4, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_EALIGN
+    assert L.sgemv_run_batched(pd, FAKE, FAKE, 4, K, tp, FAKE, FAKE, FAKE, N + 4, 0, FAKE, None) == E.SGEMV_EALIGN
+    tb = np.array([0.5, np.nan, 0.5, 0.5], dtype=np.float32)
+    assert L.sgemv_run_batched(pd, FAKE, FAKE, 4, K, tb.ctypes.data, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_EINVAL
+    tb = np.array([0.5, 0.5, -1.0, 0.5], dtype=np.float32)
+    assert L.sgemv_run_batched(pd, FAKE, FAKE, 4, K, tb.ctypes.data, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_EINVAL
+
+
+def test_workspace_bytes():
+    d = _desc()
+    w1 = sgemv.sgemv_workspace_bytes(d, 1)
+    w16 = sgemv.sgemv_workspace_bytes(d, 16)
+    assert w1 > 0 and w16 >= w1
+    for m in range(1, 17):
+        assert sgemv.sgemv_workspace_bytes(d, m) >= sgemv.sgemv_workspace_bytes(d, max(1, m - 1))
+    assert sgemv.sgemv_workspace_bytes(d, 0) == 0
+    assert sgemv.sgemv_workspace_bytes(d, 17) == 0
+    bad = _desc(); bad.K = 100
+    assert sgemv.sgemv_workspace_bytes(bad, 1) == 0
+
+
+def test_strerror():
+    for st in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(sgemv.strerror(st), str) and sgemv.strerror(st)

@@ -1,0 +1,305 @@
+"""Parity of the HIP path with the fp64 oracle (MI355X).
+
+Index lists are compared bit for bit; outputs within per-row relative L2
+1e-3 and per-element 2e-3 * sum|w^||xe| of the oracle.  Every call goes
+through the C ABI (ctypes binding)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _gather(x_np, ts, K=None):
+    from activation_sparse_bit_amd import sgemv
+    x = G.to_dev(x_np)
+    K = x_np.shape[-1] if K is None else K
+    idx = torch.full((K,), -7, dtype=torch.int32, device=G.torch_dev())
+    cnt = torch.full((1,), -7, dtype=torch.int32, device=G.torch_dev())
+    sgemv.sgemv_gather_indices(x, ts, idx, cnt, K=K)
+    torch.cuda.synchronize()
+    c = int(cnt.item())
+    return idx.cpu().numpy(), c
+
+
+# ---------------------------------------------------------------------------
+# index gathering
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("K", [128, 2048, 4096, 8192, 14336, 28672, 65536])
+@pytest.mark.parametrize("p", [0.0, 0.5, 0.7, 0.9, 0.999])
+def test_gather_single(K, p):
+    x = synth.glu_activation(K % 97, K)
+    t = synth.percentile_threshold(x, p)
+    idx, c = _gather(x, [t])
+    U = oracle.active_indices(x, t)
+    assert c == len(U)
+    assert np.array_equal(idx[:c], U)
+    assert np.all(idx[c:] == -7)   # untouched beyond count
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16])
+def test_gather_batched_union(M):
+    K = 14336
+    X = np.stack([synth.glu_activation(m, K) for m in range(M)])
+    ts = [synth.percentile_threshold(X[m], 0.7) for m in range(M)]
+    idx, c = _gather(X, ts)
+    U = oracle.active_indices(X, ts)
+    assert c == len(U) and np.array_equal(idx[:c], U)
+
+
+def test_gather_strided_rows():
+    K, ldx, M = 2048, 2048 + 64, 3
+    X = np.zeros((M, ldx), dtype=np.float16)
+    X[:, :K] = np.stack([synth.plain_activation(m, K) for m in range(M)])
+    X[:, K:] = np.float16(100.0)     # padding beyond K must be ignored
+    ts = [1.0, 1.5, 2.0]
+    from activation_sparse_bit_amd import sgemv
+    x = G.to_dev(X)
+    idx = torch.full((K,), -7, dtype=torch.int32, device=G.torch_dev())
+    cnt = torch.zeros(1, dtype=torch.int32, device=G.torch_dev())
+    sgemv.sgemv_gather_indices(x, ts, idx, cnt, K=K)
+    torch.cuda.synchronize()
+    U = oracle.active_indices(X[:, :K], ts)
+    c = int(cnt.item())
+    assert c == len(U) and np.array_equal(idx.cpu().numpy()[:c], U)
+
+
+def test_gather_special_values():
+    rng = np.random.default_rng(5)
+    K = 1024
+    bits = rng.standard_normal(K).astype(np.float16).view(np.uint16).copy()
+    specials = [0x0000, 0x8000, 0x7E00, 0xFE00, 0x7C00, 0xFC00, 0x0001, 0x8001, 0x03FF, 0x7BFF]
+    bits[rng.choice(K, len(specials) * 8, replace=False)] = np.repeat(specials, 8)
+    x = bits.view(np.float16)
+    mags = sorted(set(np.abs(x[np.isfinite(x)].astype(np.float32)).tolist()))
+    for t in [0.0, 2.0 ** -24, mags[len(mags) // 2], 65504.0, 1e30, 0.9995, float(np.float32(1 / 3))]:
+        idx, c = _gather(x, [t])
+        U = oracle.active_indices(x, t)
+        assert c == len(U) and np.array_equal(idx[:c], U), t
+
+
+def test_gather_empty_and_full():
+    K = 4096
+    x = np.zeros(K, dtype=np.float16)
+    idx, c = _gather(x, [0.5])
+    assert c == 0 and np.all(idx == -7)
+    idx, c = _gather(x, [0.0])
+    assert c == K and np.array_equal(idx, np.arange(K))
+
+
+# ---------------------------------------------------------------------------
+# sparse GEMV, one row
+# ---------------------------------------------------------------------------
+def _run_single(j, N, K, sigma, x, t, dtype=None, dense=False):
+    from activation_sparse_bit_amd import sgemv
+    pm = G.packed(j, N, K, sigma)
+    xd = G.to_dev(x)
+    dtype = dtype or torch.float16
+    y = torch.full((N,), float("nan"), dtype=dtype, device=G.torch_dev())
+    if dense:
+        sgemv.sgemv_run(pm.desc, pm.blob, xd, None, None, y, pm.workspace)
+        torch.cuda.synchronize()
+        return y.float().cpu().numpy(), None
+    idx = torch.full((K,), -7, dtype=torch.int32, device=G.torch_dev())
+    cnt = torch.zeros(1, dtype=torch.int32, device=G.torch_dev())
+    sgemv.sgemv_gather_indices(xd, [t], idx, cnt)
+    sgemv.sgemv_run(pm.desc, pm.blob, xd, idx, cnt, y, pm.workspace)
+    torch.cuda.synchronize()
+    ws_nonzero = int(torch.count_nonzero(pm.workspace[:256]).item())
+    assert ws_nonzero == 0, "arrival counters not reset"
+    return y.float().cpu().numpy(), int(cnt.item())
+
+
+@pytest.mark.parametrize("p", [0.0, 0.5, 0.7, 0.9])
+def test_run_single_2048(p):
+    K = N = 2048
+    q, s, z = G.weights(0, N, K, 0.02)
+    x = synth.plain_activation(0, K)
+    t = synth.percentile_threshold(x, p)
+    y, c = _run_single(0, N, K, 0.02, x, t)
+    y_ref, B, U = oracle.gemv_masked(q, s, z, x, t)
+    assert c == len(U)
+    G.check_y(y, y_ref, B, f"2048x2048 p={p}")
+
+
+@pytest.mark.parametrize("p", [0.0, 0.5, 0.7, 0.9])
+def test_run_down_14336(p):
+    K, N = 14336, 4096
+    q, s, z = G.weights(0, N, K, 0.02)
+    x = synth.glu_activation(0, K)
+    t = synth.percentile_threshold(x, p)
+    y, c = _run_single(0, N, K, 0.02, x, t)
+    y_ref, B, U = oracle.gemv_masked(q, s, z, x, t)
+    assert c == len(U)
+    G.check_y(y, y_ref, B, f"down p={p}")
+
+
+@pytest.mark.parametrize("K,N", [(4096, 4096), (4096, 1024), (4096, 14336), (14336, 4096)])
+def test_run_layer_8b(K, N):
+    q, s, z = G.weights(1, N, K, 0.02)
+    x = synth.plain_activation(K // 1024, K)
+    t = synth.percentile_threshold(x, 0.5)
+    y, c = _run_single(1, N, K, 0.02, x, t)
+    y_ref, B, U = oracle.gemv_masked(q, s, z, x, t)
+    G.check_y(y, y_ref, B, f"layer {K}->{N}")
+
+
+@pytest.mark.parametrize("K,N,glu", [(8192, 28672, False), (28672, 8192, True)])
+@pytest.mark.parametrize("p", [0.5, 0.9])
+def test_run_mlp_70b_sampled(K, N, glu, p):
+    q, s, z = G.weights(2, N, K, 0.015)
+    x = synth.glu_activation(0, K) if glu else synth.plain_activation(0, K)
+    t = synth.percentile_threshold(x, p)
+    y, c = _run_single(2, N, K, 0.015, x, t)
+    rows = G.sample_rows(N, 384)
+    y_ref, B, U = G.oracle_rows(q, s, z, x, t, rows)
+    assert c == len(U)
+    G.check_y(y[rows][None, :], y_ref, B, f"70b {K}->{N} p={p}")
+
+
+@pytest.mark.parametrize("K,N", [(128, 512), (384, 1536), (1152, 512), (2176, 2560)])
+def test_run_ragged_shapes(K, N):
+    """K not a multiple of the 256-column workgroup slice, tiny K, several tiles."""
+    q, s, z = synth.random_int4_problem(K + N, N, K)
+    from activation_sparse_bit_amd import sgemv
+    pm = sgemv.PackedMatrix(q, s, z, device=G.torch_dev())
+    x = synth.plain_activation(3, K)
+    for p in (0.0, 0.3, 0.95):
+        t = synth.percentile_threshold(x, p)
+        xd = G.to_dev(x)
+        idx = torch.zeros(K, dtype=torch.int32, device=G.torch_dev())
+        cnt = torch.zeros(1, dtype=torch.int32, device=G.torch_dev())
+        y = torch.full((N,), float("nan"), dtype=torch.float32, device=G.torch_dev())
+        sgemv.sgemv_gather_indices(xd, [t], idx, cnt)
+        sgemv.sgemv_run(pm.desc, pm.blob, xd, idx, cnt, y, pm.workspace)
+        torch.cuda.synchronize()
+        y_ref, B, U = oracle.gemv_masked(q, s, z, x, t)
+        G.check_y(y.cpu().numpy(), y_ref, B, f"ragged {K}x{N} p={p}")
+
+
+def test_run_dense_equals_oracle():
+    K, N = 14336, 4096
+    q, s, z = G.weights(0, N, K, 0.02)
+    x = synth.glu_activation(0, K)
+    y, _ = _run_single(0, N, K, 0.02, x, 0.0, dense=True)
+    y_ref, B = oracle.gemv_dense(q, s, z, x)
+    G.check_y(y, y_ref, B, "dense")
+
+
+def test_run_fp32_output_and_t0_equals_dense():
+    K, N = 4096, 4096
+    q, s, z = G.weights(1, N, K, 0.02)
+    x = synth.plain_activation(1, K)
+    y32, c = _run_single(1, N, K, 0.02, x, 0.0, dtype=torch.float32)
+    yd, _ = _run_single(1, N, K, 0.02, x, 0.0, dtype=torch.float32, dense=True)
+    assert c == K
+    assert np.array_equal(y32, yd)     # same list, same order, same bits
+    y_ref, B = oracle.gemv_dense(q, s, z, x)
+    rel = G.check_y(y32, y_ref, B, "fp32")
+    assert rel < 2e-6                  # no fp16 rounding: fp32 accumulation error only
+
+
+def test_run_count_zero_gives_plus_zero():
+    K, N = 4096, 4096
+    x = np.zeros(K, dtype=np.float16)
+    y, c = _run_single(1, N, K, 0.02, x, 1.0)
+    assert c == 0
+    assert np.all(y == 0) and not np.any(np.signbit(y))
+
+
+def test_run_deterministic_and_scale_equivariant():
+    from activation_sparse_bit_amd import sgemv
+    K, N = 14336, 4096
+    pm = G.packed(0, N, K, 0.02)
+    x = synth.glu_activation(0, K)
+    t = synth.percentile_threshold(x, 0.7)
+    outs = []
+    for scale in (1.0, 1.0, 2.0):
+        xs = (x.astype(np.float32) * scale).astype(np.float16)
+        xd = G.to_dev(xs)
+        idx = torch.zeros(K, dtype=torch.int32, device=G.torch_dev())
+        cnt = torch.zeros(1, dtype=torch.int32, device=G.torch_dev())
+        y = torch.empty(N, dtype=torch.float16, device=G.torch_dev())
+        sgemv.sgemv_gather_indices(xd, [t * scale], idx, cnt)
+        sgemv.sgemv_run(pm.desc, pm.blob, xd, idx, cnt, y, pm.workspace)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy().view(np.uint16))
+    assert np.array_equal(outs[0], outs[1])                      # bitwise repeatable
+    y1 = outs[0].view(np.float16).astype(np.float32)
+    y2 = outs[2].view(np.float16).astype(np.float32)
+    assert np.array_equal(y2, 2 * y1)                            # exact doubling
+
+
+def test_run_user_index_list():
+    """An arbitrary ascending list (not from the gather) and a count below the
+    list length: only the first count entries are used."""
+    from activation_sparse_bit_amd import sgemv
+    K, N = 4096, 4096
+    q, s, z = G.weights(1, N, K, 0.02)
+    pm = G.packed(1, N, K, 0.02)
+    rng = np.random.default_rng(9)
+    lst = np.sort(rng.choice(K, 1500, replace=False)).astype(np.int32)
+    full = np.full(K, K + 5, dtype=np.int32)      # junk beyond count
+    full[:1500] = lst
+    x = synth.plain_activation(2, K)
+    xd = G.to_dev(x)
+    idx = G.to_dev(full)
+    for c in (1500, 1001, 1, 0):
+        cnt = G.to_dev(np.array([c], dtype=np.int32))
+        y = torch.full((N,), float("nan"), dtype=torch.float32, device=G.torch_dev())
+        sgemv.sgemv_run(pm.desc, pm.blob, xd, idx, cnt, y, pm.workspace)
+        torch.cuda.synchronize()
+        y_ref, B = oracle.gemv_listed(q, s, z, x, lst[:c])
+        G.check_y(y.cpu().numpy(), y_ref, B, f"user list c={c}")
+
+
+# ---------------------------------------------------------------------------
+# batched
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16])
+def test_run_batched(M):
+    from activation_sparse_bit_amd import sgemv
+    K, N = 14336, 4096
+    q, s, z = G.weights(0, N, K, 0.02)
+    pm = G.packed(0, N, K, 0.02)
+    X = np.stack([synth.glu_activation(m, K) for m in range(M)])
+    ts = [synth.percentile_threshold(X[m], 0.7) for m in range(M)]
+    xd = G.to_dev(X)
+    idx = torch.zeros(K, dtype=torch.int32, device=G.torch_dev())
+    cnt = torch.zeros(1, dtype=torch.int32, device=G.torch_dev())
+    y = torch.full((M, N), float("nan"), dtype=torch.float16, device=G.torch_dev())
+    sgemv.sgemv_gather_indices(xd, ts, idx, cnt)
+    sgemv.sgemv_run_batched(pm.desc, pm.blob, xd, ts, idx, cnt, y, pm.workspace)
+    torch.cuda.synchronize()
+    rows = G.sample_rows(N, 512, seed=M)
+    y_ref, B, U = G.oracle_rows(q, s, z, X, ts, rows)
+    assert int(cnt.item()) == len(U)
+    G.check_y(y.float().cpu().numpy()[:, rows], y_ref, B, f"batched M={M}")
+
+
+def test_run_batched_unmasked_and_strides():
+    from activation_sparse_bit_amd import sgemv
+    K, N, M = 4096, 4096, 3
+    q, s, z = G.weights(1, N, K, 0.02)
+    pm = G.packed(1, N, K, 0.02)
+    ldx, ldy = K + 8, N + 16
+    X = np.zeros((M, ldx), dtype=np.float16)
+    X[:, :K] = np.stack([synth.plain_activation(m, K) for m in range(M)])
+    ts = [0.6, 1.0, 1.4]
+    xd = G.to_dev(X)
+    idx = torch.zeros(K, dtype=torch.int32, device=G.torch_dev())
+    cnt = torch.zeros(1, dtype=torch.int32, device=G.torch_dev())
+    sgemv.sgemv_gather_indices(xd, ts, idx, cnt, K=K)
+    y = torch.full((M, ldy), float("nan"), dtype=torch.float32, device=G.torch_dev())
+    sgemv.sgemv_run_batched(pm.desc, pm.blob, xd, None, idx, cnt, y, pm.workspace)
+    torch.cuda.synchronize()
+    U = oracle.active_indices(X[:, :K], ts)
+    y_ref, B = oracle.gemv_listed(q, s, z, X[:, :K], U)     # rows unmasked over the union
+    yy = y.cpu().numpy()
+    G.check_y(yy[:, :N], y_ref, B, "batched unmasked")
+    assert np.all(np.isnan(yy[:, N:]))                        # padding untouched
