@@ -56,9 +56,10 @@ struct RunArgs {
     const int32_t* count;    // number of listed columns (device)
     void* y;
     uint32_t* counters;      // one arrival counter per tile
-    float* partials;         // [tile][slice][Mt][512]
+    float* partials;         // [tile][slice][Mt][512] slice sums
+    uint32_t partial_bytes;  // size of the partials region
     int32_t K, ldx, ldy, M;
-    int32_t tiles, slices_max;
+    int32_t tiles, slices;
     uint32_t out_f32;
     Codes tc;
 };
@@ -160,81 +161,345 @@ __global__ __launch_bounds__(1024) void k_gather(const uint16_t* __restrict__ x,
 // ---------------------------------------------------------------------------
 // sparse / dense GEMV
 // ---------------------------------------------------------------------------
+//
+// Work split.  A workgroup owns 256 outputs: one half of a 512-output layout
+// tile, whose part of every column run is 128 contiguous bytes (one cache
+// line).  The grid is (N / 256 half tiles) x S slices, S set by the host so
+// that the grid is about one workgroup per CU.  At run time the listed
+// positions are cut into chunks of 16; a half tile's chunks are divided
+// evenly among its S' = min(S, chunks) slices and, inside a workgroup,
+// among its wavefronts, so every wavefront owns a contiguous run of list
+// positions whatever the sparsity.  Lane l owns outputs 4l .. 4l+3 of the
+// half tile and reads 2 bytes of each listed column.
+//
+// Pipeline.  A wavefront keeps the data of its next chunk and the list
+// entries of the chunk after it in flight while it computes the current
+// one.  Every load is issued unconditionally (past the end of the run it
+// re-reads the last chunk, which the caches serve), so each wait counts
+// exactly the loads issued after the data it needs.
+//
+// Arithmetic.  For two listed columns a, b the two 4-bit codes of one output
+// are placed in the low mantissa bits of 0x6400 (= 1024.0 in fp16), which
+// makes the fp16 values 1024 + q exactly (high nibbles: 1024 + 16 q);
+// subtracting 1024 + z (or 1024 + 16 z) in packed fp16 leaves q - z (or
+// 16 (q - z)) exactly, and v_dot2_f32_f16 adds (q_a - z) x_a + (q_b - z) x_b
+// to an fp32 sum.  All fp16 operands are normal numbers or zero: the dot
+// instruction is only used where it is accurate (with subnormal fp16 inputs
+// it is not correctly rounded).  A chunk is computed in one pass per group
+// it touches, with x masked to that group's positions, so every pass uses
+// one scale and one zero-point and runs without branches.  The scale is
+// applied once per (pass, output); the 16 of the high nibbles at the end.
+//
+// Reduction.  Wavefronts are added by a fixed-order LDS tree.  Slices
+// publish their sums with write-through (sc1) stores, wait for the stores to
+// complete, and count themselves on a per-half-tile atomic counter; the
+// workgroup that arrives last reads every slice's sums (sc1 loads), adds
+// them in slice order and writes y, then resets the counter.  The result
+// does not depend on which workgroup arrives last.
+
+constexpr int kVTile = 256;            // outputs per workgroup (half a layout tile)
+constexpr int kHalfRun = kVTile / 2;   // bytes of one column for those outputs
+constexpr uint32_t kCacheSC1 = 16;     // cache policy: coherent at device scope
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Wavefronts per workgroup: two per SIMD for few rows; four in all for
+// many rows, whose accumulators fill the register file.
 template <int MT>
-struct WaveState {
-    float y[MT][8];     // running sums per row and output (odd outputs x16)
-    float acc[MT][8];   // current group's sums of (q - z) * x
-    uint32_t md[8];     // current group's (s | z << 16) words
-    half2_t zc[8];      // 1024 + z (even outputs) / 1024 + 16 z (odd), both halves
+struct Waves {
+    static constexpr int kN = MT <= 4 ? 8 : 4;
+};
+
+// Scale/zero words of this lane's 4 outputs for one group.
+__device__ __forceinline__ void load_md4(const uint32_t* __restrict__ grp, int lane, uint32_t (&md)[4]) {
+    const uint4 v = reinterpret_cast<const uint4*>(grp)[lane];
+    md[0] = v.x; md[1] = v.y; md[2] = v.z; md[3] = v.w;
+}
+
+// Rows of x staged per lane: lane L holds row (L / 16) + 4 j of listed
+// column L % 16 in xv[j].
+template <int MT>
+struct XRows {
+    static constexpr int kPerLane = MT <= 4 ? 1 : MT / 4;
+    static constexpr int kLanes = MT < 4 ? MT * kChunk : 64;
 };
 
 template <int MT>
-__device__ __forceinline__ void fold_group(WaveState<MT>& st) {
+struct Chunk {
+    int j0;                    // first list position
+    int nv;                    // valid positions
+    int gA, gZ;                // groups of the first and last valid position
+    uint32_t codes;            // 2 bits per position: min(group - gA, 3)
+    uint32_t w[kChunk];        // this lane's 2 bytes of each column (low half)
+    uint32_t md0[4];           // metadata of group gA
+    uint32_t md1[4];           // metadata of group gA + 1 (gA when the chunk has one group)
+    uint32_t xv[XRows<MT>::kPerLane];  // staged x values (fp16 bits)
+};
+
+struct WaveCtx {
+    const uint8_t* wcol;      // weights of this half tile: column k at + k * 256
+    const uint32_t* mdh;      // metadata of this half tile: group g at + g * 512 words
+    int lane, K, p1;          // the wavefront's list positions end at p1
+    uint32_t vmagic;          // 0x64006400 (two fp16 1024.0) held in a VGPR
+};
+
+// The 16 list entries of a chunk in one VGPR: lane L holds entry
+// j0 + L % 16.  j0 is a multiple of 16 below K and K is a multiple of 128,
+// so the entries are inside the K-entry list.
+struct Idx {
+    int v;
+};
+
+template <bool DENSE>
+__device__ __forceinline__ void idx_load(const RunArgs& a, int j0, int lane, Idx& ix) {
+    if (DENSE) return;
+    ix.v = a.idx[j0 + (lane & (kChunk - 1))];
+}
+
+// The chunk's listed columns, clamped and padded: positions past nv repeat
+// the last valid column.
+template <bool DENSE>
+__device__ __forceinline__ void chunk_columns(const Idx& ix, int j0, int nv, int K, int (&kk)[kChunk]) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const float s = (float)as_h2(st.md[r]).x;
+    for (int i = 0; i < kChunk; ++i) {
+        int k;
+        if (DENSE) {
+            k = j0 + (i < nv ? i : nv - 1);
+        } else {
+            k = __builtin_amdgcn_readlane(ix.v, i);
+            k = (i == 0 || i < nv) ? k : kk[i > 0 ? i - 1 : 0];
+            k = (unsigned)k < (unsigned)K ? k : K - 1;
+        }
+        kk[i] = __builtin_amdgcn_readfirstlane(k);
+    }
+}
+
+// Issue every load of one chunk: 16 weight half-runs, the scale/zero words
+// of its first two groups, and the activations.
+template <int MT, bool DENSE, bool MASK>
+__device__ __forceinline__ void data_load(const RunArgs& a, const WaveCtx& wc, int j0, const Idx& ix,
+                                          Chunk<MT>& ch) {
+    const int K = wc.K;
+    int nv = wc.p1 - j0;
+    nv = nv > kChunk ? kChunk : nv;
+    ch.j0 = j0;
+    ch.nv = nv;
+    int kk[kChunk];
+    chunk_columns<DENSE>(ix, j0, nv, K, kk);
+    ch.gA = kk[0] >> 7;
+    ch.gZ = kk[kChunk - 1] >> 7;
+    uint32_t codes = 0;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            st.y[m][r] = __builtin_fmaf(s, st.acc[m][r], st.y[m][r]);
-            st.acc[m][r] = 0.f;
+    for (int i = 0; i < kChunk; ++i) {
+        const int d = (kk[i] >> 7) - ch.gA;
+        codes |= (uint32_t)(d < 3 ? d : 3) << (2 * i);
+    }
+    ch.codes = codes;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+        const uint16_t* col = reinterpret_cast<const uint16_t*>(wc.wcol + (size_t)kk[i] * (2 * kHalfRun));
+        ch.w[i] = __builtin_nontemporal_load(col + wc.lane);
+    }
+    const int g1 = ch.gA + 1 <= ch.gZ ? ch.gA + 1 : ch.gZ;
+    load_md4(wc.mdh + (size_t)ch.gA * (2 * kVTile), wc.lane, ch.md0);
+    load_md4(wc.mdh + (size_t)g1 * (2 * kVTile), wc.lane, ch.md1);
+    // x: one vector load per staged row; lane L fetches column L % 16,
+    // whose index it already holds
+    const int c = wc.lane & (kChunk - 1);
+    int kc = DENSE ? j0 + c : ix.v;
+    kc = (unsigned)kc < (unsigned)K ? kc : K - 1;
+#pragma unroll
+    for (int j = 0; j < XRows<MT>::kPerLane; ++j) {
+        const int m = (wc.lane >> 4) + 4 * j;
+        const bool ok = wc.lane < XRows<MT>::kLanes && m < a.M && c < nv;
+        const int mr = ok ? m : 0;
+        const int kr = ok ? kc : 0;
+        uint32_t v = a.x[(size_t)mr * a.ldx + kr];
+        if (MASK && !is_active(v, code_of(a.tc, mr))) v = 0;
+        ch.xv[j] = ok ? v : 0u;
+    }
+}
+
+// (R & mask) | magic: with the magic held in a VGPR the compiler can use one
+// v_and_or_b32 (a VOP3 instruction on this target takes no literal).
+__device__ __forceinline__ uint32_t and_or(uint32_t r, uint32_t mask, uint32_t vmagic) {
+    return (r & mask) | vmagic;
+}
+
+// One pass over the 8 column pairs of a chunk for one group: x is masked to
+// the positions of that group (pmask), so every pair uses the same scale
+// and zero-point.  Byte i of a lane's half-run holds its outputs 2i (low
+// nibble) and 2i+1 (high nibble).
+template <int MT>
+__device__ __forceinline__ void chunk_pass(float (&y)[MT][4], const Chunk<MT>& ch, const uint32_t (&md)[4],
+                                           const uint32_t (&pmask)[kChunk / 2],
+                                           const uint16_t (*xs)[kChunk], uint32_t vmagic) {
+    half2_t zc[4];
+    float sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const half2_t v = as_h2(md[r]);
+        sc[r] = (float)v.x;
+        const _Float16 z = (r & 1) ? (_Float16)(v.y * (_Float16)16.0f) : v.y;
+        zc[r] = (half2_t){z, z} + (half2_t){(_Float16)1024.0f, (_Float16)1024.0f};
+    }
+    float acc[MT][4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[m][r] = 0.f;
+#pragma unroll
+    for (int p = 0; p < kChunk / 2; ++p) {
+        uint32_t xp[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) xp[m] = reinterpret_cast<const uint32_t*>(&xs[m][0])[p] & pmask[p];
+        const uint32_t A = ch.w[2 * p], B = ch.w[2 * p + 1];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            // byte i of A and of B into the low bytes of the two halves
+            const uint32_t sel = (0x0Cu << 24) | ((uint32_t)i << 16) | (0x0Cu << 8) | (4u + i);
+            const uint32_t R = __builtin_amdgcn_perm(A, B, sel);
+            const half2_t lo = as_h2(and_or(R, 0x000F000Fu, vmagic)) - zc[2 * i];      // q - z
+            const half2_t hi = as_h2(and_or(R, 0x00F000F0u, vmagic)) - zc[2 * i + 1];  // 16 (q - z)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                acc[m][2 * i] = __builtin_amdgcn_fdot2(lo, as_h2(xp[m]), acc[m][2 * i], false);
+                acc[m][2 * i + 1] = __builtin_amdgcn_fdot2(hi, as_h2(xp[m]), acc[m][2 * i + 1], false);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) y[m][r] = __builtin_fmaf(sc[r], acc[m][r], y[m][r]);
+}
+
+// Pair masks for the positions whose bit is set in pos (bit i = position i).
+__device__ __forceinline__ void pair_masks(uint32_t pos, uint32_t (&pm)[kChunk / 2]) {
+#pragma unroll
+    for (int p = 0; p < kChunk / 2; ++p)
+        pm[p] = ((pos >> (2 * p)) & 1u ? 0x0000FFFFu : 0u) | ((pos >> (2 * p + 1)) & 1u ? 0xFFFF0000u : 0u);
+}
+
+// Positions (bit mask) whose 2-bit group code equals d.
+__device__ __forceinline__ uint32_t code_positions(uint32_t codes, uint32_t d, int nv) {
+    uint32_t pos = 0;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) pos |= (((codes >> (2 * i)) & 3u) == d ? 1u : 0u) << i;
+    return pos & ((1u << nv) - 1u);
+}
+
+template <int MT, bool DENSE>
+__device__ __forceinline__ void chunk_compute(float (&y)[MT][4], const RunArgs& a, const WaveCtx& wc,
+                                              const Chunk<MT>& ch, uint16_t (*xs)[kChunk]) {
+    // this wavefront's private LDS slice: xs[m][c] = x of row m, column c
+#pragma unroll
+    for (int j = 0; j < XRows<MT>::kPerLane; ++j) {
+        const int m = (wc.lane >> 4) + 4 * j;
+        if (wc.lane < XRows<MT>::kLanes && m < MT) xs[m][wc.lane & (kChunk - 1)] = (uint16_t)ch.xv[j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // groups gA, gA+1, gA+2: metadata prefetched (the third loaded here)
+    for (int d = 0; d <= 2; ++d) {
+        const uint32_t pos = code_positions(ch.codes, (uint32_t)d, ch.nv);
+        if (pos == 0) continue;
+        uint32_t md[4];
+        if (d == 2) {
+            load_md4(wc.mdh + (size_t)(ch.gA + 2) * (2 * kVTile), wc.lane, md);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) md[r] = d ? ch.md1[r] : ch.md0[r];
+        }
+        uint32_t pm[kChunk / 2];
+        pair_masks(pos, pm);
+        chunk_pass(y, ch, md, pm, xs, wc.vmagic);
+    }
+    // a chunk spanning more than three groups (very sparse lists): the
+    // remaining groups one by one, with the list entries read again
+    if (code_positions(ch.codes, 3u, ch.nv) != 0) {
+        Idx ix;
+        idx_load<DENSE>(a, ch.j0, wc.lane, ix);
+        int kk[kChunk];
+        chunk_columns<DENSE>(ix, ch.j0, ch.nv, wc.K, kk);
+        int g = ch.gA + 3;
+        while (g <= ch.gZ) {
+            uint32_t pos = 0;
+            int gnext = ch.gZ + 1;
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                const int gi = kk[i] >> 7;
+                pos |= (gi == g ? 1u : 0u) << i;
+                gnext = (gi > g && gi < gnext) ? gi : gnext;
+            }
+            pos &= (1u << ch.nv) - 1u;
+            if (pos != 0) {
+                uint32_t md[4];
+                load_md4(wc.mdh + (size_t)g * (2 * kVTile), wc.lane, md);
+                uint32_t pm[kChunk / 2];
+                pair_masks(pos, pm);
+                chunk_pass(y, ch, md, pm, xs, wc.vmagic);
+            }
+            g = gnext;
+        }
+    }
+    // all reads of the slice are done before the next chunk overwrites it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <int MT>
+__device__ __forceinline__ void store_y(const RunArgs& a, int vt, int lane, const float (&v)[MT][4]) {
+    const int n0 = vt * kVTile + lane * 4;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        if (m >= a.M) break;
+        if (a.out_f32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.y) + (size_t)m * a.ldy + n0) =
+                make_float4(v[m][0], v[m][1], v[m][2], v[m][3]);
+        } else {
+            const half2_t p0 = (half2_t){(_Float16)v[m][0], (_Float16)v[m][1]};
+            const half2_t p1 = (half2_t){(_Float16)v[m][2], (_Float16)v[m][3]};
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + (size_t)m * a.ldy + n0) =
+                make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
         }
     }
 }
 
+// Fixed-order tree over the workgroup's wavefronts; wavefront 0 ends with
+// the sum.  Must be reached by every wavefront.
 template <int MT>
-__device__ __forceinline__ void set_group(WaveState<MT>& st, const uint32_t (&md)[8]) {
+__device__ __forceinline__ void wg_tree(float (&v)[MT][4], float (*red)[MT][kVTile], int wave, int lane) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        st.md[r] = md[r];
-        const _Float16 z = as_h2(md[r]).y;
-        const _Float16 zz = (r & 1) ? (_Float16)(z * (_Float16)16.0f) : z;
-        st.zc[r] = (half2_t){zz, zz} + (half2_t){(_Float16)1024.0f, (_Float16)1024.0f};
-    }
-}
-
-// Two listed columns A (list position 2p) and B (2p+1) of this lane's 8
-// outputs.  Byte i of a column word holds outputs 2i (low nibble) and 2i+1
-// (high nibble).  v_perm puts byte i of A and of B into the low bytes of the
-// two halves; OR-ing 0x6400 makes each half the fp16 value 1024 + q (low
-// nibble) or 1024 + 16 q (high nibble), exactly; subtracting the matching
-// 1024 + z (or 1024 + 16 z) leaves q - z (or 16 (q - z)) exactly, and
-// v_dot2_f32_f16 adds (q_A - z) x_A + (q_B - z) x_B to the fp32 sum.
-template <int MT>
-__device__ __forceinline__ void dot_pair(WaveState<MT>& st, uint32_t A, uint32_t B,
-                                         const uint32_t (&xp)[MT]) {
+    for (int h = Waves<MT>::kN / 2; h >= 1; h /= 2) {
+        if (wave >= h && wave < 2 * h) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t sel = (0x0Cu << 24) | ((uint32_t)i << 16) | (0x0Cu << 8) | (4u + i);
-        const uint32_t R = __builtin_amdgcn_perm(A, B, sel);
-        const half2_t lo = as_h2((R & 0x000F000Fu) | 0x64006400u) - st.zc[2 * i];
-        const half2_t hi = as_h2((R & 0x00F000F0u) | 0x64006400u) - st.zc[2 * i + 1];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            st.acc[m][2 * i] = __builtin_amdgcn_fdot2(lo, as_h2(xp[m]), st.acc[m][2 * i], false);
-            st.acc[m][2 * i + 1] = __builtin_amdgcn_fdot2(hi, as_h2(xp[m]), st.acc[m][2 * i + 1], false);
+            for (int m = 0; m < MT; ++m)
+                *reinterpret_cast<float4*>(&red[wave - h][m][lane * 4]) = make_float4(v[m][0], v[m][1], v[m][2], v[m][3]);
         }
+        __syncthreads();
+        if (wave < h) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float4 u = *reinterpret_cast<const float4*>(&red[wave][m][lane * 4]);
+                v[m][0] += u.x; v[m][1] += u.y; v[m][2] += u.z; v[m][3] += u.w;
+            }
+        }
+        __syncthreads();
     }
 }
 
-// Scale/zero words of this lane's 8 outputs for one (tile, group): the
-// uniform base lives in SGPRs, the lane offset in a VGPR.
-__device__ __forceinline__ void load_md(const uint32_t* __restrict__ grp, int lane, uint32_t (&md)[8]) {
-    const uint4* p = reinterpret_cast<const uint4*>(grp) + lane * 2;
-    const uint4 a = p[0];
-    const uint4 b = p[1];
-    md[0] = a.x; md[1] = a.y; md[2] = a.z; md[3] = a.w;
-    md[4] = b.x; md[5] = b.y; md[6] = b.z; md[7] = b.w;
-}
+template <int MT, bool DENSE, bool MASK>
+__global__ __launch_bounds__(Waves<MT>::kN * 64) void k_run(RunArgs a) {
+    constexpr int kWaves = Waves<MT>::kN;
+    __shared__ float red[kWaves / 2][MT][kVTile];
+    __shared__ uint16_t xs[kWaves][MT][kChunk];
+    __shared__ uint32_t last_flag;
 
-template <int MT, int WPW, int CHUNKS, bool DENSE, bool MASK>
-__global__ __launch_bounds__(WPW * 64) void k_run(RunArgs a) {
-    constexpr int kColsWave = kChunk * CHUNKS;
-    constexpr int kColsWG = kColsWave * WPW;
-    __shared__ uint16_t xs[WPW][MT][kChunk];
-    __shared__ float red[(WPW > 1 ? WPW / 2 : 1)][MT][kTileN];
-
-    const int tile = blockIdx.x % a.tiles;
-    const int slice = blockIdx.x / a.tiles;
+    const int T = a.tiles;
+    const int vt = blockIdx.x % T;         // half tile
+    const int slice = blockIdx.x / T;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int K = a.K;
@@ -247,244 +512,148 @@ __global__ __launch_bounds__(WPW * 64) void k_run(RunArgs a) {
         count = __builtin_amdgcn_readfirstlane(*a.count);
         count = count < 0 ? 0 : (count > K ? K : count);
     }
-    const int S = count > 0 ? (count + kColsWG - 1) / kColsWG : 1;
-    if (slice >= S) return;
-
-    WaveState<MT> st;
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            st.y[m][r] = 0.f;
-            st.acc[m][r] = 0.f;
-        }
-    int gcur = -1;
-
-    const uint8_t* __restrict__ wtile = a.w + (size_t)tile * K * kColBytes;
-    const uint32_t* __restrict__ mdtile = a.md + (size_t)tile * Gk * kTileN;
-    const int wbase = slice * kColsWG + wave * kColsWave;
-
-    for (int c = 0; c < CHUNKS; ++c) {
-        const int j0 = wbase + c * kChunk;
-        int nv = count - j0;
-        nv = nv > kChunk ? kChunk : nv;
-        if (nv <= 0) break;
-
-        // listed columns of this chunk (uniform); padding repeats the last one
-        // (j0 + 16 <= K always holds, so all 16 entries are in bounds)
-        int kk[kChunk];
-        if (DENSE) {
-#pragma unroll
-            for (int i = 0; i < kChunk; ++i) kk[i] = j0 + i;
-        } else {
-            const int4* ip = reinterpret_cast<const int4*>(a.idx + j0);
-#pragma unroll
-            for (int q4 = 0; q4 < kChunk / 4; ++q4) {
-                const int4 v = ip[q4];
-                kk[4 * q4 + 0] = v.x; kk[4 * q4 + 1] = v.y;
-                kk[4 * q4 + 2] = v.z; kk[4 * q4 + 3] = v.w;
-            }
-#pragma unroll
-            for (int i = 0; i < kChunk; ++i) {
-                int k = (i == 0 || i < nv) ? kk[i] : kk[i > 0 ? i - 1 : 0];
-                k = (unsigned)k < (unsigned)K ? k : K - 1;
-                kk[i] = __builtin_amdgcn_readfirstlane(k);
-            }
-        }
-
-        // weight words of this lane for every column (256 contiguous bytes per column)
-        uint32_t wv[kChunk];
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i) {
-            const uint32_t* col = reinterpret_cast<const uint32_t*>(wtile + (size_t)kk[i] * kColBytes);
-            wv[i] = __builtin_nontemporal_load(col + lane);
-        }
-
-        // scale/zero words of up to three consecutive groups from the first
-        const int gA = kk[0] >> 7;
-        const int gZ = kk[kChunk - 1] >> 7;
-        uint32_t slot[3][8];
-#pragma unroll
-        for (int sidx = 0; sidx < 3; ++sidx)
-            if (gA + sidx <= gZ) load_md(mdtile + (size_t)(gA + sidx) * kTileN, lane, slot[sidx]);
-
-        // stage this chunk's activations (masked, zero for padding) in LDS
-        for (int e = lane; e < MT * kChunk; e += 64) {
-            const int m = e / kChunk, i = e % kChunk;
-            uint32_t v = 0;
-            if (m < a.M && i < nv) {
-                int k = DENSE ? j0 + i : a.idx[j0 + i];
-                k = (unsigned)k < (unsigned)K ? k : K - 1;
-                v = a.x[(size_t)m * a.ldx + k];
-                if (MASK && !is_active(v, code_of(a.tc, m))) v = 0;
-            }
-            xs[wave][m][i] = (uint16_t)v;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-#pragma unroll
-        for (int p = 0; p < kChunk / 2; ++p) {
-            uint32_t xp[MT];
+    if (count == 0) {  // nothing listed: y = +0
+        if (slice == 0 && wave == 0) {
+            float z[MT][4];
 #pragma unroll
             for (int m = 0; m < MT; ++m)
-                xp[m] = reinterpret_cast<const uint32_t*>(&xs[wave][m][0])[p];
-            const int ga = kk[2 * p] >> 7;
-            const int gb = kk[2 * p + 1] >> 7;
-            if (ga != gcur) {
-                if (gcur >= 0) fold_group(st);
-                const int d = ga - gA;
-                if (d == 0) set_group(st, slot[0]);
-                else if (d == 1) set_group(st, slot[1]);
-                else if (d == 2) set_group(st, slot[2]);
-                else {
-                    uint32_t tmp[8];
-                    load_md(mdtile + (size_t)ga * kTileN, lane, tmp);
-                    set_group(st, tmp);
-                }
-                gcur = ga;
-            }
-            if (gb == ga) {
-                dot_pair(st, wv[2 * p], wv[2 * p + 1], xp);
-            } else {
-                uint32_t xa[MT], xb[MT];
 #pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    xa[m] = xp[m] & 0x0000FFFFu;
-                    xb[m] = xp[m] & 0xFFFF0000u;
-                }
-                dot_pair(st, wv[2 * p], wv[2 * p + 1], xa);
-                fold_group(st);
-                const int d = gb - gA;
-                if (d == 1) set_group(st, slot[1]);
-                else if (d == 2) set_group(st, slot[2]);
-                else {
-                    uint32_t tmp[8];
-                    load_md(mdtile + (size_t)gb * kTileN, lane, tmp);
-                    set_group(st, tmp);
-                }
-                gcur = gb;
-                dot_pair(st, wv[2 * p], wv[2 * p + 1], xb);
-            }
+                for (int r = 0; r < 4; ++r) z[m][r] = 0.f;
+            store_y(a, vt, lane, z);
         }
+        return;
     }
-    if (gcur >= 0) fold_group(st);
+    const int nch = (count + kChunk - 1) / kChunk;        // chunks of 16 positions
+    const int S = a.slices < nch ? a.slices : nch;       // slices in use
+    if (slice >= S) return;
+    const int c0 = (int)((long long)nch * slice / S);
+    const int c1 = (int)((long long)nch * (slice + 1) / S);
+    const int wc0 = c0 + (c1 - c0) * wave / kWaves;
+    const int wc1 = c0 + (c1 - c0) * (wave + 1) / kWaves;
+
+    float y[MT][4];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int r = 1; r < 8; r += 2) st.y[m][r] *= 0.0625f;  // the 16 of the high nibbles
+        for (int r = 0; r < 4; ++r) y[m][r] = 0.f;
 
-    // fixed-order tree over the wavefronts of the workgroup
-#pragma unroll
-    for (int h = WPW / 2; h >= 1; h /= 2) {
-        if (wave >= h && wave < 2 * h) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                float4* dst = reinterpret_cast<float4*>(&red[wave - h][m][lane * 8]);
-                dst[0] = make_float4(st.y[m][0], st.y[m][1], st.y[m][2], st.y[m][3]);
-                dst[1] = make_float4(st.y[m][4], st.y[m][5], st.y[m][6], st.y[m][7]);
-            }
-        }
-        __syncthreads();
-        if (wave < h) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const float4* src = reinterpret_cast<const float4*>(&red[wave][m][lane * 8]);
-                const float4 u = src[0], v = src[1];
-                st.y[m][0] += u.x; st.y[m][1] += u.y; st.y[m][2] += u.z; st.y[m][3] += u.w;
-                st.y[m][4] += v.x; st.y[m][5] += v.y; st.y[m][6] += v.z; st.y[m][7] += v.w;
-            }
-        }
-        __syncthreads();
-    }
-    if (wave != 0) return;
+    if (wc1 > wc0) {
+        const int t = vt >> 1, h = vt & 1;
+        WaveCtx wc;
+        wc.wcol = a.w + (size_t)t * K * (2 * kHalfRun) + h * kHalfRun;
+        wc.mdh = a.md + (size_t)t * Gk * (2 * kVTile) + h * kVTile;
+        wc.lane = lane;
+        wc.K = K;
+        wc.p1 = wc1 * kChunk < count ? wc1 * kChunk : count;
+        wc.vmagic = 0x64006400u | __builtin_amdgcn_mbcnt_lo(0u, 0u);  // per-lane (VGPR) copy
 
-    const int n0 = tile * kTileN + lane * 8;
-    auto store_y = [&](const float (&v)[MT][8]) {
+        // Loads are issued in the order idx(c+2), data(c+1), so that the data
+        // of a chunk only ever waits for its own, older, list entries.
+        const int cl = wc1 - 1;
+        Idx I0, I1;
+        Chunk<MT> A, B;
+        idx_load<DENSE>(a, wc0 * kChunk, lane, I0);
+        idx_load<DENSE>(a, min(wc0 + 1, cl) * kChunk, lane, I1);
+        data_load<MT, DENSE, MASK>(a, wc, wc0 * kChunk, I0, A);
+        for (int c = wc0; c < wc1; c += 2) {
+            idx_load<DENSE>(a, min(c + 2, cl) * kChunk, lane, I0);
+            data_load<MT, DENSE, MASK>(a, wc, min(c + 1, cl) * kChunk, I1, B);
+            chunk_compute<MT, DENSE>(y, a, wc, A, xs[wave]);
+            idx_load<DENSE>(a, min(c + 3, cl) * kChunk, lane, I1);
+            data_load<MT, DENSE, MASK>(a, wc, min(c + 2, cl) * kChunk, I0, A);
+            if (c + 1 < wc1) chunk_compute<MT, DENSE>(y, a, wc, B, xs[wave]);
+        }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            if (m >= a.M) break;
-            if (a.out_f32) {
-                float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.y) + (size_t)m * a.ldy + n0);
-                dst[0] = make_float4(v[m][0], v[m][1], v[m][2], v[m][3]);
-                dst[1] = make_float4(v[m][4], v[m][5], v[m][6], v[m][7]);
-            } else {
-                uint32_t h[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const half2_t pr = (half2_t){(_Float16)v[m][2 * r], (_Float16)v[m][2 * r + 1]};
-                    h[r] = __builtin_bit_cast(uint32_t, pr);
-                }
-                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + (size_t)m * a.ldy + n0) =
-                    make_uint4(h[0], h[1], h[2], h[3]);
-            }
+            y[m][1] *= 0.0625f;  // the 16 of the high nibbles
+            y[m][3] *= 0.0625f;
         }
-    };
+    }
+
+    wg_tree(y, red, wave, lane);
 
     if (S == 1) {
-        store_y(st.y);
+        if (wave == 0) store_y(a, vt, lane, y);
         return;
     }
 
-    // publish this slice's sums; the last workgroup of the tile adds all
-    // slices in slice order and writes y
-    float* part = a.partials + ((size_t)tile * a.slices_max + slice) * MT * kTileN + lane * 8;
+    // publish this slice's sums (write-through), then count the arrival
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc(a.partials, (short)0, (int)a.partial_bytes, 0x00020000);
+    const uint32_t tile_base = (uint32_t)vt * a.slices * MT * kVTile * 4u;
+    if (wave == 0) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        float4* dst = reinterpret_cast<float4*>(part + m * kTileN);
-        dst[0] = make_float4(st.y[m][0], st.y[m][1], st.y[m][2], st.y[m][3]);
-        dst[1] = make_float4(st.y[m][4], st.y[m][5], st.y[m][6], st.y[m][7]);
+        for (int m = 0; m < MT; ++m) {
+            const uint32_t off = tile_base + ((uint32_t)slice * MT + m) * kVTile * 4u + lane * 16u;
+            const u32x4 v = {__float_as_uint(y[m][0]), __float_as_uint(y[m][1]),
+                             __float_as_uint(y[m][2]), __float_as_uint(y[m][3])};
+            __builtin_amdgcn_raw_buffer_store_b128(v, prs, off, 0, kCacheSC1);
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // stores acknowledged before the count
+        uint32_t old = 0;
+        if (lane == 0)
+            old = __hip_atomic_fetch_add(&a.counters[vt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __builtin_amdgcn_readfirstlane(old);
+        if (lane == 0) last_flag = (old == (uint32_t)(S - 1)) ? 1u : 0u;
     }
-    __threadfence();
-    uint32_t old = 0;
-    if (lane == 0) old = atomicAdd(&a.counters[tile], 1u);
-    old = __builtin_amdgcn_readfirstlane(old);
-    if (old != (uint32_t)(S - 1)) return;
-    __threadfence();
+    __syncthreads();
+    if (last_flag == 0u) return;
 
-    float tot[MT][8];
+    // last to arrive: wavefront w adds slices w, w + kWaves, ... in order;
+    // the loads of up to four slices are issued together
+    float tot[MT][4];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) tot[m][r] = 0.f;
-    const float* p0 = a.partials + (size_t)tile * a.slices_max * MT * kTileN + lane * 8;
-    for (int s = 0; s < S; ++s) {
+        for (int r = 0; r < 4; ++r) tot[m][r] = 0.f;
+    for (int sl0 = wave; sl0 < S; sl0 += 4 * kWaves) {
+        u32x4 u[4][MT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const float4* src = reinterpret_cast<const float4*>(p0 + ((size_t)s * MT + m) * kTileN);
-            const float4 u = src[0];
-            const float4 v = src[1];
-            tot[m][0] += u.x; tot[m][1] += u.y; tot[m][2] += u.z; tot[m][3] += u.w;
-            tot[m][4] += v.x; tot[m][5] += v.y; tot[m][6] += v.z; tot[m][7] += v.w;
+        for (int q = 0; q < 4; ++q) {
+            const int sl = sl0 + q * kWaves;
+            const int sc = sl < S ? sl : sl0;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const uint32_t off = tile_base + ((uint32_t)sc * MT + m) * kVTile * 4u + lane * 16u;
+                u[q][m] = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, kCacheSC1);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (sl0 + q * kWaves >= S) break;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                tot[m][0] += __uint_as_float(u[q][m].x); tot[m][1] += __uint_as_float(u[q][m].y);
+                tot[m][2] += __uint_as_float(u[q][m].z); tot[m][3] += __uint_as_float(u[q][m].w);
+            }
         }
     }
-    store_y(tot);
-    if (lane == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wg_tree(tot, red, wave, lane);
+    if (wave == 0) {
+        store_y(a, vt, lane, tot);
+        if (lane == 0) __hip_atomic_store(&a.counters[vt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-struct Shape {
-    int wpw, chunks;
-    int cols() const { return 16 * chunks * wpw; }
-};
-
-Shape shape_for(int mt) {
-    switch (mt) {
-        case 1: return {8, 2};
-        case 2: return {8, 2};
-        case 4: return {8, 2};
-        case 8: return {8, 4};
-        default: return {4, 8};
-    }
-}
+constexpr int kTargetWGs = 256;   // about one workgroup per CU
 
 int pow2_ceil(int m) {
     int p = 1;
     while (p < m) p <<= 1;
     return p;
+}
+
+// Slices per tile: enough workgroups to cover the chip, never more slices
+// than 16-position chunks in a full list.
+int slices_for(const sgemv_desc* d) {
+    const int tiles = d->N / kVTile;
+    int s = (kTargetWGs + tiles / 2) / tiles;
+    if (s < 1) s = 1;
+    const int maxs = d->K / kChunk;
+    return s > maxs ? maxs : s;
 }
 
 float half_value(uint32_t b) {
@@ -534,22 +703,18 @@ int check_desc(const sgemv_desc* d) {
 
 size_t ws_counters_bytes(int tiles) { return ((size_t)tiles * 4 + 255) / 256 * 256; }
 
-size_t ws_bytes_for(const sgemv_desc* d, int mt) {
-    const int tiles = d->N / kTileN;
-    const Shape sh = shape_for(mt);
-    const int smax = (d->K + sh.cols() - 1) / sh.cols();
-    size_t b = ws_counters_bytes(tiles);
-    if (smax > 1) b += (size_t)tiles * smax * mt * kTileN * sizeof(float);
-    return b;
+size_t ws_partial_bytes(const sgemv_desc* d, int mt) {
+    const int tiles = d->N / kVTile;
+    const int s = slices_for(d);
+    return s > 1 ? (size_t)tiles * s * mt * kVTile * sizeof(float) : 0;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 template <int MT, bool DENSE, bool MASK>
 hipError_t launch_run(const RunArgs& a, hipStream_t s) {
-    constexpr Shape sh = {MT <= 8 ? 8 : 4, MT <= 4 ? 2 : MT == 8 ? 4 : 8};
-    const dim3 grid((unsigned)(a.tiles * a.slices_max));
-    hipLaunchKernelGGL((k_run<MT, sh.wpw, sh.chunks, DENSE, MASK>), grid, dim3(sh.wpw * 64), 0, s, a);
+    const dim3 grid((unsigned)(a.tiles * a.slices));
+    hipLaunchKernelGGL((k_run<MT, DENSE, MASK>), grid, dim3(Waves<MT>::kN * 64), 0, s, a);
     return hipGetLastError();
 }
 
@@ -576,20 +741,20 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
     if (ldx < d->K || ldy < d->N) return SGEMV_ESIZE;
     if (ldx % 8 || ldy % 8) return SGEMV_EALIGN;
     if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16)) return SGEMV_EALIGN;
-    if (idx && !aligned(idx, 4)) return SGEMV_EALIGN;
+    if (idx && !aligned(idx, 16)) return SGEMV_EALIGN;
     if (count && !aligned(count, 4)) return SGEMV_EALIGN;
 
     const int mt = pow2_ceil(M);
-    const Shape sh = shape_for(mt);
     RunArgs a;
     std::memset(&a, 0, sizeof a);
     if (thr) {
         st = fill_codes(thr, M, a.tc);
         if (st) return st;
     }
-    a.tiles = d->N / kTileN;
-    a.slices_max = (d->K + sh.cols() - 1) / sh.cols();
-    if (a.slices_max > 1) {
+    a.tiles = d->N / kVTile;
+    a.slices = slices_for(d);
+    const size_t pbytes = ws_partial_bytes(d, mt);
+    if (a.slices > 1) {
         if (!ws) return SGEMV_EINVAL;
         if (!aligned(ws, 256)) return SGEMV_EALIGN;
     }
@@ -603,6 +768,7 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
     a.counters = static_cast<uint32_t*>(ws);
     a.partials = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ws_counters_bytes(a.tiles))
                     : nullptr;
+    a.partial_bytes = (uint32_t)pbytes;
     a.K = d->K;
     a.ldx = ldx;
     a.ldy = ldy;
@@ -663,12 +829,8 @@ extern "C" int sgemv_run_batched(const sgemv_desc* d, const void* packed, const 
 
 extern "C" size_t sgemv_workspace_bytes(const sgemv_desc* d, int32_t M) {
     if (check_desc(d) != SGEMV_OK || M < 1 || M > SGEMV_MAX_BATCH) return 0;
-    size_t b = 0;
-    for (int mt = 1; mt <= pow2_ceil(M); mt <<= 1) {
-        const size_t v = ws_bytes_for(d, mt);
-        b = v > b ? v : b;
-    }
-    return b;
+    const int tiles = d->N / kVTile;
+    return ws_counters_bytes(tiles) + ws_partial_bytes(d, pow2_ceil(M));
 }
 
 extern "C" const char* sgemv_strerror(int status) {

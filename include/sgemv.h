@@ -165,8 +165,10 @@ int sgemv_gather_indices(const void* x_f16, int32_t M, int32_t K, int32_t ldx,
  *   d          host description of the packed matrix (tile_n = 512)
  *   packed     device blob from sgemv_pack_layout, 256-byte aligned
  *   x_f16      device fp16 [K], 16-byte aligned
- *   idx        device int32: ascending, unique, each < K (as produced by
- *              sgemv_gather_indices); or NULL for all columns
+ *   idx        device int32 buffer of K entries, 16-byte aligned, whose
+ *              first *count entries are ascending, unique and < K (as
+ *              produced by sgemv_gather_indices); or NULL for all columns.
+ *              Entries beyond *count may hold anything.
  *   count      device int32 [1], 0 <= *count <= K (clamped to that range)
  *   y          device fp16 [N] (fp32 with SGEMV_OUT_F32), 16-byte aligned
  *   flags      0 or SGEMV_OUT_F32
