@@ -12,18 +12,21 @@
 //   k_gather   one 1024-thread workgroup: per-lane 8-element masks from
 //              16-byte loads, wavefront ballots and mbcnt for in-wave ranks,
 //              an LDS scan across the 16 wavefronts, ordered index writes.
-//   k_run      grid = (tiles of 512 outputs) x (slices of the index list).
-//              Each wavefront owns all 512 outputs of its tile (8 per lane)
-//              and a run of list positions; it reads the listed columns with
-//              one 4-byte load per lane (256 contiguous bytes per column),
-//              dequantizes pairs of columns exactly in fp16
-//              (magic-number nibble extraction, q - z in fp16) and
-//              accumulates with v_dot2_f32_f16 in fp32, applying the group
-//              scale once per (group, output).  Wavefronts are summed by a
-//              fixed-order LDS tree, slices through a workspace by the last
-//              workgroup to arrive, in slice order: the result is
-//              bitwise reproducible.  No MFMA: this is a matrix-vector
-//              product bound by HBM bandwidth.
+//   k_sp       one or two activation rows (the decode case): every
+//              wavefront takes 32 list positions of one half tile (256
+//              outputs) and loads them at once with 16-byte loads that
+//              cover 8 listed columns per instruction.
+//   k_run      3 to 16 rows: each wavefront walks a contiguous run of list
+//              positions of one half tile, every lane reading 2 bytes
+//              (4 outputs) of each listed column, with the next chunk's
+//              loads in flight while it computes the current one.
+// Both GEMV kernels dequantize exactly in fp16 (magic-number nibble
+// extraction, q - z in fp16) and accumulate with v_dot2_f32_f16 in fp32,
+// applying the group scale once per (group, output).  Lanes, wavefronts and
+// workgroups are combined in fixed orders (the last workgroup of a half tile
+// to arrive adds the others' published sums in slice order), so the result
+// is bitwise reproducible.  No MFMA: a matrix-vector product is bound by HBM
+// bandwidth and by the dequantization arithmetic, not by multiply-adds.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -39,6 +42,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kTileN = SGEMV_TILE_N;  // outputs per tile
 constexpr int kGroup = SGEMV_GROUP;
+constexpr int kCounterStride = 64;   // uint32 words between arrival counters
 constexpr int kChunk = 16;            // list positions a wavefront loads at once
 constexpr int kColBytes = kTileN / 2; // bytes of one column within one tile
 
@@ -55,7 +59,7 @@ struct RunArgs {
     const int32_t* idx;      // listed columns (unused when dense)
     const int32_t* count;    // number of listed columns (device)
     void* y;
-    uint32_t* counters;      // one arrival counter per tile
+    uint32_t* counters;      // one arrival counter per half tile, kCounterStride words apart
     float* partials;         // [tile][slice][Mt][512] slice sums
     uint32_t partial_bytes;  // size of the partials region
     int32_t K, ldx, ldy, M;
@@ -592,7 +596,7 @@ __global__ __launch_bounds__(Waves<MT>::kN * 64) void k_run(RunArgs a) {
         __builtin_amdgcn_s_waitcnt(0);  // stores acknowledged before the count
         uint32_t old = 0;
         if (lane == 0)
-            old = __hip_atomic_fetch_add(&a.counters[vt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __hip_atomic_fetch_add(&a.counters[vt * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         old = __builtin_amdgcn_readfirstlane(old);
         if (lane == 0) last_flag = (old == (uint32_t)(S - 1)) ? 1u : 0u;
     }
@@ -631,7 +635,424 @@ __global__ __launch_bounds__(Waves<MT>::kN * 64) void k_run(RunArgs a) {
     wg_tree(tot, red, wave, lane);
     if (wave == 0) {
         store_y(a, vt, lane, tot);
-        if (lane == 0) __hip_atomic_store(&a.counters[vt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(&a.counters[vt * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// sparse / dense GEMV for one or two rows
+// ---------------------------------------------------------------------------
+//
+// Memory first.  Listed columns are scattered 128-byte runs (one per half
+// tile).  On this GPU a wavefront load that fetches one such run per
+// instruction (4 bytes per lane) tops out near 2 TB/s, while loads that
+// fetch 16 bytes per lane from 8 different runs per instruction reach the
+// HBM limit.  So each lane reads 16 bytes of one column: lane
+// (c = lane / 8, o = lane % 8) reads bytes 16 o .. 16 o + 15 of the half
+// tile's run of its columns, which hold its 32 outputs 32 o .. 32 o + 31,
+// and one load instruction covers 8 listed columns.
+//
+// Work split.  A decode-time product is small next to the GPU (at 50 %
+// sparsity a 14336 -> 4096 matrix is about one 32-position chunk per
+// wavefront of the whole chip), so every wavefront takes exactly one chunk
+// of 32 list positions of one half tile and issues all its loads at once:
+// slot c owns positions 4c .. 4c + 3 (two column pairs for v_dot2).  A
+// workgroup of 8 wavefronts covers 256 consecutive positions; a half tile
+// has as many workgroups (slices) as its list needs, the rest of the grid,
+// sized for a full list, exits at once.
+//
+// Metadata.  The workgroup stages the scale/zero rows of the groups its
+// positions touch in LDS as (1024 + z | s) fp16 pairs (1024 + 16 z for odd
+// outputs).  Those loads are issued before the weight loads, so waiting for
+// them never waits for weights.  A lane handles its 4 positions group by
+// group (a ballot-driven loop, normally one pass), reading that group's
+// pairs for 8 of its outputs at a time.
+//
+// Sums.  The 8 slots of an output are combined by a fixed reduce-scatter
+// butterfly across lanes (each lane ends with 4 outputs), wavefronts by a
+// fixed-order LDS tree, slices as in the kernel above: bitwise reproducible.
+
+namespace sp {
+constexpr int kWaves = 8;
+constexpr int kCh = 32;                  // list positions per wavefront
+constexpr int kPos = kWaves * kCh;       // list positions per workgroup
+constexpr int kGCap = 24;                // scale/zero rows staged in LDS
+constexpr int kOut = 32;                 // outputs per lane while computing
+}  // namespace sp
+
+// Output (within the half tile) of sum d (0..3) that lane l keeps after the
+// per-8-output reduce-scatter over lane bits 3, 4, 5.
+__device__ __forceinline__ int sp_out(int lane, int d) {
+    return 32 * (lane & 7) + 8 * d + 4 * ((lane >> 3) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 5) & 1);
+}
+
+template <int MT>
+__device__ __forceinline__ void sp_store_y(const RunArgs& a, int vt, int lane, const float (&v)[MT][4]) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        if (m >= a.M) break;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const size_t n = (size_t)vt * kVTile + sp_out(lane, d);
+            if (a.out_f32) static_cast<float*>(a.y)[(size_t)m * a.ldy + n] = v[m][d];
+            else static_cast<_Float16*>(a.y)[(size_t)m * a.ldy + n] = (_Float16)v[m][d];
+        }
+    }
+}
+
+// (1024 + z | s) pair of an output from its stored (s | z) word; odd outputs
+// (high nibbles) use 1024 + 16 z.
+__device__ __forceinline__ uint32_t sp_zc(uint32_t sz_word, int odd) {
+    const half2_t sz = as_h2(sz_word);
+    const _Float16 zc = odd ? (_Float16)(sz.y * (_Float16)16.0f + (_Float16)1024.0f)
+                            : (_Float16)(sz.y + (_Float16)1024.0f);
+    return __builtin_bit_cast(uint32_t, (half2_t){zc, sz.x});
+}
+
+// Pairs (1024 + z | s) of 8 outputs 8d .. 8d + 7 of the lane's block for group g.
+__device__ __forceinline__ void sp_md8(const uint32_t (*s_md)[kVTile], const uint32_t* mdh, int gF, int staged,
+                                       int g, int blk, int d, uint32_t (&md)[8]) {
+    if (staged) {
+        int gi = g - gF;  // a list that is not ascending gives wrong results, never a stray access
+        gi = gi < 0 ? 0 : (gi >= sp::kGCap ? sp::kGCap - 1 : gi);
+        const u32x4* src = reinterpret_cast<const u32x4*>(&s_md[gi][blk * sp::kOut + 8 * d]);
+        const u32x4 u = src[0], v = src[1];
+        md[0] = u.x; md[1] = u.y; md[2] = u.z; md[3] = u.w;
+        md[4] = v.x; md[5] = v.y; md[6] = v.z; md[7] = v.w;
+    } else {
+        const u32x4* src = reinterpret_cast<const u32x4*>(mdh + (size_t)g * (2 * kVTile) + blk * sp::kOut + 8 * d);
+        const u32x4 u = src[0], v = src[1];
+        const uint32_t raw[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int r = 0; r < 8; ++r) md[r] = sp_zc(raw[r], r & 1);
+    }
+}
+
+template <int MT, bool DENSE, bool MASK>
+__global__ __launch_bounds__(sp::kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_sp(RunArgs a) {
+    __shared__ uint32_t s_md[sp::kGCap][kVTile];
+    __shared__ float red[sp::kWaves / 2][MT][kVTile];
+    __shared__ uint32_t last_flag;
+
+    const int T = a.tiles;
+    const int vt = blockIdx.x % T;
+    const int slice = blockIdx.x / T;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int K = a.K;
+    const int Gk = K / kGroup;
+
+    int count;
+    if (DENSE) {
+        count = K;
+    } else {
+        count = __builtin_amdgcn_readfirstlane(*a.count);
+        count = count < 0 ? 0 : (count > K ? K : count);
+    }
+    if (count == 0) {  // nothing listed: y = +0
+        if (slice == 0 && wave == 0) {
+            float z[MT][4];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) z[m][r] = 0.f;
+            sp_store_y(a, vt, lane, z);
+        }
+        return;
+    }
+    const int S = (count + sp::kPos - 1) / sp::kPos;   // slices in use
+    if (slice >= S) return;
+    const int P0 = slice * sp::kPos;
+    const int P1 = P0 + sp::kPos < count ? P0 + sp::kPos : count;
+
+    const int t = vt >> 1, hh = vt & 1;
+    const uint8_t* __restrict__ wcol = a.w + (size_t)t * K * (2 * kHalfRun) + hh * kHalfRun;
+    const uint32_t* __restrict__ mdh = a.md + (size_t)t * Gk * (2 * kVTile) + hh * kVTile;
+    const int slot = lane >> 3, blk = lane & 7;
+
+    // groups of the workgroup's first and last position
+    int gF, gL;
+    if (DENSE) {
+        gF = P0 >> 7;
+        gL = (P1 - 1) >> 7;
+    } else {
+        int f = a.idx[P0], l = a.idx[P1 - 1];
+        f = (unsigned)f < (unsigned)K ? f : K - 1;
+        l = (unsigned)l < (unsigned)K ? l : K - 1;
+        gF = __builtin_amdgcn_readfirstlane(f >> 7);
+        gL = __builtin_amdgcn_readfirstlane(l >> 7);
+    }
+    const int ng = gL - gF + 1;
+    const int staged = ng <= sp::kGCap;
+
+    // this wavefront's chunk and this lane's 4 positions of it
+    const int j0 = P0 + wave * sp::kCh;
+    const int nv = j0 < P1 ? (P1 - j0 < sp::kCh ? P1 - j0 : sp::kCh) : 0;
+    int kk[4];
+    uint32_t valid = 0;
+    if (nv > 0) {
+        const int jl = j0 + 4 * slot;   // j0 is a multiple of 32 below K: in the K-entry list
+        int4 k4;
+        if (DENSE) k4 = make_int4(jl, jl + 1, jl + 2, jl + 3);
+        else k4 = *reinterpret_cast<const int4*>(a.idx + jl);
+        const int kv[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool ok = 4 * slot + q < nv;
+            int k = kv[q];
+            k = (unsigned)k < (unsigned)K ? k : K - 1;
+            kk[q] = ok ? k : -1;
+            valid |= (ok ? 1u : 0u) << q;
+        }
+        // padding positions repeat a valid column of the lane (or of the chunk)
+        int kfill = -1;
+#pragma unroll
+        for (int q = 3; q >= 0; --q) kfill = kk[q] >= 0 ? kk[q] : kfill;
+        if (kfill < 0) {
+            int k = DENSE ? j0 : a.idx[j0];
+            kfill = (unsigned)k < (unsigned)K ? k : K - 1;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) kk[q] = kk[q] >= 0 ? kk[q] : kfill;
+    }
+
+    // 1. scale/zero rows of the workgroup's groups (issued first)
+    u32x4 mdraw[2];
+    int mdn = 0;
+    if (staged) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int e = threadIdx.x + r * sp::kWaves * 64;
+            if (e < ng * (kVTile / 4)) {
+                const int gi = e / (kVTile / 4), q = e % (kVTile / 4);
+                mdraw[r] = *reinterpret_cast<const u32x4*>(mdh + (size_t)(gF + gi) * (2 * kVTile) + 4 * q);
+                mdn = r + 1;
+            }
+        }
+    }
+    // 2. activations and weights of the lane's 4 columns
+    uint32_t xw[MT][4];
+    u32x4 w[4];
+    if (nv > 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int mr = m < a.M ? m : a.M - 1;  // rows past M are never stored
+                uint32_t v = a.x[(size_t)mr * a.ldx + kk[q]];
+                if (MASK && !is_active(v, code_of(a.tc, m))) v = 0;
+                xw[m][q] = ((valid >> q) & 1u) ? v : 0u;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            w[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wcol + (size_t)kk[q] * (2 * kHalfRun)) + blk);
+    }
+    // 3. stage the metadata
+    if (staged) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            if (r < mdn) {
+                const int e = threadIdx.x + r * sp::kWaves * 64;
+                const int gi = e / (kVTile / 4), q = e % (kVTile / 4);
+                const uint32_t raw[4] = {mdraw[r].x, mdraw[r].y, mdraw[r].z, mdraw[r].w};
+                *reinterpret_cast<u32x4*>(&s_md[gi][4 * q]) =
+                    (u32x4){sp_zc(raw[0], 0), sp_zc(raw[1], 1), sp_zc(raw[2], 0), sp_zc(raw[3], 1)};
+            }
+        }
+        for (int e = threadIdx.x + 2 * sp::kWaves * 64; e < ng * (kVTile / 4); e += sp::kWaves * 64) {
+            const int gi = e / (kVTile / 4), q = e % (kVTile / 4);
+            const u32x4 raw4 = *reinterpret_cast<const u32x4*>(mdh + (size_t)(gF + gi) * (2 * kVTile) + 4 * q);
+            *reinterpret_cast<u32x4*>(&s_md[gi][4 * q]) =
+                (u32x4){sp_zc(raw4.x, 0), sp_zc(raw4.y, 1), sp_zc(raw4.z, 0), sp_zc(raw4.w, 1)};
+        }
+    }
+    __syncthreads();
+
+    // 4. the lane's positions, 8 outputs at a time, group by group; then the
+    //    8 slots of those outputs: reduce-scatter over lane bits 3, 4, 5
+    const uint32_t vmagic = 0x64006400u | __builtin_amdgcn_mbcnt_lo(0u, 0u);  // per-lane (VGPR) copy
+    const bool b3 = (lane >> 3) & 1, b4 = (lane >> 4) & 1, b5 = (lane >> 5) & 1;
+    float v4[MT][4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        float y8[MT][8];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int r = 0; r < 8; ++r) y8[m][r] = 0.f;
+        uint32_t todo = valid;
+        while (__ballot(todo != 0) != 0ull) {
+            int g = gF;
+            if (todo) {
+                const int q0 = __builtin_ctz(todo);
+                g = kk[0] >> 7;
+#pragma unroll
+                for (int q = 1; q < 4; ++q) g = (q == q0) ? (kk[q] >> 7) : g;
+            }
+            uint32_t msk = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) msk |= (((todo >> q) & 1u) && ((kk[q] >> 7) == g)) ? (1u << q) : 0u;
+            todo &= ~msk;
+            uint32_t md[8];
+            sp_md8(s_md, mdh, gF, staged, g, blk, d, md);
+            float acc[MT][8];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) acc[m][r] = 0.f;
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                uint32_t xp[MT];
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const uint32_t lo = ((msk >> (2 * pr)) & 1u) ? xw[m][2 * pr] : 0u;
+                    const uint32_t hi = ((msk >> (2 * pr + 1)) & 1u) ? xw[m][2 * pr + 1] : 0u;
+                    xp[m] = lo | (hi << 16);
+                }
+                const u32x4 A = w[2 * pr], B = w[2 * pr + 1];
+                const uint32_t Ad = d == 0 ? A.x : d == 1 ? A.y : d == 2 ? A.z : A.w;
+                const uint32_t Bd = d == 0 ? B.x : d == 1 ? B.y : d == 2 ? B.z : B.w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    // byte i of the two columns into the low bytes of the two halves
+                    const uint32_t sel = (0x0Cu << 24) | ((uint32_t)i << 16) | (0x0Cu << 8) | (4u + i);
+                    const uint32_t R = __builtin_amdgcn_perm(Ad, Bd, sel);
+                    const _Float16 zl = as_h2(md[2 * i]).x, zh = as_h2(md[2 * i + 1]).x;
+                    const half2_t lo = as_h2(and_or(R, 0x000F000Fu, vmagic)) - (half2_t){zl, zl};  // q - z
+                    const half2_t hi = as_h2(and_or(R, 0x00F000F0u, vmagic)) - (half2_t){zh, zh};  // 16 (q - z)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        acc[m][2 * i] = __builtin_amdgcn_fdot2(lo, as_h2(xp[m]), acc[m][2 * i], false);
+                        acc[m][2 * i + 1] = __builtin_amdgcn_fdot2(hi, as_h2(xp[m]), acc[m][2 * i + 1], false);
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const float sc = (float)as_h2(md[r]).y;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) y8[m][r] = __builtin_fmaf(sc, acc[m][r], y8[m][r]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+            for (int r = 1; r < 8; r += 2) y8[m][r] *= 0.0625f;  // the 16 of the high nibbles
+            float t4[4], t2[2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float send = b3 ? y8[m][j] : y8[m][4 + j];
+                const float keep = b3 ? y8[m][4 + j] : y8[m][j];
+                t4[j] = keep + __shfl_xor(send, 8, 64);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float send = b4 ? t4[j] : t4[2 + j];
+                const float keep = b4 ? t4[2 + j] : t4[j];
+                t2[j] = keep + __shfl_xor(send, 16, 64);
+            }
+            const float send = b5 ? t2[0] : t2[1];
+            const float keep = b5 ? t2[1] : t2[0];
+            v4[m][d] = keep + __shfl_xor(send, 32, 64);
+        }
+    }
+
+    // 6. wavefronts: fixed-order tree (lane-major: lane l's 4 sums at 4 l)
+    const int o0 = 4 * lane;
+#pragma unroll
+    for (int hw = sp::kWaves / 2; hw >= 1; hw /= 2) {
+        if (wave >= hw && wave < 2 * hw) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                *reinterpret_cast<float4*>(&red[wave - hw][m][o0]) = make_float4(v4[m][0], v4[m][1], v4[m][2], v4[m][3]);
+        }
+        __syncthreads();
+        if (wave < hw) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float4 u = *reinterpret_cast<const float4*>(&red[wave][m][o0]);
+                v4[m][0] += u.x; v4[m][1] += u.y; v4[m][2] += u.z; v4[m][3] += u.w;
+            }
+        }
+        __syncthreads();
+    }
+
+    if (S == 1) {
+        if (wave == 0) sp_store_y(a, vt, lane, v4);
+        return;
+    }
+
+    // 7. publish this slice's sums (write-through), count the arrival; the
+    //    last workgroup of the half tile adds every slice in slice order
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc(a.partials, (short)0, (int)a.partial_bytes, 0x00020000);
+    const uint32_t tile_base = (uint32_t)vt * a.slices * MT * kVTile * 4u;
+    if (wave == 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint32_t off = tile_base + ((uint32_t)slice * MT + m) * kVTile * 4u + o0 * 4u;
+            const u32x4 v = {__float_as_uint(v4[m][0]), __float_as_uint(v4[m][1]),
+                             __float_as_uint(v4[m][2]), __float_as_uint(v4[m][3])};
+            __builtin_amdgcn_raw_buffer_store_b128(v, prs, off, 0, kCacheSC1);
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // stores acknowledged before the count
+        uint32_t old = 0;
+        if (lane == 0)
+            old = __hip_atomic_fetch_add(&a.counters[vt * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __builtin_amdgcn_readfirstlane(old);
+        if (lane == 0) last_flag = (old == (uint32_t)(S - 1)) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (last_flag == 0u) return;
+
+    float tot[MT][4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot[m][r] = 0.f;
+    for (int sl0 = wave; sl0 < S; sl0 += 4 * sp::kWaves) {
+        u32x4 u[4][MT];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int sl = sl0 + q * sp::kWaves;
+            const int sc = sl < S ? sl : sl0;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const uint32_t off = tile_base + ((uint32_t)sc * MT + m) * kVTile * 4u + o0 * 4u;
+                u[q][m] = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, kCacheSC1);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (sl0 + q * sp::kWaves >= S) break;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                tot[m][0] += __uint_as_float(u[q][m].x); tot[m][1] += __uint_as_float(u[q][m].y);
+                tot[m][2] += __uint_as_float(u[q][m].z); tot[m][3] += __uint_as_float(u[q][m].w);
+            }
+        }
+    }
+#pragma unroll
+    for (int hw = sp::kWaves / 2; hw >= 1; hw /= 2) {
+        if (wave >= hw && wave < 2 * hw) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                *reinterpret_cast<float4*>(&red[wave - hw][m][o0]) = make_float4(tot[m][0], tot[m][1], tot[m][2], tot[m][3]);
+        }
+        __syncthreads();
+        if (wave < hw) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float4 u = *reinterpret_cast<const float4*>(&red[wave][m][o0]);
+                tot[m][0] += u.x; tot[m][1] += u.y; tot[m][2] += u.z; tot[m][3] += u.w;
+            }
+        }
+        __syncthreads();
+    }
+    if (wave == 0) {
+        sp_store_y(a, vt, lane, tot);
+        if (lane == 0) __hip_atomic_store(&a.counters[vt * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -648,7 +1069,8 @@ int pow2_ceil(int m) {
 
 // Slices per tile: enough workgroups to cover the chip, never more slices
 // than 16-position chunks in a full list.
-int slices_for(const sgemv_desc* d) {
+int slices_for(const sgemv_desc* d, int mt) {
+    if (mt <= 2) return (d->K + sp::kPos - 1) / sp::kPos;  // one workgroup per 256 list positions
     const int tiles = d->N / kVTile;
     int s = (kTargetWGs + tiles / 2) / tiles;
     if (s < 1) s = 1;
@@ -701,11 +1123,13 @@ int check_desc(const sgemv_desc* d) {
     return SGEMV_OK;
 }
 
-size_t ws_counters_bytes(int tiles) { return ((size_t)tiles * 4 + 255) / 256 * 256; }
+// Each arrival counter sits on its own 256-byte line, so the atomics of
+// different half tiles go to different cache lines (and L2 channels).
+size_t ws_counters_bytes(int tiles) { return (size_t)tiles * kCounterStride * 4; }
 
 size_t ws_partial_bytes(const sgemv_desc* d, int mt) {
     const int tiles = d->N / kVTile;
-    const int s = slices_for(d);
+    const int s = slices_for(d, mt);
     return s > 1 ? (size_t)tiles * s * mt * kVTile * sizeof(float) : 0;
 }
 
@@ -713,8 +1137,12 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 template <int MT, bool DENSE, bool MASK>
 hipError_t launch_run(const RunArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)(a.tiles * a.slices));
-    hipLaunchKernelGGL((k_run<MT, DENSE, MASK>), grid, dim3(Waves<MT>::kN * 64), 0, s, a);
+    const dim3 grid((unsigned)(a.tiles * a.slices));  // slices: see slices_for
+    if (MT <= 2) {
+        hipLaunchKernelGGL((k_sp<(MT <= 2 ? MT : 1), DENSE, MASK>), grid, dim3(sp::kWaves * 64), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((k_run<MT, DENSE, MASK>), grid, dim3(Waves<MT>::kN * 64), 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -752,7 +1180,7 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
         if (st) return st;
     }
     a.tiles = d->N / kVTile;
-    a.slices = slices_for(d);
+    a.slices = slices_for(d, mt);
     const size_t pbytes = ws_partial_bytes(d, mt);
     if (a.slices > 1) {
         if (!ws) return SGEMV_EINVAL;
@@ -830,7 +1258,12 @@ extern "C" int sgemv_run_batched(const sgemv_desc* d, const void* packed, const 
 extern "C" size_t sgemv_workspace_bytes(const sgemv_desc* d, int32_t M) {
     if (check_desc(d) != SGEMV_OK || M < 1 || M > SGEMV_MAX_BATCH) return 0;
     const int tiles = d->N / kVTile;
-    return ws_counters_bytes(tiles) + ws_partial_bytes(d, pow2_ceil(M));
+    size_t part = 0;  // enough for every batch size up to M
+    for (int mt = 1; mt <= pow2_ceil(M); mt *= 2) {
+        const size_t b = ws_partial_bytes(d, mt);
+        part = b > part ? b : part;
+    }
+    return ws_counters_bytes(tiles) + part;
 }
 
 extern "C" const char* sgemv_strerror(int status) {

@@ -241,7 +241,7 @@ def main():
         "config": {"workload": "Llama-3-8B-shaped down_proj 14336->4096, batch 1, int4 g128, "
                                "50% magnitude sparsity (step = gather + sparse GEMV)",
                    "K": K_DOWN, "N": N_DOWN, "sparsity": 0.5, "weight_copies_rotated": R},
-        "roofline": {"bound": "hbm", "kernel": "k_run (sparse GEMV, M=1)",
+        "roofline": {"bound": "hbm", "kernel": "k_sp (sparse GEMV, M=1)",
                      "achieved": round(rb, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(rb / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": main_res["run_bytes"],
