@@ -66,6 +66,9 @@ struct RunArgs {
     int32_t tiles, slices;
     uint32_t out_f32;
     Codes tc;
+    int32_t* idx_out;        // fused kernel: list output (optional)
+    int32_t* count_out;      // fused kernel: count output (optional)
+    int32_t segs;            // fused kernel: 512-column segments
 };
 
 __device__ __forceinline__ uint32_t code_of(const Codes& c, int m) {
@@ -674,30 +677,47 @@ __global__ __launch_bounds__(Waves<MT>::kN * 64) void k_run(RunArgs a) {
 
 namespace sp {
 constexpr int kWaves = 8;
-constexpr int kCh = 32;                  // list positions per wavefront
-constexpr int kPos = kWaves * kCh;       // list positions per workgroup
-constexpr int kGCap = 24;                // scale/zero rows staged in LDS
+constexpr int kThreads = kWaves * 64;
+constexpr int kCh = 32;                  // list positions per wavefront and chunk
+constexpr int kPos = kWaves * kCh;       // list positions per workgroup (list-driven kernel)
+constexpr int kGCap = 24;                // scale/zero rows staged in LDS (list-driven kernel)
 constexpr int kOut = 32;                 // outputs per lane while computing
+constexpr int kSeg = 512;                // columns per workgroup (fused kernel)
+constexpr int kSegG = kSeg / kGroup;     // groups per segment
 }  // namespace sp
 
+__device__ __forceinline__ float u2f(uint32_t v) { return __uint_as_float(v); }
+__device__ __forceinline__ uint32_t f2u(float v) { return __float_as_uint(v); }
+
 // Output (within the half tile) of sum d (0..3) that lane l keeps after the
-// per-8-output reduce-scatter over lane bits 3, 4, 5.
+// reduce-scatter over lane bits 5, 4 and 3.
 __device__ __forceinline__ int sp_out(int lane, int d) {
-    return 32 * (lane & 7) + 8 * d + 4 * ((lane >> 3) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 5) & 1);
+    return 32 * (lane & 7) + 8 * d + 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
 }
 
-template <int MT>
-__device__ __forceinline__ void sp_store_y(const RunArgs& a, int vt, int lane, const float (&v)[MT][4]) {
+// Sum over the 8 slots (lane bits 5, 4, 3) of 8 per-lane sums v[0..7]
+// (outputs 8d .. 8d + 7 of the lane's block); each lane returns one output,
+// sp_out(lane, d).  Lane swaps, no LDS: the halves of the wavefront
+// exchange with v_permlane32_swap, rows of 16 with v_permlane16_swap, and
+// lanes 8 apart with a DPP row rotation.  Fixed order, so reproducible.
+__device__ __forceinline__ float sp_reduce8(const float (&v)[8], int lane) {
+    float t4[4], t2[2];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        if (m >= a.M) break;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const size_t n = (size_t)vt * kVTile + sp_out(lane, d);
-            if (a.out_f32) static_cast<float*>(a.y)[(size_t)m * a.ldy + n] = v[m][d];
-            else static_cast<_Float16*>(a.y)[(size_t)m * a.ldy + n] = (_Float16)v[m][d];
-        }
+    for (int j = 0; j < 4; ++j) {
+        // lanes 0-31 keep output j (own + partner's), lanes 32-63 output 4 + j
+        const auto r = __builtin_amdgcn_permlane32_swap(f2u(v[j]), f2u(v[4 + j]), false, false);
+        t4[j] = u2f(r[0]) + u2f(r[1]);
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        // even rows keep the lower pair, odd rows the upper pair
+        const auto r = __builtin_amdgcn_permlane16_swap(f2u(t4[j]), f2u(t4[2 + j]), false, false);
+        t2[j] = u2f(r[0]) + u2f(r[1]);
+    }
+    const bool b3 = (lane >> 3) & 1;
+    const float send = b3 ? t2[0] : t2[1];
+    const float keep = b3 ? t2[1] : t2[0];
+    return keep + u2f(__builtin_amdgcn_update_dpp(0u, f2u(send), 0x128 /* row_ror:8 */, 0xF, 0xF, false));
 }
 
 // (1024 + z | s) pair of an output from its stored (s | z) word; odd outputs
@@ -709,12 +729,13 @@ __device__ __forceinline__ uint32_t sp_zc(uint32_t sz_word, int odd) {
     return __builtin_bit_cast(uint32_t, (half2_t){zc, sz.x});
 }
 
-// Pairs (1024 + z | s) of 8 outputs 8d .. 8d + 7 of the lane's block for group g.
-__device__ __forceinline__ void sp_md8(const uint32_t (*s_md)[kVTile], const uint32_t* mdh, int gF, int staged,
-                                       int g, int blk, int d, uint32_t (&md)[8]) {
+// Pairs (1024 + z | s) of 8 outputs 8d .. 8d + 7 of the lane's block for
+// group g: from the rows gF .. gF + gcap - 1 staged in LDS, else from HBM.
+__device__ __forceinline__ void sp_md8(const uint32_t (*s_md)[kVTile], int gcap, const uint32_t* mdh, int gF,
+                                       int staged, int g, int blk, int d, uint32_t (&md)[8]) {
     if (staged) {
         int gi = g - gF;  // a list that is not ascending gives wrong results, never a stray access
-        gi = gi < 0 ? 0 : (gi >= sp::kGCap ? sp::kGCap - 1 : gi);
+        gi = gi < 0 ? 0 : (gi >= gcap ? gcap - 1 : gi);
         const u32x4* src = reinterpret_cast<const u32x4*>(&s_md[gi][blk * sp::kOut + 8 * d]);
         const u32x4 u = src[0], v = src[1];
         md[0] = u.x; md[1] = u.y; md[2] = u.z; md[3] = u.w;
@@ -728,152 +749,49 @@ __device__ __forceinline__ void sp_md8(const uint32_t (*s_md)[kVTile], const uin
     }
 }
 
-template <int MT, bool DENSE, bool MASK>
-__global__ __launch_bounds__(sp::kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_sp(RunArgs a) {
-    __shared__ uint32_t s_md[sp::kGCap][kVTile];
-    __shared__ float red[sp::kWaves / 2][MT][kVTile];
-    __shared__ uint32_t last_flag;
-
-    const int T = a.tiles;
-    const int vt = blockIdx.x % T;
-    const int slice = blockIdx.x / T;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int K = a.K;
-    const int Gk = K / kGroup;
-
-    int count;
-    if (DENSE) {
-        count = K;
-    } else {
-        count = __builtin_amdgcn_readfirstlane(*a.count);
-        count = count < 0 ? 0 : (count > K ? K : count);
+// Stage the scale/zero rows gF .. gF + ng - 1 of a half tile in LDS as
+// (1024 + z | s) pairs: thread e converts 4 words of row e / 64.  The
+// 16-byte loads of the first two rounds are issued by sp_md_issue before the
+// other loads of the kernel; sp_md_store writes them (and any further rows).
+struct SpMdRaw {
+    u32x4 v[2];
+};
+__device__ __forceinline__ void sp_md_issue(const uint32_t* mdh, int gF, int ng, SpMdRaw& r) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int e = threadIdx.x + i * sp::kThreads;
+        if (e < ng * (kVTile / 4))
+            r.v[i] = *reinterpret_cast<const u32x4*>(mdh + (size_t)(gF + e / (kVTile / 4)) * (2 * kVTile) +
+                                                     4 * (e % (kVTile / 4)));
     }
-    if (count == 0) {  // nothing listed: y = +0
-        if (slice == 0 && wave == 0) {
-            float z[MT][4];
+}
+__device__ __forceinline__ void sp_md_put(uint32_t (*s_md)[kVTile], int e, u32x4 raw) {
+    *reinterpret_cast<u32x4*>(&s_md[e / (kVTile / 4)][4 * (e % (kVTile / 4))]) =
+        (u32x4){sp_zc(raw.x, 0), sp_zc(raw.y, 1), sp_zc(raw.z, 0), sp_zc(raw.w, 1)};
+}
+__device__ __forceinline__ void sp_md_store(uint32_t (*s_md)[kVTile], const uint32_t* mdh, int gF, int ng,
+                                            const SpMdRaw& r) {
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) z[m][r] = 0.f;
-            sp_store_y(a, vt, lane, z);
-        }
-        return;
+    for (int i = 0; i < 2; ++i) {
+        const int e = threadIdx.x + i * sp::kThreads;
+        if (e < ng * (kVTile / 4)) sp_md_put(s_md, e, r.v[i]);
     }
-    const int S = (count + sp::kPos - 1) / sp::kPos;   // slices in use
-    if (slice >= S) return;
-    const int P0 = slice * sp::kPos;
-    const int P1 = P0 + sp::kPos < count ? P0 + sp::kPos : count;
+    for (int e = threadIdx.x + 2 * sp::kThreads; e < ng * (kVTile / 4); e += sp::kThreads)
+        sp_md_put(s_md, e, *reinterpret_cast<const u32x4*>(mdh + (size_t)(gF + e / (kVTile / 4)) * (2 * kVTile) +
+                                                          4 * (e % (kVTile / 4))));
+}
 
-    const int t = vt >> 1, hh = vt & 1;
-    const uint8_t* __restrict__ wcol = a.w + (size_t)t * K * (2 * kHalfRun) + hh * kHalfRun;
-    const uint32_t* __restrict__ mdh = a.md + (size_t)t * Gk * (2 * kVTile) + hh * kVTile;
-    const int slot = lane >> 3, blk = lane & 7;
-
-    // groups of the workgroup's first and last position
-    int gF, gL;
-    if (DENSE) {
-        gF = P0 >> 7;
-        gL = (P1 - 1) >> 7;
-    } else {
-        int f = a.idx[P0], l = a.idx[P1 - 1];
-        f = (unsigned)f < (unsigned)K ? f : K - 1;
-        l = (unsigned)l < (unsigned)K ? l : K - 1;
-        gF = __builtin_amdgcn_readfirstlane(f >> 7);
-        gL = __builtin_amdgcn_readfirstlane(l >> 7);
-    }
-    const int ng = gL - gF + 1;
-    const int staged = ng <= sp::kGCap;
-
-    // this wavefront's chunk and this lane's 4 positions of it
-    const int j0 = P0 + wave * sp::kCh;
-    const int nv = j0 < P1 ? (P1 - j0 < sp::kCh ? P1 - j0 : sp::kCh) : 0;
-    int kk[4];
-    uint32_t valid = 0;
-    if (nv > 0) {
-        const int jl = j0 + 4 * slot;   // j0 is a multiple of 32 below K: in the K-entry list
-        int4 k4;
-        if (DENSE) k4 = make_int4(jl, jl + 1, jl + 2, jl + 3);
-        else k4 = *reinterpret_cast<const int4*>(a.idx + jl);
-        const int kv[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const bool ok = 4 * slot + q < nv;
-            int k = kv[q];
-            k = (unsigned)k < (unsigned)K ? k : K - 1;
-            kk[q] = ok ? k : -1;
-            valid |= (ok ? 1u : 0u) << q;
-        }
-        // padding positions repeat a valid column of the lane (or of the chunk)
-        int kfill = -1;
-#pragma unroll
-        for (int q = 3; q >= 0; --q) kfill = kk[q] >= 0 ? kk[q] : kfill;
-        if (kfill < 0) {
-            int k = DENSE ? j0 : a.idx[j0];
-            kfill = (unsigned)k < (unsigned)K ? k : K - 1;
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) kk[q] = kk[q] >= 0 ? kk[q] : kfill;
-    }
-
-    // 1. scale/zero rows of the workgroup's groups (issued first)
-    u32x4 mdraw[2];
-    int mdn = 0;
-    if (staged) {
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int e = threadIdx.x + r * sp::kWaves * 64;
-            if (e < ng * (kVTile / 4)) {
-                const int gi = e / (kVTile / 4), q = e % (kVTile / 4);
-                mdraw[r] = *reinterpret_cast<const u32x4*>(mdh + (size_t)(gF + gi) * (2 * kVTile) + 4 * q);
-                mdn = r + 1;
-            }
-        }
-    }
-    // 2. activations and weights of the lane's 4 columns
-    uint32_t xw[MT][4];
-    u32x4 w[4];
-    if (nv > 0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const int mr = m < a.M ? m : a.M - 1;  // rows past M are never stored
-                uint32_t v = a.x[(size_t)mr * a.ldx + kk[q]];
-                if (MASK && !is_active(v, code_of(a.tc, m))) v = 0;
-                xw[m][q] = ((valid >> q) & 1u) ? v : 0u;
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            w[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wcol + (size_t)kk[q] * (2 * kHalfRun)) + blk);
-    }
-    // 3. stage the metadata
-    if (staged) {
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            if (r < mdn) {
-                const int e = threadIdx.x + r * sp::kWaves * 64;
-                const int gi = e / (kVTile / 4), q = e % (kVTile / 4);
-                const uint32_t raw[4] = {mdraw[r].x, mdraw[r].y, mdraw[r].z, mdraw[r].w};
-                *reinterpret_cast<u32x4*>(&s_md[gi][4 * q]) =
-                    (u32x4){sp_zc(raw[0], 0), sp_zc(raw[1], 1), sp_zc(raw[2], 0), sp_zc(raw[3], 1)};
-            }
-        }
-        for (int e = threadIdx.x + 2 * sp::kWaves * 64; e < ng * (kVTile / 4); e += sp::kWaves * 64) {
-            const int gi = e / (kVTile / 4), q = e % (kVTile / 4);
-            const u32x4 raw4 = *reinterpret_cast<const u32x4*>(mdh + (size_t)(gF + gi) * (2 * kVTile) + 4 * q);
-            *reinterpret_cast<u32x4*>(&s_md[gi][4 * q]) =
-                (u32x4){sp_zc(raw4.x, 0), sp_zc(raw4.y, 1), sp_zc(raw4.z, 0), sp_zc(raw4.w, 1)};
-        }
-    }
-    __syncthreads();
-
-    // 4. the lane's positions, 8 outputs at a time, group by group; then the
-    //    8 slots of those outputs: reduce-scatter over lane bits 3, 4, 5
+// One chunk of a wavefront: lane (slot, blk) holds listed columns kk[0..3]
+// (bit q of valid set where position q is in the list), their 16 weight
+// bytes w[q] (outputs 32 blk .. 32 blk + 31 of the half tile) and the
+// activations xw[m][q] (fp16 bits, 0 where masked).  Adds to v4[m][d] the
+// chunk's sum of output sp_out(lane, d).
+template <int MT>
+__device__ __forceinline__ void sp_chunk(const u32x4 (&w)[4], const uint32_t (&xw)[MT][4], const int (&kk)[4],
+                                         uint32_t valid, const uint32_t (*s_md)[kVTile], int gcap,
+                                         const uint32_t* mdh, int gF, int staged, int blk, int lane,
+                                         float (&v4)[MT][4]) {
     const uint32_t vmagic = 0x64006400u | __builtin_amdgcn_mbcnt_lo(0u, 0u);  // per-lane (VGPR) copy
-    const bool b3 = (lane >> 3) & 1, b4 = (lane >> 4) & 1, b5 = (lane >> 5) & 1;
-    float v4[MT][4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         float y8[MT][8];
@@ -895,7 +813,7 @@ __global__ __launch_bounds__(sp::kWaves * 64) __attribute__((amdgpu_waves_per_eu
             for (int q = 0; q < 4; ++q) msk |= (((todo >> q) & 1u) && ((kk[q] >> 7) == g)) ? (1u << q) : 0u;
             todo &= ~msk;
             uint32_t md[8];
-            sp_md8(s_md, mdh, gF, staged, g, blk, d, md);
+            sp_md8(s_md, gcap, mdh, gF, staged, g, blk, d, md);
             float acc[MT][8];
 #pragma unroll
             for (int m = 0; m < MT; ++m)
@@ -939,121 +857,365 @@ __global__ __launch_bounds__(sp::kWaves * 64) __attribute__((amdgpu_waves_per_eu
         for (int m = 0; m < MT; ++m) {
 #pragma unroll
             for (int r = 1; r < 8; r += 2) y8[m][r] *= 0.0625f;  // the 16 of the high nibbles
-            float t4[4], t2[2];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float send = b3 ? y8[m][j] : y8[m][4 + j];
-                const float keep = b3 ? y8[m][4 + j] : y8[m][j];
-                t4[j] = keep + __shfl_xor(send, 8, 64);
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float send = b4 ? t4[j] : t4[2 + j];
-                const float keep = b4 ? t4[2 + j] : t4[j];
-                t2[j] = keep + __shfl_xor(send, 16, 64);
-            }
-            const float send = b5 ? t2[0] : t2[1];
-            const float keep = b5 ? t2[1] : t2[0];
-            v4[m][d] = keep + __shfl_xor(send, 32, 64);
+            v4[m][d] += sp_reduce8(y8[m], lane);
         }
     }
+}
 
-    // 6. wavefronts: fixed-order tree (lane-major: lane l's 4 sums at 4 l)
-    const int o0 = 4 * lane;
+// Issue the weight loads of a lane's 4 columns.
+__device__ __forceinline__ void sp_load_w(const uint8_t* wcol, const int (&kk)[4], int blk, u32x4 (&w)[4]) {
 #pragma unroll
-    for (int hw = sp::kWaves / 2; hw >= 1; hw /= 2) {
-        if (wave >= hw && wave < 2 * hw) {
+    for (int q = 0; q < 4; ++q)
+        w[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wcol + (size_t)kk[q] * (2 * kHalfRun)) + blk);
+}
+
+template <int MT>
+struct SpShared {
+    float red[sp::kWaves][MT][kVTile];
+    uint32_t flag;
+};
+
+// Sum the workgroup's wavefronts and write y (S == 1), or publish the
+// workgroup's sums as slice `slice` of S and let the last workgroup of the
+// half tile to arrive add every slice in slice order and write y.  Every
+// thread of the workgroup calls it.  Thread t handles row t / 256 (MT = 2)
+// or, for MT = 1, output t % 256 (threads 256..511 help reading slices).
+template <int MT>
+__device__ __forceinline__ void sp_finish(const RunArgs& a, int vt, int slice, int S, int wave, int lane,
+                                          const float (&v4)[MT][4], SpShared<MT>& sh) {
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
-                *reinterpret_cast<float4*>(&red[wave - hw][m][o0]) = make_float4(v4[m][0], v4[m][1], v4[m][2], v4[m][3]);
-        }
-        __syncthreads();
-        if (wave < hw) {
+    for (int m = 0; m < MT; ++m)
+        *reinterpret_cast<float4*>(&sh.red[wave][m][4 * lane]) = make_float4(v4[m][0], v4[m][1], v4[m][2], v4[m][3]);
+    __syncthreads();
+    const int t = threadIdx.x;
+    const int o = t % kVTile;                 // lane-major slot: lane o / 4, sum o % 4
+    const int m = MT == 1 ? 0 : t / kVTile;
+    const int half = MT == 1 ? t / kVTile : 0;
+    const bool own = half == 0;
+    float sum = 0.f;
+    if (own) {
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const float4 u = *reinterpret_cast<const float4*>(&red[wave][m][o0]);
-                v4[m][0] += u.x; v4[m][1] += u.y; v4[m][2] += u.z; v4[m][3] += u.w;
-            }
-        }
-        __syncthreads();
+        for (int w = 0; w < sp::kWaves; ++w) sum += sh.red[w][m][o];
     }
-
+    const size_t n = (size_t)vt * kVTile + sp_out(o >> 2, o & 3);
     if (S == 1) {
-        if (wave == 0) sp_store_y(a, vt, lane, v4);
+        if (own && m < a.M) {
+            if (a.out_f32) static_cast<float*>(a.y)[(size_t)m * a.ldy + n] = sum;
+            else static_cast<_Float16*>(a.y)[(size_t)m * a.ldy + n] = (_Float16)sum;
+        }
         return;
     }
-
-    // 7. publish this slice's sums (write-through), count the arrival; the
-    //    last workgroup of the half tile adds every slice in slice order
     const __amdgpu_buffer_rsrc_t prs =
         __builtin_amdgcn_make_buffer_rsrc(a.partials, (short)0, (int)a.partial_bytes, 0x00020000);
     const uint32_t tile_base = (uint32_t)vt * a.slices * MT * kVTile * 4u;
-    if (wave == 0) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const uint32_t off = tile_base + ((uint32_t)slice * MT + m) * kVTile * 4u + o0 * 4u;
-            const u32x4 v = {__float_as_uint(v4[m][0]), __float_as_uint(v4[m][1]),
-                             __float_as_uint(v4[m][2]), __float_as_uint(v4[m][3])};
-            __builtin_amdgcn_raw_buffer_store_b128(v, prs, off, 0, kCacheSC1);
-        }
-        __builtin_amdgcn_s_waitcnt(0);  // stores acknowledged before the count
-        uint32_t old = 0;
-        if (lane == 0)
-            old = __hip_atomic_fetch_add(&a.counters[vt * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        old = __builtin_amdgcn_readfirstlane(old);
-        if (lane == 0) last_flag = (old == (uint32_t)(S - 1)) ? 1u : 0u;
+    if (own) {
+        const uint32_t off = tile_base + (((uint32_t)slice * MT + m) * kVTile + o) * 4u;
+        __builtin_amdgcn_raw_buffer_store_b32(f2u(sum), prs, off, 0, kCacheSC1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's store acknowledged
+    __syncthreads();                // ... and every thread's, before the count
+    if (t == 0) {
+        const uint32_t old =
+            __hip_atomic_fetch_add(&a.counters[vt * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh.flag = (old == (uint32_t)(S - 1)) ? 1u : 0u;
     }
     __syncthreads();
-    if (last_flag == 0u) return;
+    if (sh.flag == 0u) return;
 
-    float tot[MT][4];
+    // last to arrive: slices s0 .. s1 - 1 of this thread, 16 loads in flight
+    const int per = MT == 1 ? (S + 1) / 2 : S;
+    const int s0 = half * per;
+    const int s1 = s0 + per < S ? s0 + per : S;
+    float tot = 0.f;
+    for (int sb = s0; sb < s1; sb += 16) {
+        float v[16];
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+        for (int i = 0; i < 16; ++i) {
+            const int sl = sb + i < s1 ? sb + i : sb;
+            const uint32_t off = tile_base + (((uint32_t)sl * MT + m) * kVTile + o) * 4u;
+            v[i] = u2f(__builtin_amdgcn_raw_buffer_load_b32(prs, off, 0, kCacheSC1));
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) tot[m][r] = 0.f;
-    for (int sl0 = wave; sl0 < S; sl0 += 4 * sp::kWaves) {
-        u32x4 u[4][MT];
+        for (int i = 0; i < 16; ++i)
+            if (sb + i < s1) tot += v[i];
+    }
+    if (MT == 1) {  // add the second half's sum to the first's
+        if (!own) sh.red[0][0][o] = tot;
+        __syncthreads();
+        if (own) tot += sh.red[0][0][o];
+    }
+    if (own && m < a.M) {
+        if (a.out_f32) static_cast<float*>(a.y)[(size_t)m * a.ldy + n] = tot;
+        else static_cast<_Float16*>(a.y)[(size_t)m * a.ldy + n] = (_Float16)tot;
+    }
+    if (t == 0) __hip_atomic_store(&a.counters[vt * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// List-driven kernel: the list positions of the workgroup are
+// slice * 256 .. slice * 256 + 255 (one chunk per wavefront).
+template <int MT, bool DENSE, bool MASK>
+__global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_sp(RunArgs a) {
+    __shared__ uint32_t s_md[sp::kGCap][kVTile];
+    __shared__ SpShared<MT> sh;
+
+    const int T = a.tiles;
+    const int vt = blockIdx.x % T;
+    const int slice = blockIdx.x / T;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int slot = lane >> 3, blk = lane & 7;
+    const int K = a.K;
+    const int Gk = K / kGroup;
+    const int P0 = slice * sp::kPos;
+    const int j0 = P0 + wave * sp::kCh;   // this wavefront's chunk
+
+    // the count, the workgroup's first and (if the list is long enough) last
+    // entry, and the lane's 4 entries are read together
+    int count, f = 0, l = 0;
+    int4 k4 = make_int4(0, 0, 0, 0);
+    if (DENSE) {
+        count = K;
+    } else {
+        count = __builtin_amdgcn_readfirstlane(*a.count);
+        const int pl = P0 + sp::kPos - 1 < K ? P0 + sp::kPos - 1 : K - 1;
+        f = a.idx[P0 < K ? P0 : K - 1];
+        l = a.idx[pl];
+        int jl = j0 + 4 * slot;
+        jl = jl + 3 < K ? jl : K - 4;  // K is a multiple of 128: stays in the K-entry list, 16-byte aligned
+        k4 = *reinterpret_cast<const int4*>(a.idx + jl);
+    }
+    count = count < 0 ? 0 : (count > K ? K : count);
+    const int S = (count + sp::kPos - 1) / sp::kPos;   // slices in use
+    if (count == 0) {  // nothing listed: y = +0
+        if (slice == 0) {
+            const float z[MT][4] = {};
+            sp_finish<MT>(a, vt, 0, 1, wave, lane, z, sh);
+        }
+        return;
+    }
+    if (slice >= S) return;
+    const int P1 = P0 + sp::kPos < count ? P0 + sp::kPos : count;
+
+    const int tt = vt >> 1, hh = vt & 1;
+    const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
+    const uint32_t* __restrict__ mdh = a.md + (size_t)tt * Gk * (2 * kVTile) + hh * kVTile;
+
+    // groups of the workgroup's first and last position
+    int gF, gL;
+    if (DENSE) {
+        gF = P0 >> 7;
+        gL = (P1 - 1) >> 7;
+    } else {
+        if (P1 != P0 + sp::kPos) l = a.idx[P1 - 1];  // the last slice of the list
+        f = (unsigned)f < (unsigned)K ? f : K - 1;
+        l = (unsigned)l < (unsigned)K ? l : K - 1;
+        gF = __builtin_amdgcn_readfirstlane(f >> 7);
+        gL = __builtin_amdgcn_readfirstlane(l >> 7);
+    }
+    const int ng = gL - gF + 1;
+    const int staged = (ng >= 1 && ng <= sp::kGCap) ? 1 : 0;
+
+    // this lane's 4 positions
+    const int nv = j0 < P1 ? (P1 - j0 < sp::kCh ? P1 - j0 : sp::kCh) : 0;
+    int kk[4];
+    uint32_t valid = 0;
+    {
+        const int jl = j0 + 4 * slot;
+        const int kv[4] = {DENSE ? jl : k4.x, DENSE ? jl + 1 : k4.y, DENSE ? jl + 2 : k4.z, DENSE ? jl + 3 : k4.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int sl = sl0 + q * sp::kWaves;
-            const int sc = sl < S ? sl : sl0;
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const uint32_t off = tile_base + ((uint32_t)sc * MT + m) * kVTile * 4u + o0 * 4u;
-                u[q][m] = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, kCacheSC1);
-            }
+            const bool ok = 4 * slot + q < nv;
+            int k = kv[q];
+            k = (unsigned)k < (unsigned)K ? k : K - 1;
+            kk[q] = ok ? k : -1;
+            valid |= (ok ? 1u : 0u) << q;
         }
+        // padding positions repeat a valid column of the lane, else the workgroup's first
+        int kfill = f;
+#pragma unroll
+        for (int q = 3; q >= 0; --q) kfill = kk[q] >= 0 ? kk[q] : kfill;
+        if (DENSE && kfill < 0) kfill = P0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) kk[q] = kk[q] >= 0 ? kk[q] : kfill;
+    }
+
+    // 1. scale/zero rows (issued first), 2. activations and weights
+    SpMdRaw mdr;
+    if (staged) sp_md_issue(mdh, gF, ng, mdr);
+    uint32_t xw[MT][4];
+    u32x4 w[4];
+    if (nv > 0) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            if (sl0 + q * sp::kWaves >= S) break;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                tot[m][0] += __uint_as_float(u[q][m].x); tot[m][1] += __uint_as_float(u[q][m].y);
-                tot[m][2] += __uint_as_float(u[q][m].z); tot[m][3] += __uint_as_float(u[q][m].w);
+                const int mr = m < a.M ? m : a.M - 1;  // rows past M are never stored
+                uint32_t v = a.x[(size_t)mr * a.ldx + kk[q]];
+                if (MASK && !is_active(v, code_of(a.tc, mr))) v = 0;
+                xw[m][q] = ((valid >> q) & 1u) ? v : 0u;
             }
         }
+        sp_load_w(wcol, kk, blk, w);
     }
+    // 3. stage the metadata
+    if (staged) sp_md_store(s_md, mdh, gF, ng, mdr);
+    __syncthreads();
+
+    // 4. the chunk, 5. the sums
+    float v4[MT][4] = {};
+    if (nv > 0) sp_chunk<MT>(w, xw, kk, valid, s_md, sp::kGCap, mdh, gF, staged, blk, lane, v4);
+    sp_finish<MT>(a, vt, slice, S, wave, lane, v4, sh);
+}
+
+// ---------------------------------------------------------------------------
+// fused threshold + compact + sparse GEMV (one or two rows)
+// ---------------------------------------------------------------------------
+//
+// Workgroup (half tile vt, segment seg) owns columns seg * 512 ..
+// seg * 512 + 511: it reads their activations (one per thread and row),
+// thresholds them, and compacts the active columns in LDS with a wavefront
+// ballot and a scan over the 8 wavefront counts.  Its wavefronts then take
+// chunks of 32 of those columns exactly as the list-driven kernel does
+// (the scale/zero rows of the segment's 4 groups are staged while the
+// activations are in flight), and the segments of a half tile are summed as
+// its slices.  No global list and no count stand between thresholding and
+// the weight loads.
+//
+// When asked for, the workgroups of half tile 0 also write the global
+// list: a workgroup counts the active columns below its segment (reading
+// those activations again, from the caches) and stores its own columns
+// after them; the last segment's workgroup stores the count.
+
+// Number of columns below k_end that are active for some row (every thread
+// of the workgroup calls it; the result is the same in all).
+template <int MT>
+__device__ __forceinline__ uint32_t fs_prefix(const RunArgs& a, int k_end, uint32_t* s_tmp, int wave, int lane) {
+    uint32_t c = 0;
+    for (int e = 8 * threadIdx.x; e < k_end; e += 8 * sp::kThreads) {
+        uint32_t m8 = 0;
 #pragma unroll
-    for (int hw = sp::kWaves / 2; hw >= 1; hw /= 2) {
-        if (wave >= hw && wave < 2 * hw) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                *reinterpret_cast<float4*>(&red[wave - hw][m][o0]) = make_float4(tot[m][0], tot[m][1], tot[m][2], tot[m][3]);
+        for (int m = 0; m < MT; ++m) {
+            const int mr = m < a.M ? m : a.M - 1;
+            const uint4 v = *reinterpret_cast<const uint4*>(a.x + (size_t)mr * a.ldx + e);
+            m8 |= mask8_of(v, code_of(a.tc, mr));
         }
-        __syncthreads();
-        if (wave < hw) {
+        c += (uint32_t)__popc(m8);
+    }
+    uint32_t tot = 0;  // wavefront total from bit-plane ballots (c <= 8 * 16)
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const float4 u = *reinterpret_cast<const float4*>(&red[wave][m][o0]);
-                tot[m][0] += u.x; tot[m][1] += u.y; tot[m][2] += u.z; tot[m][3] += u.w;
-            }
+    for (int b = 0; b < 8; ++b) tot += (uint32_t)__popcll(__ballot((c >> b) & 1u)) << b;
+    if (lane == 0) s_tmp[wave] = tot;
+    __syncthreads();
+    uint32_t p = 0;
+#pragma unroll
+    for (int w = 0; w < sp::kWaves; ++w) p += s_tmp[w];
+    return p;
+}
+
+template <int MT>
+__global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_fs(RunArgs a) {
+    __shared__ uint32_t s_md[sp::kSegG][kVTile];
+    __shared__ __align__(16) int s_k[sp::kSeg];
+    __shared__ __align__(16) uint16_t s_x[MT][sp::kSeg];
+    __shared__ uint32_t s_cnt[2][sp::kWaves];
+    __shared__ SpShared<MT> sh;
+
+    const int T = a.tiles;
+    const int vt = blockIdx.x % T;
+    const int seg = blockIdx.x / T;
+    const int S = a.segs;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int slot = lane >> 3, blk = lane & 7;
+    const int t = threadIdx.x;
+    const int K = a.K;
+    const int Gk = K / kGroup;
+    const int k0 = seg * sp::kSeg;
+    const int kn = K - k0 < sp::kSeg ? K - k0 : sp::kSeg;   // a multiple of 128
+    const int gF = k0 / kGroup, ng = kn / kGroup;
+
+    const int tt = vt >> 1, hh = vt & 1;
+    const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
+    const uint32_t* __restrict__ mdh = a.md + (size_t)tt * Gk * (2 * kVTile) + hh * kVTile;
+
+    // 1. the segment's activations, then its scale/zero rows
+    uint32_t xr[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int mr = m < a.M ? m : a.M - 1;
+        xr[m] = t < kn ? a.x[(size_t)mr * a.ldx + k0 + t] : 0u;
+    }
+    SpMdRaw mdr;
+    sp_md_issue(mdh, gF, ng, mdr);
+
+    // 2. threshold, rank within the wavefront
+    bool act = false;
+    uint32_t xm[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int mr = m < a.M ? m : a.M - 1;
+        const bool am = t < kn && is_active(xr[m], code_of(a.tc, mr));
+        act = act || am;
+        xm[m] = am ? xr[m] : 0u;
+    }
+    const unsigned long long bal = __ballot(act);
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (lane == 0) s_cnt[0][wave] = (uint32_t)__popcll(bal);
+    sp_md_store(s_md, mdh, gF, ng, mdr);
+    __syncthreads();
+
+    // 3. compact: columns and their (masked) activations in list order
+    uint32_t base = 0, nact = 0;
+#pragma unroll
+    for (int w = 0; w < sp::kWaves; ++w) {
+        const uint32_t c = s_cnt[0][w];
+        base += w < wave ? c : 0u;
+        nact += c;
+    }
+    if (act) {
+        s_k[base + rank] = k0 + t;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) s_x[m][base + rank] = (uint16_t)xm[m];
+    }
+    __syncthreads();
+
+    // 4. the global list (first half tile only, on request)
+    if (a.idx_out && vt == 0) {
+        const uint32_t pre = fs_prefix<MT>(a, k0, s_cnt[1], wave, lane);
+        if (act) a.idx_out[pre + base + rank] = k0 + t;
+        if (seg == S - 1 && t == 0) *a.count_out = (int32_t)(pre + nact);
+    }
+
+    // 5. chunks of 32 listed columns per wavefront
+    const int nch = ((int)nact + sp::kCh - 1) / sp::kCh;
+    float v4[MT][4] = {};
+    for (int c = wave; c < nch; c += sp::kWaves) {
+        const int p0 = c * sp::kCh + 4 * slot;
+        const int4 k4 = *reinterpret_cast<const int4*>(&s_k[p0]);
+        const int kfirst = s_k[c * sp::kCh];
+        const int kv[4] = {k4.x, k4.y, k4.z, k4.w};
+        int kk[4];
+        uint32_t valid = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool ok = p0 + q < (int)nact;
+            int k = ok ? kv[q] : kfirst;
+            kk[q] = (unsigned)k < (unsigned)K ? k : K - 1;
+            valid |= (ok ? 1u : 0u) << q;
         }
-        __syncthreads();
+        u32x4 w[4];
+        sp_load_w(wcol, kk, blk, w);
+        uint32_t xw[MT][4];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint2 x4 = *reinterpret_cast<const uint2*>(&s_x[m][p0]);
+            const uint32_t xv[4] = {x4.x & 0xFFFFu, x4.x >> 16, x4.y & 0xFFFFu, x4.y >> 16};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xw[m][q] = ((valid >> q) & 1u) ? xv[q] : 0u;
+        }
+        sp_chunk<MT>(w, xw, kk, valid, s_md, sp::kSegG, mdh, gF, 1, blk, lane, v4);
     }
-    if (wave == 0) {
-        sp_store_y(a, vt, lane, tot);
-        if (lane == 0) __hip_atomic_store(&a.counters[vt * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    sp_finish<MT>(a, vt, seg, S, wave, lane, v4, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1216,7 +1378,64 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
     return SGEMV_OK;
 }
 
+int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx, const float* thr,
+              int32_t* idx, int32_t* count, void* y, int ldy, uint32_t flags, void* ws, void* stream) {
+    int st = check_desc(d);
+    if (st) return st;
+    if (!packed || !x || !y || !thr) return SGEMV_EINVAL;
+    if ((idx == nullptr) != (count == nullptr)) return SGEMV_EINVAL;
+    if (flags & ~SGEMV_OUT_F32) return SGEMV_EINVAL;
+    if (M < 1 || M > 2) return SGEMV_ESIZE;
+    if (ldx < d->K || ldy < d->N) return SGEMV_ESIZE;
+    if (ldx % 8 || ldy % 8) return SGEMV_EALIGN;
+    if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16)) return SGEMV_EALIGN;
+    if (idx && (!aligned(idx, 4) || !aligned(count, 4))) return SGEMV_EALIGN;
+
+    RunArgs a;
+    std::memset(&a, 0, sizeof a);
+    st = fill_codes(thr, M, a.tc);
+    if (st) return st;
+    a.tiles = d->N / kVTile;
+    a.slices = slices_for(d, M);   // stride of the partials region
+    a.segs = (d->K + sp::kSeg - 1) / sp::kSeg;
+    if (a.segs > 1) {
+        if (!ws) return SGEMV_EINVAL;
+        if (!aligned(ws, 256)) return SGEMV_EALIGN;
+    }
+    const uint8_t* blob = static_cast<const uint8_t*>(packed);
+    a.w = blob + d->w_off;
+    a.md = reinterpret_cast<const uint32_t*>(blob + d->m_off);
+    a.x = static_cast<const uint16_t*>(x);
+    a.y = y;
+    a.idx_out = idx;
+    a.count_out = count;
+    a.counters = static_cast<uint32_t*>(ws);
+    a.partials = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ws_counters_bytes(a.tiles)) : nullptr;
+    a.partial_bytes = (uint32_t)ws_partial_bytes(d, M);
+    a.K = d->K;
+    a.ldx = ldx;
+    a.ldy = ldy;
+    a.M = M;
+    a.out_f32 = (flags & SGEMV_OUT_F32) ? 1u : 0u;
+    const dim3 grid((unsigned)(a.tiles * a.segs));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (M == 1) hipLaunchKernelGGL((k_fs<1>), grid, dim3(sp::kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_fs<2>), grid, dim3(sp::kThreads), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return SGEMV_EHIP;
+    }
+    return SGEMV_OK;
+}
+
 }  // namespace
+
+extern "C" int sgemv_run_fused(const sgemv_desc* d, const void* packed, const void* x_f16, int32_t M,
+                               int32_t ldx, const float* thresholds, int32_t* idx, int32_t* count,
+                               void* y, int32_t ldy, uint32_t flags, void* workspace, void* stream) {
+    return run_fused(d, packed, x_f16, M, ldx, thresholds, idx, count, y, ldy, flags, workspace, stream);
+}
 
 extern "C" int sgemv_gather_indices(const void* x_f16, int32_t M, int32_t K, int32_t ldx,
                                     const float* thresholds, int32_t* idx, int32_t* count,

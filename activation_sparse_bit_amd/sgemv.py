@@ -27,7 +27,7 @@ SGEMV_TILE_N = 512
 SGEMV_MAX_BATCH = 16
 
 EXPORTED = ["sgemv_pack_layout", "sgemv_desc_from_header", "sgemv_gather_indices",
-            "sgemv_run", "sgemv_run_batched", "sgemv_workspace_bytes",
+            "sgemv_run", "sgemv_run_batched", "sgemv_run_fused", "sgemv_workspace_bytes",
             "sgemv_strerror", "sgemv_last_hip_error"]
 
 
@@ -71,6 +71,8 @@ def lib():
     L.sgemv_run.restype = ctypes.c_int
     L.sgemv_run_batched.argtypes = [pd, vp, vp, i32, i32, vp, vp, vp, vp, i32, u32, vp, vp]
     L.sgemv_run_batched.restype = ctypes.c_int
+    L.sgemv_run_fused.argtypes = [pd, vp, vp, i32, i32, vp, vp, vp, vp, i32, u32, vp, vp]
+    L.sgemv_run_fused.restype = ctypes.c_int
     L.sgemv_workspace_bytes.argtypes = [pd, i32]
     L.sgemv_workspace_bytes.restype = sz
     L.sgemv_strerror.argtypes = [ctypes.c_int]
@@ -120,7 +122,7 @@ def _thresholds(t, M):
 
 
 # ---------------------------------------------------------------------------
-# the four calls
+# the device and host calls
 # ---------------------------------------------------------------------------
 def sgemv_pack_layout(q, scales_f16, zeros_f16, tile_n: int = SGEMV_TILE_N):
     """Pack int4 codes q (uint8 [N][K]) and fp16 bit patterns of scales and
@@ -189,6 +191,19 @@ def sgemv_run_batched(desc: Desc, packed, x, thresholds, idx, count, y, workspac
                                    _ptr(t), _ptr(idx), _ptr(count), _ptr(y), y.stride(0),
                                    _flags(y), _ptr(workspace), _stream(stream)),
            "sgemv_run_batched")
+
+
+def sgemv_run_fused(desc: Desc, packed, x, thresholds, y, workspace, idx=None, count=None,
+                    stream=None):
+    """Threshold + compact + GEMV in one launch; x is [K] or [M][ldx] with
+    M <= 2, y matches; idx/count (optional) receive the active list."""
+    M = 1 if x.dim() == 1 else x.shape[0]
+    ldx = desc.K if x.dim() == 1 else x.stride(0)
+    ldy = desc.N if y.dim() == 1 else y.stride(0)
+    t = _thresholds(thresholds, M)
+    _check(lib().sgemv_run_fused(ctypes.byref(desc), _ptr(packed), _ptr(x), M, ldx, _ptr(t),
+                                 _ptr(idx), _ptr(count), _ptr(y), ldy, _flags(y),
+                                 _ptr(workspace), _stream(stream)), "sgemv_run_fused")
 
 
 def sgemv_workspace_bytes(desc: Desc, M: int = 1) -> int:

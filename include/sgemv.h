@@ -16,6 +16,8 @@
  *   sgemv_run             device: y = W . x over the listed columns (M = 1)
  *   sgemv_run_batched     device: M <= 16 rows over the union list, each row
  *                         masked by its own threshold
+ *   sgemv_run_fused       device: threshold, compact and GEMV in one launch
+ *                         (M <= 2), the list optional
  *
  * Weights.  W is [N][K] (output x input, like a Linear weight), quantized
  * asymmetrically to 4 bits with one fp16 scale s and one fp16 zero-point z
@@ -172,11 +174,12 @@ int sgemv_gather_indices(const void* x_f16, int32_t M, int32_t K, int32_t ldx,
  *   count      device int32 [1], 0 <= *count <= K (clamped to that range)
  *   y          device fp16 [N] (fp32 with SGEMV_OUT_F32), 16-byte aligned
  *   flags      0 or SGEMV_OUT_F32
- *   workspace  device, sgemv_workspace_bytes(d, 1) bytes, zero-filled once
- *              by the caller; every call leaves it zero-filled again (the
- *              per-tile arrival counters), so it can be reused for any
- *              later call on the same stream.  May be NULL when
- *              sgemv_workspace_bytes returns 0.
+ *   workspace  device, sgemv_workspace_bytes(d, 1) bytes, 256-byte
+ *              aligned, zero-filled once by the caller.  It holds one
+ *              arrival counter per 256 outputs, which every call returns to
+ *              zero, and scratch sums that need no clearing; so it can be
+ *              reused by any later call on the same stream.  May be NULL
+ *              when sgemv_workspace_bytes returns 0.
  */
 int sgemv_run(const sgemv_desc* d, const void* packed, const void* x_f16,
               const int32_t* idx, const int32_t* count, void* y,
@@ -204,8 +207,35 @@ int sgemv_run_batched(const sgemv_desc* d, const void* packed,
                       const int32_t* count, void* y, int32_t ldy,
                       uint32_t flags, void* workspace, void* stream);
 
-/* Bytes of workspace needed by sgemv_run (M = 1) or sgemv_run_batched with
- * up to M rows on matrix d; 0 for an invalid description. */
+/*
+ * sgemv_run_fused - the gathering step and the GEMV in one launch, so that
+ * no kernel boundary and no round trip through a global list separate the
+ * thresholding from the weight reads (the page's Abstract asks for index
+ * gathering with minimal overhead).  Each workgroup thresholds its own
+ * 512-column segment, compacts the active columns in LDS and reads only
+ * their weight bytes; segments are summed as in sgemv_run.
+ *   y[m][n] = sum over active k of w^[n][k] * xe[m][k]
+ * with xe and the union of active columns as in sgemv_run_batched (with
+ * thresholds), which it equals within the same error bound (the order of
+ * the fp32 additions differs, so the bits may differ).
+ *
+ *   M          1 or 2 (ESIZE otherwise; use sgemv_gather_indices and
+ *              sgemv_run_batched for more rows)
+ *   thresholds host float [M], each finite and >= 0 (required)
+ *   idx, count both NULL, or both device int32 ([K] and [1], 4-byte
+ *              aligned): then they receive exactly what
+ *              sgemv_gather_indices writes for the same x and thresholds
+ *   workspace  sgemv_workspace_bytes(d, M) bytes, same contract as above
+ * Other arguments as in sgemv_run_batched.  Bitwise reproducible.
+ */
+int sgemv_run_fused(const sgemv_desc* d, const void* packed, const void* x_f16,
+                    int32_t M, int32_t ldx, const float* thresholds,
+                    int32_t* idx, int32_t* count, void* y, int32_t ldy,
+                    uint32_t flags, void* workspace, void* stream);
+
+/* Bytes of workspace needed by sgemv_run (M = 1), sgemv_run_batched or
+ * sgemv_run_fused with up to M rows on matrix d; 0 for an invalid
+ * description. */
 size_t sgemv_workspace_bytes(const sgemv_desc* d, int32_t M);
 
 /* Static string for a status code. */

@@ -172,6 +172,37 @@ def test_run_batched_validation():
     assert L.sgemv_run_batched(pd, FAKE, FAKE, 4, K, tb.ctypes.data, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_EINVAL
 
 
+def test_run_fused_validation():
+    L = sgemv.lib()
+    E = sgemv
+    d = _desc()
+    pd = ctypes.byref(d)
+    t = np.array([0.5, 0.5, 0.5], dtype=np.float32)
+    tp = t.ctypes.data
+    K, N = d.K, d.N
+    f = L.sgemv_run_fused
+    assert f(None, FAKE, FAKE, 1, K, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_EINVAL
+    assert f(pd, None, FAKE, 1, K, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_EINVAL
+    assert f(pd, FAKE, None, 1, K, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_EINVAL
+    assert f(pd, FAKE, FAKE, 1, K, None, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_EINVAL
+    assert f(pd, FAKE, FAKE, 1, K, tp, FAKE, FAKE, None, N, 0, FAKE, None) == E.SGEMV_EINVAL
+    assert f(pd, FAKE, FAKE, 1, K, tp, FAKE, None, FAKE, N, 0, FAKE, None) == E.SGEMV_EINVAL  # idx without count
+    assert f(pd, FAKE, FAKE, 1, K, tp, None, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_EINVAL  # count without idx
+    assert f(pd, FAKE, FAKE, 1, K, tp, FAKE, FAKE, FAKE, N, 2, FAKE, None) == E.SGEMV_EINVAL
+    assert f(pd, FAKE, FAKE, 1, K, tp, None, None, FAKE, N, 0, None, None) == E.SGEMV_EINVAL  # no workspace
+    assert f(pd, FAKE, FAKE, 0, K, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_ESIZE
+    assert f(pd, FAKE, FAKE, 3, K, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_ESIZE
+    assert f(pd, FAKE, FAKE, 2, K - 8, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_ESIZE
+    assert f(pd, FAKE, FAKE, 2, K + 4, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_EALIGN
+    assert f(pd, FAKE, FAKE, 1, K, tp, FAKE, FAKE, FAKE + 4, N, 0, FAKE, None) == E.SGEMV_EALIGN
+    assert f(pd, FAKE, FAKE, 1, K, tp, FAKE + 2, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_EALIGN
+    assert f(pd, FAKE, FAKE, 1, K, tp, FAKE, FAKE, FAKE, N, 0, FAKE + 64, None) == E.SGEMV_EALIGN
+    tb = np.array([np.inf], dtype=np.float32)
+    assert f(pd, FAKE, FAKE, 1, K, tb.ctypes.data, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_EINVAL
+    d2 = _desc(N=4096, K=14336, tile=256)
+    assert f(ctypes.byref(d2), FAKE, FAKE, 1, K, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_EUNSUPPORTED
+
+
 def test_workspace_bytes():
     d = _desc()
     w1 = sgemv.sgemv_workspace_bytes(d, 1)

@@ -110,7 +110,7 @@ def _run_single(j, N, K, sigma, x, t, dtype=None, dense=False):
     sgemv.sgemv_gather_indices(xd, [t], idx, cnt)
     sgemv.sgemv_run(pm.desc, pm.blob, xd, idx, cnt, y, pm.workspace)
     torch.cuda.synchronize()
-    ws_nonzero = int(torch.count_nonzero(pm.workspace[:256]).item())
+    ws_nonzero = int(torch.count_nonzero(pm.workspace[:(N // 256) * 256]).item())
     assert ws_nonzero == 0, "arrival counters not reset"
     return y.float().cpu().numpy(), int(cnt.item())
 
