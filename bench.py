@@ -2,20 +2,23 @@
 
 Workload: the Llama-3-8B-shaped down projection, K = 14336 inputs ->
 N = 4096 outputs, int4 group-128 weights ~N(0, 0.02), activation
-x = silu(g) * u with g, u ~N(0, 1), magnitude-thresholded at 50 % (the step),
-with 70 % and 90 %, the dense int4 GEMV and the batched M = 1..16 union
-variant measured beside it.  Synthetic, seeded data.
+x = silu(g) * u with g, u ~N(0, 1), magnitude-thresholded at 50 % (the
+step); 70 % and 90 %, the two-launch path (gather + run), the dense int4
+GEMV and the batched M = 1..16 union variant are measured beside it.
+Synthetic, seeded data.
 
-One step = one pass of the hot path on one activation vector:
-threshold + compact (sgemv_gather_indices) then the sparse GEMV
-(sgemv_run), reading the weights of the next of R packed copies whose total
-exceeds 1 GiB so neither the L2 nor the 256 MB Infinity Cache can serve
-them.  Inputs are resident in HBM before timing starts.
+One step = one pass of the hot path on one activation vector: threshold,
+compact into the ascending list of active indices (written, with its
+count) and the sparse GEMV over those columns - one launch of
+sgemv_run_fused.  Every call reads the weights of the next of R packed
+copies whose total exceeds 1 GiB, so neither the L2 nor the 256 MB
+Infinity Cache can serve them.  Inputs are resident in HBM before timing.
 
-Prints one JSON line.  `value` is microseconds per step (lower is better);
-the effective HBM bandwidth of the sparse GEMV kernel and its fraction of
-the 8 TB/s peak are in `roofline`, measured with HIP events around every
-launch of that kernel on the stream it runs on.
+Prints one JSON line.  `value` is microseconds per step (lower is better).
+`roofline` gives, for the step's kernel, the algorithmic bytes of one
+launch divided by its average duration, against the 8 TB/s HBM peak.  The
+K timed steps are one HIP graph replay (launches back to back, as in a
+decode loop) bracketed by HIP events on the stream the kernels run on.
 """
 from __future__ import annotations
 
@@ -35,7 +38,7 @@ HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 1 << 30
 K_DOWN, N_DOWN = 14336, 4096
 KERNEL_SRC = os.path.join(ROOT, "activation_sparse_bit_amd", "csrc", "sgemv.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_run_down14336_p50_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fs_down14336_p50_traffic.json")
 
 
 def kernel_source_hash() -> str:
@@ -43,31 +46,26 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def run_bytes(A: int, Ag: int, N: int, M: int = 1) -> int:
-    """Algorithmic bytes of one sparse GEMV launch: listed weight columns
-    (N/2 bytes each), scale+zero of every touched group (4 bytes per output),
-    the index list, the gathered activations and the output."""
+def gemv_bytes(A: int, Ag: int, N: int, M: int = 1) -> int:
+    """Algorithmic bytes of the sparse GEMV over a given list: listed weight
+    columns (N/2 bytes each), scale+zero of every touched group (4 bytes per
+    output), the list, the gathered activations and the fp16 output."""
     return A * N // 2 + Ag * N * 4 + A * 4 + M * A * 2 + M * N * 2
 
 
 def gather_bytes(K: int, A: int, M: int = 1) -> int:
+    """Threshold + compact: the activations, the list and its count."""
     return M * K * 2 + A * 4 + 4
+
+
+def fused_bytes(A: int, Ag: int, N: int, K: int, M: int = 1, with_list: bool = True) -> int:
+    """One fused step: weight columns and metadata as above, every
+    activation once, the list and count (when written) and the output."""
+    return A * N // 2 + Ag * N * 4 + M * K * 2 + (A * 4 + 4 if with_list else 0) + M * N * 2
 
 
 def touched_groups(idx: np.ndarray) -> int:
     return int(np.unique(np.asarray(idx) // 128).size)
-
-
-class Timer:
-    """HIP-event timing of a sequence of launches on one stream."""
-
-    def __init__(self, torch, n):
-        self.torch = torch
-        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(n)]
-
-    def mean_ms(self, n):
-        return float(np.mean([a.elapsed_time(b) for a, b in self.ev[:n]]))
 
 
 def main():
@@ -76,7 +74,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--quick", action="store_true", help="only the 50%% step (for profiling)")
+    ap.add_argument("--quick", action="store_true", help="only the timed step (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy three times (counter calibration)")
     args = ap.parse_args()
@@ -91,7 +89,6 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
 
     # ---------------- inputs, resident in HBM ----------------
     q, s, z = synth.quantized_weights(0, N_DOWN, K_DOWN, 0.02)
@@ -107,75 +104,108 @@ def main():
     cnt = torch.zeros(1, dtype=torch.int32, device=dev)
     y = torch.empty(N_DOWN, dtype=torch.float16, device=dev)
 
-    def measure(p, steps, warmup, dense=False):
-        t = synth.percentile_threshold(x, p)
-        gath = Timer(torch, steps)
-        runt = Timer(torch, steps)
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def graph_time(launches, steps, warmup):
+        """Capture `steps` steps (each step calls every launch with the step
+        number, on the current stream) in one HIP graph, then time one replay
+        bracketed by synchronisations.  Returns microseconds per step.  A
+        graph replay puts the launches back to back, as a decode loop does;
+        eager Python launches would leave the GPU waiting for the host."""
         for i in range(warmup):
-            if not dense:
-                sgemv.sgemv_gather_indices(xd, [t], idx, cnt, stream=stream)
-            sgemv.sgemv_run(desc, copies[i % R], xd, None if dense else idx, None if dense else cnt,
-                            y, ws, stream=stream)
+            for f in launches:
+                f(i)
         torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for i in range(steps):
-            if not dense:
-                gath.ev[i][0].record(stream)
-                sgemv.sgemv_gather_indices(xd, [t], idx, cnt, stream=stream)
-                gath.ev[i][1].record(stream)
-            runt.ev[i][0].record(stream)
-            sgemv.sgemv_run(desc, copies[i % R], xd, None if dense else idx, None if dense else cnt,
-                            y, ws, stream=stream)
-            runt.ev[i][1].record(stream)
-        t1.record(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                for f in launches:
+                    f(i)
+        g.replay()                      # upload and first replay, untimed
         torch.cuda.synchronize()
-        total_ms = t0.elapsed_time(t1)
+        t0, t1 = ev(), ev()
+        cur = torch.cuda.current_stream()
+        t0.record(cur)
+        g.replay()
+        t1.record(cur)
+        torch.cuda.synchronize()
+        del g
+        return t0.elapsed_time(t1) * 1000.0 / steps
+
+    def eager_latency(launch, n=50):
+        """Mean duration of single launches issued one at a time (events
+        around each, GPU idle in between): the latency of one call."""
+        ms = []
+        for i in range(n):
+            a, b = ev(), ev()
+            cur = torch.cuda.current_stream()
+            a.record(cur)
+            launch(i)
+            b.record(cur)
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return float(np.mean(ms) * 1000.0)
+
+    def list_now():
+        c = int(cnt.item())
+        lst = idx[:c].cpu().numpy()
+        return c, touched_groups(lst)
+
+    def measure_fused(p, steps, warmup, with_list=True, latency=False):
+        t = synth.percentile_threshold(x, p)
+        il, cl = (idx, cnt) if with_list else (None, None)
+        f = lambda i: sgemv.sgemv_run_fused(desc, copies[i % R], xd, [t], y, ws, il, cl)
+        us = graph_time([f], steps, warmup)
+        sgemv.sgemv_run_fused(desc, copies[0], xd, [t], y, ws, idx, cnt)
+        A, Ag = list_now()
+        fb = fused_bytes(A, Ag, N_DOWN, K_DOWN, with_list=with_list)
+        out = {"p": p, "active": A, "groups_touched": Ag, "us_per_step": us, "bytes": fb,
+               "GBps": fb / (us * 1e-6) / 1e9, "frac_hbm_peak": fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        if latency:
+            out["single_call_latency_us"] = eager_latency(f)
+        return out
+
+    def measure_split(p, steps, warmup, dense=False):
+        t = synth.percentile_threshold(x, p)
+        gat = lambda i: sgemv.sgemv_gather_indices(xd, [t], idx, cnt)
+        run = lambda i: sgemv.sgemv_run(desc, copies[i % R], xd, None if dense else idx,
+                                        None if dense else cnt, y, ws)
+        out = {"p": p}
         if dense:
             A, Ag = K_DOWN, K_DOWN // 128
+            out["us_per_step"] = graph_time([run], steps, warmup)
+            rb = K_DOWN * N_DOWN // 2 + Ag * N_DOWN * 4 + K_DOWN * 2 + N_DOWN * 2
+            run_us = out["us_per_step"]
         else:
-            c = int(cnt.item())
-            lst = idx[:c].cpu().numpy()
-            A, Ag = c, touched_groups(lst)
-        run_ms = runt.mean_ms(steps)
-        gat_ms = gath.mean_ms(steps) if not dense else 0.0
-        rb = run_bytes(A, Ag, N_DOWN)
-        return {
-            "p": p, "active": A, "groups_touched": Ag,
-            "us_per_step": total_ms * 1000.0 / steps,
-            "us_run": run_ms * 1000.0, "us_gather": gat_ms * 1000.0,
-            "run_bytes": rb, "run_GBps": rb / (run_ms * 1e-3) / 1e9,
-            "run_frac_hbm_peak": rb / (run_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-            "gather_bytes": 0 if dense else gather_bytes(K_DOWN, A),
-        }
+            out["us_per_step"] = graph_time([gat, run], steps, warmup)
+            out["gather_us"] = graph_time([gat], steps, warmup)
+            run_us = graph_time([run], steps, warmup)
+            A, Ag = list_now()
+            rb = gemv_bytes(A, Ag, N_DOWN)
+            out["gather_bytes"] = gather_bytes(K_DOWN, A)
+        out.update({"active": A, "groups_touched": Ag, "run_us": run_us, "run_bytes": rb,
+                    "run_GBps": rb / (run_us * 1e-6) / 1e9,
+                    "run_frac_hbm_peak": rb / (run_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
+        return out
 
     def measure_batched(M, steps, warmup):
         X = np.stack([synth.glu_activation(m, K_DOWN) for m in range(M)])
         ts = [synth.percentile_threshold(X[m], 0.7) for m in range(M)]
         Xd = torch.from_numpy(X).to(dev)
         Y = torch.empty((M, N_DOWN), dtype=torch.float16, device=dev)
-        runt = Timer(torch, steps)
-        for i in range(warmup):
-            sgemv.sgemv_gather_indices(Xd, ts, idx, cnt, stream=stream)
-            sgemv.sgemv_run_batched(desc, copies[i % R], Xd, ts, idx, cnt, Y, ws, stream=stream)
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for i in range(steps):
-            sgemv.sgemv_gather_indices(Xd, ts, idx, cnt, stream=stream)
-            runt.ev[i][0].record(stream)
-            sgemv.sgemv_run_batched(desc, copies[i % R], Xd, ts, idx, cnt, Y, ws, stream=stream)
-            runt.ev[i][1].record(stream)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        c = int(cnt.item())
-        A, Ag = c, touched_groups(idx[:c].cpu().numpy())
-        run_ms = runt.mean_ms(steps)
-        rb = run_bytes(A, Ag, N_DOWN, M)
-        return {"M": M, "active": A, "us_per_step": t0.elapsed_time(t1) * 1000.0 / steps,
-                "us_run": run_ms * 1000.0, "run_GBps": rb / (run_ms * 1e-3) / 1e9}
+        gat = lambda i: sgemv.sgemv_gather_indices(Xd, ts, idx, cnt)
+        run = lambda i: sgemv.sgemv_run_batched(desc, copies[i % R], Xd, ts, idx, cnt, Y, ws)
+        step_us = graph_time([gat, run], steps, warmup)
+        run_us = graph_time([run], steps, warmup)
+        A, Ag = list_now()
+        rb = gemv_bytes(A, Ag, N_DOWN, M)
+        res = {"M": M, "active_union": A, "us_per_step": step_us, "run_us": run_us,
+               "run_GBps": rb / (run_us * 1e-6) / 1e9}
+        if M <= 2:
+            res["fused_us_per_step"] = graph_time(
+                [lambda i: sgemv.sgemv_run_fused(desc, copies[i % R], Xd, ts, Y, ws, idx, cnt)], steps, warmup)
+        return res
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -186,20 +216,23 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # ---------------- the timed step: 50 % ----------------
+    # ---------------- the timed step: 50 %, fused, list written ----------------
     torch.cuda.synchronize()
-    main_res = measure(0.5, args.steps, args.warmup)
-    sweep = {"p50": main_res}
+    main_res = measure_fused(0.5, args.steps, args.warmup, latency=not args.quick)
+    sweep = {"fused_p50": main_res}
     batched = []
     if not args.quick:
         for p in (0.7, 0.9):
-            sweep[f"p{int(p * 100)}"] = measure(p, args.steps, args.warmup)
-        sweep["dense"] = measure(0.0, args.steps, args.warmup, dense=True)
+            sweep[f"fused_p{int(p * 100)}"] = measure_fused(p, args.steps, args.warmup)
+        sweep["fused_p50_no_list"] = measure_fused(0.5, args.steps, args.warmup, with_list=False)
+        for p in (0.5, 0.7, 0.9):
+            sweep[f"split_p{int(p * 100)}"] = measure_split(p, args.steps, args.warmup)
+        sweep["dense_int4"] = measure_split(0.0, args.steps, args.warmup, dense=True)
+        dense_us = sweep["dense_int4"]["us_per_step"]
+        for k in ("fused_p50", "fused_p70", "fused_p90", "split_p50", "split_p70", "split_p90"):
+            sweep[k]["speedup_vs_dense_int4"] = dense_us / sweep[k]["us_per_step"]
         for M in (1, 2, 4, 8, 16):
             batched.append(measure_batched(M, max(20, args.steps // 4), max(5, args.warmup // 4)))
-        dense_us = sweep["dense"]["us_run"]
-        for k in ("p50", "p70", "p90"):
-            sweep[k]["speedup_vs_dense_int4"] = dense_us / sweep[k]["us_per_step"]
 
     # ---------------- HBM traffic from committed counters ----------------
     traffic = None
@@ -216,17 +249,18 @@ def main():
         t = synth.percentile_threshold(x, 0.5)
         n_calls, t_start = 0, time.perf_counter()
         while True:
+            oracle.active_indices(x, t)
             oracle.gemv_masked(q, s, z, x, t)
             n_calls += 1
             if time.perf_counter() - t_start > 10.0 or n_calls >= 50:
                 break
         el = time.perf_counter() - t_start
         cpu = {"value": el / n_calls * 1e6, "unit": "us/call", "cores": 1, "kind": "oracle",
-               "sample": f"{n_calls} full calls of the fp64 oracle (threshold, union, per-column "
+               "sample": f"{n_calls} full calls of the fp64 oracle (threshold, compact, per-column "
                          f"dequantize and accumulate) on the 14336->4096 @50% input; "
                          f"single-threaded NumPy"}
 
-    rb = main_res["run_GBps"]
+    kmean = main_res["us_per_step"]   # one launch per step
     out = {
         "metric": "µs/call + effective HBM GB/s (% of peak), sparse int4 GEMV 14336→4096 @50/90%",
         "value": round(main_res["us_per_step"], 3),
@@ -239,13 +273,14 @@ def main():
         "dtype": "int4xfp16->fp32",
         "data": "synthetic (seeded Gaussian weights quantized to int4 g128; x = silu(g)*u)",
         "config": {"workload": "Llama-3-8B-shaped down_proj 14336->4096, batch 1, int4 g128, "
-                               "50% magnitude sparsity (step = gather + sparse GEMV)",
+                               "50% magnitude sparsity; step = threshold + compact (list written) + "
+                               "sparse GEMV in one launch",
                    "K": K_DOWN, "N": N_DOWN, "sparsity": 0.5, "weight_copies_rotated": R},
-        "roofline": {"bound": "hbm", "kernel": "k_sp (sparse GEMV, M=1)",
-                     "achieved": round(rb, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(rb / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": main_res["run_bytes"],
-                     "avg_launch_us": round(main_res["us_run"], 3)},
+        "roofline": {"bound": "hbm", "kernel": "k_fs<1> (fused threshold + compact + sparse GEMV)",
+                     "achieved": round(main_res["GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(main_res["frac_hbm_peak"], 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": main_res["bytes"],
+                     "avg_launch_us": round(kmean, 3)},
         "cpu_baseline": cpu,
         "sweep": sweep,
         "batched_p70": batched,
