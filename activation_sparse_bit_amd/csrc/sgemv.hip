@@ -113,14 +113,23 @@ __device__ __forceinline__ void wave_scan16(uint32_t c, uint32_t& prefix, uint32
     }
 }
 
-__global__ __launch_bounds__(1024) void k_gather(const uint16_t* __restrict__ x, int M, int K, int ldx,
-                                                 Codes tc, int32_t* __restrict__ idx,
-                                                 int32_t* __restrict__ count) {
-    __shared__ uint8_t masks[SGEMV_MAX_K / 8];
-    __shared__ uint32_t wtot[16];
+// The list for rows x[0..M) by one workgroup of W wavefronts: wavefront w
+// owns the K / W consecutive columns w K / W ..; pass 1 builds per-lane
+// 8-column masks (kept in LDS) and counts, an LDS exchange of the
+// wavefront totals gives every wavefront its base, pass 2 writes the
+// columns in order.
+struct GatherShared {
+    uint8_t masks[SGEMV_MAX_K / 8];
+    uint32_t wtot[16];
+};
+
+template <int W>
+__device__ __forceinline__ void gather_body(const uint16_t* __restrict__ x, int M, int K, int ldx, const Codes& tc,
+                                            int32_t* __restrict__ idx, int32_t* __restrict__ count,
+                                            GatherShared& gs) {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int Kw = K >> 4;          // elements per wavefront, a multiple of 8
+    const int Kw = K / W;           // columns per wavefront, a multiple of 8
     const int base = wave * Kw;
 
     uint32_t mytotal = 0;
@@ -132,18 +141,18 @@ __global__ __launch_bounds__(1024) void k_gather(const uint16_t* __restrict__ x,
                 const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)m * ldx + base + off);
                 m8 |= mask8_of(v, code_of(tc, m));
             }
-            masks[(base + off) >> 3] = (uint8_t)m8;
+            gs.masks[(base + off) >> 3] = (uint8_t)m8;
         }
         uint32_t pre, tot;
         wave_scan16((uint32_t)__popc(m8), pre, tot);
         mytotal += tot;
     }
-    if (lane == 0) wtot[wave] = mytotal;
+    if (lane == 0) gs.wtot[wave] = mytotal;
     __syncthreads();
     uint32_t wbase = 0, grand = 0;
 #pragma unroll
-    for (int w = 0; w < 16; ++w) {
-        const uint32_t t = wtot[w];
+    for (int w = 0; w < W; ++w) {
+        const uint32_t t = gs.wtot[w];
         wbase += (w < wave) ? t : 0u;
         grand += t;
     }
@@ -152,7 +161,7 @@ __global__ __launch_bounds__(1024) void k_gather(const uint16_t* __restrict__ x,
     uint32_t running = wbase;
     for (int s = 0; s * 512 < Kw; ++s) {
         const int off = s * 512 + lane * 8;
-        uint32_t m8 = (off < Kw) ? masks[(base + off) >> 3] : 0u;
+        uint32_t m8 = (off < Kw) ? gs.masks[(base + off) >> 3] : 0u;
         uint32_t pre, tot;
         wave_scan16((uint32_t)__popc(m8), pre, tot);
         uint32_t pos = running + pre;
@@ -163,6 +172,13 @@ __global__ __launch_bounds__(1024) void k_gather(const uint16_t* __restrict__ x,
         }
         running += tot;
     }
+}
+
+__global__ __launch_bounds__(1024) void k_gather(const uint16_t* __restrict__ x, int M, int K, int ldx,
+                                                 Codes tc, int32_t* __restrict__ idx,
+                                                 int32_t* __restrict__ count) {
+    __shared__ GatherShared gs;
+    gather_body<16>(x, M, K, ldx, tc, idx, count, gs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1072,150 +1088,187 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
 // ---------------------------------------------------------------------------
 //
 // Workgroup (half tile vt, segment seg) owns columns seg * 512 ..
-// seg * 512 + 511: it reads their activations (one per thread and row),
-// thresholds them, and compacts the active columns in LDS with a wavefront
-// ballot and a scan over the 8 wavefront counts.  Its wavefronts then take
-// chunks of 32 of those columns exactly as the list-driven kernel does
-// (the scale/zero rows of the segment's 4 groups are staged while the
-// activations are in flight), and the segments of a half tile are summed as
-// its slices.  No global list and no count stand between thresholding and
-// the weight loads.
+// seg * 512 + 511, and its wavefront w the 64 columns seg * 512 + 64 w ..,
+// which lie in one quantization group.  Every wavefront works on its own
+// until the final sums, with no workgroup barrier:
+//   1. it loads its 64 activations (one per lane and row) and its group's
+//      scale/zero row for the half tile (16 bytes per lane);
+//   2. thresholds them, ranks the active lanes with a ballot and mbcnt, and
+//      writes the active columns and their masked activations to its own
+//      LDS rows, beside the converted (1024 + z | s) pairs;
+//   3. splits its n active columns over the 8 slots, ceil(n / 16) column
+//      pairs per lane, and issues all their 16-byte weight loads at once;
+//   4. dequantizes and accumulates per lane (one group: the scale is applied
+//      once per output), and sums the slots with lane swaps.
+// The workgroup then sums its wavefronts, and the segments of a half tile
+// are added as slices (as in the list-driven kernel).
 //
-// When asked for, the workgroups of half tile 0 also write the global
-// list: a workgroup counts the active columns below its segment (reading
-// those activations again, from the caches) and stores its own columns
-// after them; the last segment's workgroup stores the count.
+// When the global list is asked for, one more workgroup (block 0) writes it
+// with the gathering routine while the others compute; it reads only the
+// activations.
 
-// Number of columns below k_end that are active for some row (every thread
-// of the workgroup calls it; the result is the same in all).
+constexpr int kFsMaxPairs = 4;   // 64 columns over 8 slots: at most 4 pairs per lane
+
 template <int MT>
-__device__ __forceinline__ uint32_t fs_prefix(const RunArgs& a, int k_end, uint32_t* s_tmp, int wave, int lane) {
-    uint32_t c = 0;
-    for (int e = 8 * threadIdx.x; e < k_end; e += 8 * sp::kThreads) {
-        uint32_t m8 = 0;
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int mr = m < a.M ? m : a.M - 1;
-            const uint4 v = *reinterpret_cast<const uint4*>(a.x + (size_t)mr * a.ldx + e);
-            m8 |= mask8_of(v, code_of(a.tc, mr));
-        }
-        c += (uint32_t)__popc(m8);
-    }
-    uint32_t tot = 0;  // wavefront total from bit-plane ballots (c <= 8 * 16)
-#pragma unroll
-    for (int b = 0; b < 8; ++b) tot += (uint32_t)__popcll(__ballot((c >> b) & 1u)) << b;
-    if (lane == 0) s_tmp[wave] = tot;
-    __syncthreads();
-    uint32_t p = 0;
-#pragma unroll
-    for (int w = 0; w < sp::kWaves; ++w) p += s_tmp[w];
-    return p;
-}
+struct FsShared {
+    uint32_t md[sp::kWaves][kVTile];                 // per wavefront: its group's (1024 + z | s) pairs
+    __align__(16) int k[sp::kWaves][64];            // per wavefront: its active columns
+    __align__(16) uint16_t xs[sp::kWaves][MT][64];  // ... and their masked activations
+};
+
+template <int MT>
+union FsLds {
+    struct {
+        FsShared<MT> f;
+        SpShared<MT> sh;
+    } g;
+    GatherShared gl;
+};
 
 template <int MT>
 __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_fs(RunArgs a) {
-    __shared__ uint32_t s_md[sp::kSegG][kVTile];
-    __shared__ __align__(16) int s_k[sp::kSeg];
-    __shared__ __align__(16) uint16_t s_x[MT][sp::kSeg];
-    __shared__ uint32_t s_cnt[2][sp::kWaves];
-    __shared__ SpShared<MT> sh;
+    __shared__ FsLds<MT> lds;
+    int bid = blockIdx.x;
+    if (a.idx_out) {  // block 0 writes the list
+        if (bid == 0) {
+            gather_body<sp::kWaves>(a.x, a.M, a.K, a.ldx, a.tc, a.idx_out, a.count_out, lds.gl);
+            return;
+        }
+        --bid;
+    }
+    FsShared<MT>& fs = lds.g.f;
 
     const int T = a.tiles;
-    const int vt = blockIdx.x % T;
-    const int seg = blockIdx.x / T;
+    const int vt = bid % T;
+    const int seg = bid / T;
     const int S = a.segs;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int slot = lane >> 3, blk = lane & 7;
-    const int t = threadIdx.x;
     const int K = a.K;
     const int Gk = K / kGroup;
-    const int k0 = seg * sp::kSeg;
-    const int kn = K - k0 < sp::kSeg ? K - k0 : sp::kSeg;   // a multiple of 128
-    const int gF = k0 / kGroup, ng = kn / kGroup;
+    const int kw = seg * sp::kSeg + wave * 64;     // this wavefront's first column
+    const bool has = kw < K;                       // K is a multiple of 128: all 64 or none
+    const int g = (has ? kw : 0) / kGroup;
 
     const int tt = vt >> 1, hh = vt & 1;
     const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
     const uint32_t* __restrict__ mdh = a.md + (size_t)tt * Gk * (2 * kVTile) + hh * kVTile;
 
-    // 1. the segment's activations, then its scale/zero rows
+    // 1. activations, then the group's scale/zero row
     uint32_t xr[MT];
+    u32x4 mdv = {0u, 0u, 0u, 0u};
+    if (has) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const int mr = m < a.M ? m : a.M - 1;
-        xr[m] = t < kn ? a.x[(size_t)mr * a.ldx + k0 + t] : 0u;
+        for (int m = 0; m < MT; ++m) {
+            const int mr = m < a.M ? m : a.M - 1;
+            xr[m] = a.x[(size_t)mr * a.ldx + kw + lane];
+        }
+        mdv = *reinterpret_cast<const u32x4*>(mdh + (size_t)g * (2 * kVTile) + 4 * lane);
+    } else {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) xr[m] = 0u;
     }
-    SpMdRaw mdr;
-    sp_md_issue(mdh, gF, ng, mdr);
 
-    // 2. threshold, rank within the wavefront
+    // 2. threshold, rank, compact into this wavefront's LDS rows
     bool act = false;
     uint32_t xm[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         const int mr = m < a.M ? m : a.M - 1;
-        const bool am = t < kn && is_active(xr[m], code_of(a.tc, mr));
+        const bool am = has && is_active(xr[m], code_of(a.tc, mr));
         act = act || am;
         xm[m] = am ? xr[m] : 0u;
     }
     const unsigned long long bal = __ballot(act);
+    const int nact = __popcll(bal);
     const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-    if (lane == 0) s_cnt[0][wave] = (uint32_t)__popcll(bal);
-    sp_md_store(s_md, mdh, gF, ng, mdr);
-    __syncthreads();
-
-    // 3. compact: columns and their (masked) activations in list order
-    uint32_t base = 0, nact = 0;
-#pragma unroll
-    for (int w = 0; w < sp::kWaves; ++w) {
-        const uint32_t c = s_cnt[0][w];
-        base += w < wave ? c : 0u;
-        nact += c;
-    }
     if (act) {
-        s_k[base + rank] = k0 + t;
+        fs.k[wave][rank] = kw + lane;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) s_x[m][base + rank] = (uint16_t)xm[m];
+        for (int m = 0; m < MT; ++m) fs.xs[wave][m][rank] = (uint16_t)xm[m];
     }
-    __syncthreads();
+    *reinterpret_cast<u32x4*>(&fs.md[wave][4 * lane]) =
+        (u32x4){sp_zc(mdv.x, 0), sp_zc(mdv.y, 1), sp_zc(mdv.z, 0), sp_zc(mdv.w, 1)};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // 4. the global list (first half tile only, on request)
-    if (a.idx_out && vt == 0) {
-        const uint32_t pre = fs_prefix<MT>(a, k0, s_cnt[1], wave, lane);
-        if (act) a.idx_out[pre + base + rank] = k0 + t;
-        if (seg == S - 1 && t == 0) *a.count_out = (int32_t)(pre + nact);
-    }
-
-    // 5. chunks of 32 listed columns per wavefront
-    const int nch = ((int)nact + sp::kCh - 1) / sp::kCh;
+    // 3. np column pairs per lane: slot c takes positions 2 np c .. 2 np c + 2 np - 1
+    const int np = (nact + 15) / 16;
     float v4[MT][4] = {};
-    for (int c = wave; c < nch; c += sp::kWaves) {
-        const int p0 = c * sp::kCh + 4 * slot;
-        const int4 k4 = *reinterpret_cast<const int4*>(&s_k[p0]);
-        const int kfirst = s_k[c * sp::kCh];
-        const int kv[4] = {k4.x, k4.y, k4.z, k4.w};
-        int kk[4];
-        uint32_t valid = 0;
+    if (np > 0) {
+        const int kfirst = fs.k[wave][0];
+        int kk[2 * kFsMaxPairs];
+        uint32_t xp[kFsMaxPairs][MT];
+        u32x4 w[2 * kFsMaxPairs];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const bool ok = p0 + q < (int)nact;
-            int k = ok ? kv[q] : kfirst;
-            kk[q] = (unsigned)k < (unsigned)K ? k : K - 1;
-            valid |= (ok ? 1u : 0u) << q;
+        for (int pr = 0; pr < kFsMaxPairs; ++pr) {
+            if (pr < np) {
+                const int p = 2 * np * slot + 2 * pr;          // even: 8-byte aligned pairs
+                const int2 k2 = *reinterpret_cast<const int2*>(&fs.k[wave][p < 62 ? p : 62]);
+                const bool ok0 = p < nact, ok1 = p + 1 < nact;
+                int k0 = ok0 ? k2.x : kfirst, k1 = ok1 ? k2.y : kfirst;
+                kk[2 * pr] = (unsigned)k0 < (unsigned)K ? k0 : K - 1;
+                kk[2 * pr + 1] = (unsigned)k1 < (unsigned)K ? k1 : K - 1;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const uint32_t x2 = *reinterpret_cast<const uint32_t*>(&fs.xs[wave][m][p < 62 ? p : 62]);
+                    xp[pr][m] = (ok0 ? (x2 & 0xFFFFu) : 0u) | (ok1 ? (x2 & 0xFFFF0000u) : 0u);
+                }
+            }
         }
-        u32x4 w[4];
-        sp_load_w(wcol, kk, blk, w);
-        uint32_t xw[MT][4];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const uint2 x4 = *reinterpret_cast<const uint2*>(&s_x[m][p0]);
-            const uint32_t xv[4] = {x4.x & 0xFFFFu, x4.x >> 16, x4.y & 0xFFFFu, x4.y >> 16};
+        for (int j = 0; j < 2 * kFsMaxPairs; ++j)
+            if (j < 2 * np)
+                w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wcol + (size_t)kk[j] * (2 * kHalfRun)) + blk);
+
+        // 4. dequantize, accumulate, scale, sum the slots
+        const uint32_t vmagic = 0x64006400u | __builtin_amdgcn_mbcnt_lo(0u, 0u);  // per-lane (VGPR) copy
 #pragma unroll
-            for (int q = 0; q < 4; ++q) xw[m][q] = ((valid >> q) & 1u) ? xv[q] : 0u;
+        for (int d = 0; d < 4; ++d) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(&fs.md[wave][blk * sp::kOut + 8 * d]);
+            const u32x4 mu = src[0], mv = src[1];
+            const uint32_t md[8] = {mu.x, mu.y, mu.z, mu.w, mv.x, mv.y, mv.z, mv.w};
+            float acc[MT][8];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) acc[m][r] = 0.f;
+#pragma unroll
+            for (int pr = 0; pr < kFsMaxPairs; ++pr) {
+                if (pr < np) {
+                    const u32x4 A = w[2 * pr], B = w[2 * pr + 1];
+                    const uint32_t Ad = d == 0 ? A.x : d == 1 ? A.y : d == 2 ? A.z : A.w;
+                    const uint32_t Bd = d == 0 ? B.x : d == 1 ? B.y : d == 2 ? B.z : B.w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t sel = (0x0Cu << 24) | ((uint32_t)i << 16) | (0x0Cu << 8) | (4u + i);
+                        const uint32_t R = __builtin_amdgcn_perm(Ad, Bd, sel);
+                        const _Float16 zl = as_h2(md[2 * i]).x, zh = as_h2(md[2 * i + 1]).x;
+                        const half2_t lo = as_h2(and_or(R, 0x000F000Fu, vmagic)) - (half2_t){zl, zl};
+                        const half2_t hi = as_h2(and_or(R, 0x00F000F0u, vmagic)) - (half2_t){zh, zh};
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) {
+                            acc[m][2 * i] = __builtin_amdgcn_fdot2(lo, as_h2(xp[pr][m]), acc[m][2 * i], false);
+                            acc[m][2 * i + 1] = __builtin_amdgcn_fdot2(hi, as_h2(xp[pr][m]), acc[m][2 * i + 1], false);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                float y8[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const float sc = (float)as_h2(md[r]).y;
+                    y8[r] = sc * acc[m][r] * ((r & 1) ? 0.0625f : 1.0f);  // the 16 of the high nibbles
+                }
+                v4[m][d] = sp_reduce8(y8, lane);
+            }
         }
-        sp_chunk<MT>(w, xw, kk, valid, s_md, sp::kSegG, mdh, gF, 1, blk, lane, v4);
     }
-    sp_finish<MT>(a, vt, seg, S, wave, lane, v4, sh);
+    sp_finish<MT>(a, vt, seg, S, wave, lane, v4, lds.g.sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1417,7 +1470,7 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     a.ldy = ldy;
     a.M = M;
     a.out_f32 = (flags & SGEMV_OUT_F32) ? 1u : 0u;
-    const dim3 grid((unsigned)(a.tiles * a.segs));
+    const dim3 grid((unsigned)(a.tiles * a.segs + (idx ? 1 : 0)));  // + the list's workgroup
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (M == 1) hipLaunchKernelGGL((k_fs<1>), grid, dim3(sp::kThreads), 0, s, a);
     else hipLaunchKernelGGL((k_fs<2>), grid, dim3(sp::kThreads), 0, s, a);
