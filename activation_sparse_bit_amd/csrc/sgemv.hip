@@ -1111,8 +1111,9 @@ constexpr int kFsMaxPairs = 4;   // 64 columns over 8 slots: at most 4 pairs per
 
 template <int MT>
 struct FsShared {
-    uint32_t md[sp::kWaves][kVTile];                 // per wavefront: its group's (1024 + z | s) pairs
-    __align__(16) int k[sp::kWaves][64];            // per wavefront: its active columns
+    uint32_t zc[sp::kWaves][kVTile / 2];            // per wavefront: (1024 + z, 1024 + 16 z) of output pairs
+    __align__(16) float sc[sp::kWaves][kVTile];     // ... scale of output sp_out(l, d) at 4 l + d (1/16 folded in for odd)
+    __align__(16) int k[sp::kWaves][64];            // ... its active columns
     __align__(16) uint16_t xs[sp::kWaves][MT][64];  // ... and their masked activations
 };
 
@@ -1124,6 +1125,111 @@ union FsLds {
     } g;
     GatherShared gl;
 };
+
+// Column pair (A, B) of one lane against its 8 outputs 8d .. 8d + 7:
+// acc[m][r] += (q - z) x over the pair, exactly dequantized.
+template <int MT>
+__device__ __forceinline__ void fs_pair8(uint32_t Ad, uint32_t Bd, const uint32_t (&zc4)[4], const uint32_t (&xp)[MT],
+                                         uint32_t vmagic, float (&acc)[MT][8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // byte i of the two columns into the low bytes of the two halves
+        const uint32_t sel = (0x0Cu << 24) | ((uint32_t)i << 16) | (0x0Cu << 8) | (4u + i);
+        const uint32_t R = __builtin_amdgcn_perm(Ad, Bd, sel);
+        const half2_t z2 = as_h2(zc4[i]);   // (1024 + z, 1024 + 16 z) of outputs 2i, 2i + 1
+        const half2_t lo = as_h2(and_or(R, 0x000F000Fu, vmagic)) - (half2_t){z2.x, z2.x};  // q - z
+        const half2_t hi = as_h2(and_or(R, 0x00F000F0u, vmagic)) - (half2_t){z2.y, z2.y};  // 16 (q - z)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            acc[m][2 * i] = __builtin_amdgcn_fdot2(lo, as_h2(xp[m]), acc[m][2 * i], false);
+            acc[m][2 * i + 1] = __builtin_amdgcn_fdot2(hi, as_h2(xp[m]), acc[m][2 * i + 1], false);
+        }
+    }
+}
+
+// A wavefront's nact active columns (nact <= 64, in its LDS rows) as NP
+// column pairs per lane: slot c takes positions 2 NP c .. 2 NP c + 2 NP - 1
+// (positions past nact repeat the first column with x = 0).  Issues all
+// 16-byte weight loads, then accumulates pair by pair as they arrive, and
+// returns in v4[m][d] the scaled sum of output sp_out(lane, d).
+template <int MT, int NP>
+__device__ __forceinline__ void fs_block(const FsShared<MT>& fs, int wave, int lane, int slot, int blk, int nact,
+                                         int K, const uint8_t* __restrict__ wcol, float (&v4)[MT][4]) {
+    const int kfirst = fs.k[wave][0];
+    int kk[2 * NP];
+    uint32_t xp[NP][MT];
+    u32x4 w[2 * NP];
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+        const int p = 2 * NP * slot + 2 * pr;          // even, at most 62: 8-byte aligned pairs
+        const int2 k2 = *reinterpret_cast<const int2*>(&fs.k[wave][p]);
+        const bool ok0 = p < nact, ok1 = p + 1 < nact;
+        const int k0 = ok0 ? k2.x : kfirst, k1 = ok1 ? k2.y : kfirst;
+        kk[2 * pr] = (unsigned)k0 < (unsigned)K ? k0 : K - 1;
+        kk[2 * pr + 1] = (unsigned)k1 < (unsigned)K ? k1 : K - 1;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint32_t x2 = *reinterpret_cast<const uint32_t*>(&fs.xs[wave][m][p]);
+            xp[pr][m] = (ok0 ? (x2 & 0xFFFFu) : 0u) | (ok1 ? (x2 & 0xFFFF0000u) : 0u);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2 * NP; ++j)
+        w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wcol + (size_t)kk[j] * (2 * kHalfRun)) + blk);
+
+    // zero codes of the lane's 32 outputs, scales of its 4 final outputs
+    uint32_t zc[16];
+    {
+        const u32x4* src = reinterpret_cast<const u32x4*>(&fs.zc[wave][blk * (sp::kOut / 2)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 u = src[i];
+            zc[4 * i] = u.x; zc[4 * i + 1] = u.y; zc[4 * i + 2] = u.z; zc[4 * i + 3] = u.w;
+        }
+    }
+    const float4 s4 = *reinterpret_cast<const float4*>(&fs.sc[wave][4 * lane]);
+    const float sc[4] = {s4.x, s4.y, s4.z, s4.w};
+    const uint32_t vmagic = 0x64006400u | __builtin_amdgcn_mbcnt_lo(0u, 0u);  // per-lane (VGPR) copy
+    if constexpr (MT == 1) {
+        float acc[4][MT][8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int r = 0; r < 8; ++r) acc[d][0][r] = 0.f;
+#pragma unroll
+        for (int pr = 0; pr < NP; ++pr) {
+            const u32x4 A = w[2 * pr], B = w[2 * pr + 1];
+            const uint32_t Ad[4] = {A.x, A.y, A.z, A.w}, Bd[4] = {B.x, B.y, B.z, B.w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t zc4[4] = {zc[4 * d], zc[4 * d + 1], zc[4 * d + 2], zc[4 * d + 3]};
+                fs_pair8<MT>(Ad[d], Bd[d], zc4, xp[pr], vmagic, acc[d]);
+            }
+        }
+        // slot sums, then the scale (one group per wavefront)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) v4[0][d] = sc[d] * sp_reduce8(acc[d][0], lane);
+    } else {  // two rows: 8 outputs at a time (register budget)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            float acc[MT][8];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) acc[m][r] = 0.f;
+            const uint32_t zc4[4] = {zc[4 * d], zc[4 * d + 1], zc[4 * d + 2], zc[4 * d + 3]};
+#pragma unroll
+            for (int pr = 0; pr < NP; ++pr) {
+                const u32x4 A = w[2 * pr], B = w[2 * pr + 1];
+                const uint32_t Ad = d == 0 ? A.x : d == 1 ? A.y : d == 2 ? A.z : A.w;
+                const uint32_t Bd = d == 0 ? B.x : d == 1 ? B.y : d == 2 ? B.z : B.w;
+                fs_pair8<MT>(Ad, Bd, zc4, xp[pr], vmagic, acc);
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) v4[m][d] = sc[d] * sp_reduce8(acc[m], lane);
+        }
+    }
+}
 
 template <int MT>
 __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_fs(RunArgs a) {
@@ -1188,85 +1294,39 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
 #pragma unroll
         for (int m = 0; m < MT; ++m) fs.xs[wave][m][rank] = (uint16_t)xm[m];
     }
-    *reinterpret_cast<u32x4*>(&fs.md[wave][4 * lane]) =
-        (u32x4){sp_zc(mdv.x, 0), sp_zc(mdv.y, 1), sp_zc(mdv.z, 0), sp_zc(mdv.w, 1)};
+    {
+        // lane l holds outputs 4l .. 4l + 3: zero codes as two (even, odd) pairs,
+        // scales at the lane and sum that will own them after the slot sums
+        const half2_t s01 = as_h2(mdv.x), s11 = as_h2(mdv.y), s21 = as_h2(mdv.z), s31 = as_h2(mdv.w);
+        const half2_t zp0 = (half2_t){(_Float16)(s01.y + (_Float16)1024.0f),
+                                      (_Float16)(s11.y * (_Float16)16.0f + (_Float16)1024.0f)};
+        const half2_t zp1 = (half2_t){(_Float16)(s21.y + (_Float16)1024.0f),
+                                      (_Float16)(s31.y * (_Float16)16.0f + (_Float16)1024.0f)};
+        *reinterpret_cast<uint2*>(&fs.zc[wave][2 * lane]) =
+            make_uint2(__builtin_bit_cast(uint32_t, zp0), __builtin_bit_cast(uint32_t, zp1));
+        const float sv[4] = {(float)s01.x, (float)s11.x * 0.0625f, (float)s21.x, (float)s31.x * 0.0625f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int o = 4 * lane + r;        // output o = 32 blk + 8 d + 4 b5 + 2 b4 + b3
+            const int j = o & 7;
+            const int L = (o >> 5) + 8 * (j & 1) + 16 * ((j >> 1) & 1) + 32 * (j >> 2);
+            fs.sc[wave][4 * L + ((o >> 3) & 3)] = sv[r];
+        }
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // 3. np column pairs per lane: slot c takes positions 2 np c .. 2 np c + 2 np - 1
+    // 3-5. np column pairs per lane (straight-line code per np, so that every
+    //      pair waits only for its own loads)
     const int np = (nact + 15) / 16;
     float v4[MT][4] = {};
-    if (np > 0) {
-        const int kfirst = fs.k[wave][0];
-        int kk[2 * kFsMaxPairs];
-        uint32_t xp[kFsMaxPairs][MT];
-        u32x4 w[2 * kFsMaxPairs];
-#pragma unroll
-        for (int pr = 0; pr < kFsMaxPairs; ++pr) {
-            if (pr < np) {
-                const int p = 2 * np * slot + 2 * pr;          // even: 8-byte aligned pairs
-                const int2 k2 = *reinterpret_cast<const int2*>(&fs.k[wave][p < 62 ? p : 62]);
-                const bool ok0 = p < nact, ok1 = p + 1 < nact;
-                int k0 = ok0 ? k2.x : kfirst, k1 = ok1 ? k2.y : kfirst;
-                kk[2 * pr] = (unsigned)k0 < (unsigned)K ? k0 : K - 1;
-                kk[2 * pr + 1] = (unsigned)k1 < (unsigned)K ? k1 : K - 1;
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    const uint32_t x2 = *reinterpret_cast<const uint32_t*>(&fs.xs[wave][m][p < 62 ? p : 62]);
-                    xp[pr][m] = (ok0 ? (x2 & 0xFFFFu) : 0u) | (ok1 ? (x2 & 0xFFFF0000u) : 0u);
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 2 * kFsMaxPairs; ++j)
-            if (j < 2 * np)
-                w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wcol + (size_t)kk[j] * (2 * kHalfRun)) + blk);
-
-        // 4. dequantize, accumulate, scale, sum the slots
-        const uint32_t vmagic = 0x64006400u | __builtin_amdgcn_mbcnt_lo(0u, 0u);  // per-lane (VGPR) copy
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const u32x4* src = reinterpret_cast<const u32x4*>(&fs.md[wave][blk * sp::kOut + 8 * d]);
-            const u32x4 mu = src[0], mv = src[1];
-            const uint32_t md[8] = {mu.x, mu.y, mu.z, mu.w, mv.x, mv.y, mv.z, mv.w};
-            float acc[MT][8];
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int r = 0; r < 8; ++r) acc[m][r] = 0.f;
-#pragma unroll
-            for (int pr = 0; pr < kFsMaxPairs; ++pr) {
-                if (pr < np) {
-                    const u32x4 A = w[2 * pr], B = w[2 * pr + 1];
-                    const uint32_t Ad = d == 0 ? A.x : d == 1 ? A.y : d == 2 ? A.z : A.w;
-                    const uint32_t Bd = d == 0 ? B.x : d == 1 ? B.y : d == 2 ? B.z : B.w;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t sel = (0x0Cu << 24) | ((uint32_t)i << 16) | (0x0Cu << 8) | (4u + i);
-                        const uint32_t R = __builtin_amdgcn_perm(Ad, Bd, sel);
-                        const _Float16 zl = as_h2(md[2 * i]).x, zh = as_h2(md[2 * i + 1]).x;
-                        const half2_t lo = as_h2(and_or(R, 0x000F000Fu, vmagic)) - (half2_t){zl, zl};
-                        const half2_t hi = as_h2(and_or(R, 0x00F000F0u, vmagic)) - (half2_t){zh, zh};
-#pragma unroll
-                        for (int m = 0; m < MT; ++m) {
-                            acc[m][2 * i] = __builtin_amdgcn_fdot2(lo, as_h2(xp[pr][m]), acc[m][2 * i], false);
-                            acc[m][2 * i + 1] = __builtin_amdgcn_fdot2(hi, as_h2(xp[pr][m]), acc[m][2 * i + 1], false);
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                float y8[8];
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const float sc = (float)as_h2(md[r]).y;
-                    y8[r] = sc * acc[m][r] * ((r & 1) ? 0.0625f : 1.0f);  // the 16 of the high nibbles
-                }
-                v4[m][d] = sp_reduce8(y8, lane);
-            }
-        }
+    switch (np) {
+        case 1: fs_block<MT, 1>(fs, wave, lane, slot, blk, nact, K, wcol, v4); break;
+        case 2: fs_block<MT, 2>(fs, wave, lane, slot, blk, nact, K, wcol, v4); break;
+        case 3: fs_block<MT, 3>(fs, wave, lane, slot, blk, nact, K, wcol, v4); break;
+        case 4: fs_block<MT, 4>(fs, wave, lane, slot, blk, nact, K, wcol, v4); break;
+        default: break;
     }
     sp_finish<MT>(a, vt, seg, S, wave, lane, v4, lds.g.sh);
 }
