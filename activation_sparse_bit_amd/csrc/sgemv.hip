@@ -421,9 +421,7 @@ __device__ __forceinline__ void chunk_compute(float (&y)[MT][4], const RunArgs& 
         const int m = (wc.lane >> 4) + 4 * j;
         if (wc.lane < XRows<MT>::kLanes && m < MT) xs[m][wc.lane & (kChunk - 1)] = (uint16_t)ch.xv[j];
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // LDS operations of a wavefront complete in order
     // groups gA, gA+1, gA+2: metadata prefetched (the third loaded here)
     for (int d = 0; d <= 2; ++d) {
         const uint32_t pos = code_positions(ch.codes, (uint32_t)d, ch.nv);
@@ -1153,8 +1151,9 @@ __device__ __forceinline__ void fs_pair8(uint32_t Ad, uint32_t Bd, const uint32_
 // 16-byte weight loads, then accumulates pair by pair as they arrive, and
 // returns in v4[m][d] the scaled sum of output sp_out(lane, d).
 template <int MT, int NP>
-__device__ __forceinline__ void fs_block(const FsShared<MT>& fs, int wave, int lane, int slot, int blk, int nact,
-                                         int K, const uint8_t* __restrict__ wcol, float (&v4)[MT][4]) {
+__device__ __forceinline__ void fs_block(FsShared<MT>& fs, int wave, int lane, int slot, int blk, int nact,
+                                         int K, const uint8_t* __restrict__ wcol, const u32x4& mdv,
+                                         float (&v4)[MT][4]) {
     const int kfirst = fs.k[wave][0];
     int kk[2 * NP];
     uint32_t xp[NP][MT];
@@ -1177,6 +1176,27 @@ __device__ __forceinline__ void fs_block(const FsShared<MT>& fs, int wave, int l
     for (int j = 0; j < 2 * NP; ++j)
         w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wcol + (size_t)kk[j] * (2 * kHalfRun)) + blk);
 
+    {
+        // the group row: lane l holds outputs 4l .. 4l + 3; zero codes as two
+        // (even, odd) pairs, scales at the lane and sum that will own them
+        // after the slot sums
+        const half2_t s01 = as_h2(mdv.x), s11 = as_h2(mdv.y), s21 = as_h2(mdv.z), s31 = as_h2(mdv.w);
+        const half2_t zp0 = (half2_t){(_Float16)(s01.y + (_Float16)1024.0f),
+                                      (_Float16)(s11.y * (_Float16)16.0f + (_Float16)1024.0f)};
+        const half2_t zp1 = (half2_t){(_Float16)(s21.y + (_Float16)1024.0f),
+                                      (_Float16)(s31.y * (_Float16)16.0f + (_Float16)1024.0f)};
+        *reinterpret_cast<uint2*>(&fs.zc[wave][2 * lane]) =
+            make_uint2(__builtin_bit_cast(uint32_t, zp0), __builtin_bit_cast(uint32_t, zp1));
+        const float sv[4] = {(float)s01.x, (float)s11.x * 0.0625f, (float)s21.x, (float)s31.x * 0.0625f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int o = 4 * lane + r;        // output o = 32 blk + 8 d + 4 b5 + 2 b4 + b3
+            const int j = o & 7;
+            const int L = (o >> 5) + 8 * (j & 1) + 16 * ((j >> 1) & 1) + 32 * (j >> 2);
+            fs.sc[wave][4 * L + ((o >> 3) & 3)] = sv[r];
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
     // zero codes of the lane's 32 outputs, scales of its 4 final outputs
     uint32_t zc[16];
     {
@@ -1261,19 +1281,13 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
     const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
     const uint32_t* __restrict__ mdh = a.md + (size_t)tt * Gk * (2 * kVTile) + hh * kVTile;
 
-    // 1. activations, then the group's scale/zero row
+    // 1. activations (one per lane and row; a wavefront past K reads column
+    //    lane and ignores it, so the load is unconditional)
     uint32_t xr[MT];
-    u32x4 mdv = {0u, 0u, 0u, 0u};
-    if (has) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int mr = m < a.M ? m : a.M - 1;
-            xr[m] = a.x[(size_t)mr * a.ldx + kw + lane];
-        }
-        mdv = *reinterpret_cast<const u32x4*>(mdh + (size_t)g * (2 * kVTile) + 4 * lane);
-    } else {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) xr[m] = 0u;
+    for (int m = 0; m < MT; ++m) {
+        const int mr = m < a.M ? m : a.M - 1;
+        xr[m] = a.x[(size_t)mr * a.ldx + (has ? kw : 0) + lane];
     }
 
     // 2. threshold, rank, compact into this wavefront's LDS rows
@@ -1282,50 +1296,33 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         const int mr = m < a.M ? m : a.M - 1;
-        const bool am = has && is_active(xr[m], code_of(a.tc, mr));
-        act = act || am;
+        const bool am = is_active(xr[m], code_of(a.tc, mr)) & has;  // no branch: x is waited for on every path
+        act = act | am;
         xm[m] = am ? xr[m] : 0u;
     }
     const unsigned long long bal = __ballot(act);
     const int nact = __popcll(bal);
     const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    const int np = (nact + 15) / 16;
+    // the group's scale/zero row (16 bytes per lane), only with work to do;
+    // converted after the weight loads are issued
+    u32x4 mdv = {0u, 0u, 0u, 0u};
+    if (np > 0) mdv = *reinterpret_cast<const u32x4*>(mdh + (size_t)g * (2 * kVTile) + 4 * lane);
     if (act) {
         fs.k[wave][rank] = kw + lane;
 #pragma unroll
         for (int m = 0; m < MT; ++m) fs.xs[wave][m][rank] = (uint16_t)xm[m];
     }
-    {
-        // lane l holds outputs 4l .. 4l + 3: zero codes as two (even, odd) pairs,
-        // scales at the lane and sum that will own them after the slot sums
-        const half2_t s01 = as_h2(mdv.x), s11 = as_h2(mdv.y), s21 = as_h2(mdv.z), s31 = as_h2(mdv.w);
-        const half2_t zp0 = (half2_t){(_Float16)(s01.y + (_Float16)1024.0f),
-                                      (_Float16)(s11.y * (_Float16)16.0f + (_Float16)1024.0f)};
-        const half2_t zp1 = (half2_t){(_Float16)(s21.y + (_Float16)1024.0f),
-                                      (_Float16)(s31.y * (_Float16)16.0f + (_Float16)1024.0f)};
-        *reinterpret_cast<uint2*>(&fs.zc[wave][2 * lane]) =
-            make_uint2(__builtin_bit_cast(uint32_t, zp0), __builtin_bit_cast(uint32_t, zp1));
-        const float sv[4] = {(float)s01.x, (float)s11.x * 0.0625f, (float)s21.x, (float)s31.x * 0.0625f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int o = 4 * lane + r;        // output o = 32 blk + 8 d + 4 b5 + 2 b4 + b3
-            const int j = o & 7;
-            const int L = (o >> 5) + 8 * (j & 1) + 16 * ((j >> 1) & 1) + 32 * (j >> 2);
-            fs.sc[wave][4 * L + ((o >> 3) & 3)] = sv[r];
-        }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // LDS operations of a wavefront complete in order
 
     // 3-5. np column pairs per lane (straight-line code per np, so that every
     //      pair waits only for its own loads)
-    const int np = (nact + 15) / 16;
     float v4[MT][4] = {};
     switch (np) {
-        case 1: fs_block<MT, 1>(fs, wave, lane, slot, blk, nact, K, wcol, v4); break;
-        case 2: fs_block<MT, 2>(fs, wave, lane, slot, blk, nact, K, wcol, v4); break;
-        case 3: fs_block<MT, 3>(fs, wave, lane, slot, blk, nact, K, wcol, v4); break;
-        case 4: fs_block<MT, 4>(fs, wave, lane, slot, blk, nact, K, wcol, v4); break;
+        case 1: fs_block<MT, 1>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
+        case 2: fs_block<MT, 2>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
+        case 3: fs_block<MT, 3>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
+        case 4: fs_block<MT, 4>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
         default: break;
     }
     sp_finish<MT>(a, vt, seg, S, wave, lane, v4, lds.g.sh);
