@@ -123,17 +123,20 @@ struct GatherShared {
     uint32_t wtot[16];
 };
 
+// Wavefronts W and above of the workgroup only join the barrier.
 template <int W>
 __device__ __forceinline__ void gather_body(const uint16_t* __restrict__ x, int M, int K, int ldx, const Codes& tc,
                                             int32_t* __restrict__ idx, int32_t* __restrict__ count,
                                             GatherShared& gs) {
+    static_assert(W == 4 || W == 8 || W == 16, "K / W must stay a multiple of 8");
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int Kw = K / W;           // columns per wavefront, a multiple of 8
     const int base = wave * Kw;
+    const bool work = wave < W;
 
     uint32_t mytotal = 0;
-    for (int s = 0; s * 512 < Kw; ++s) {
+    for (int s = 0; work && s * 512 < Kw; ++s) {
         const int off = s * 512 + lane * 8;
         uint32_t m8 = 0;
         if (off < Kw) {
@@ -147,8 +150,9 @@ __device__ __forceinline__ void gather_body(const uint16_t* __restrict__ x, int 
         wave_scan16((uint32_t)__popc(m8), pre, tot);
         mytotal += tot;
     }
-    if (lane == 0) gs.wtot[wave] = mytotal;
+    if (work && lane == 0) gs.wtot[wave] = mytotal;
     __syncthreads();
+    if (!work) return;
     uint32_t wbase = 0, grand = 0;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
@@ -696,8 +700,6 @@ constexpr int kCh = 32;                  // list positions per wavefront and chu
 constexpr int kPos = kWaves * kCh;       // list positions per workgroup (list-driven kernel)
 constexpr int kGCap = 24;                // scale/zero rows staged in LDS (list-driven kernel)
 constexpr int kOut = 32;                 // outputs per lane while computing
-constexpr int kSeg = 512;                // columns per workgroup (fused kernel)
-constexpr int kSegG = kSeg / kGroup;     // groups per segment
 }  // namespace sp
 
 __device__ __forceinline__ float u2f(uint32_t v) { return __uint_as_float(v); }
@@ -883,33 +885,38 @@ __device__ __forceinline__ void sp_load_w(const uint8_t* wcol, const int (&kk)[4
         w[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wcol + (size_t)kk[q] * (2 * kHalfRun)) + blk);
 }
 
-template <int MT>
+template <int MT, int NW>
 struct SpShared {
-    float red[sp::kWaves][MT][kVTile];
+    float red[NW][MT][kVTile];
     uint32_t flag;
 };
 
-// Sum the workgroup's wavefronts and write y (S == 1), or publish the
+// Sum the workgroup's NW wavefronts and write y (S == 1), or publish the
 // workgroup's sums as slice `slice` of S and let the last workgroup of the
 // half tile to arrive add every slice in slice order and write y.  Every
-// thread of the workgroup calls it.  Thread t handles row t / 256 (MT = 2)
-// or, for MT = 1, output t % 256 (threads 256..511 help reading slices).
-template <int MT>
+// thread of the workgroup calls it (NW >= 4 MT).  Thread t handles output
+// t % 256 of row (t / 256) % MT; the NH = NW / (4 MT) groups of 256 MT
+// threads split the slices of the last workgroup, whose partial sums are
+// then added in group order.
+template <int MT, int NW>
 __device__ __forceinline__ void sp_finish(const RunArgs& a, int vt, int slice, int S, int wave, int lane,
-                                          const float (&v4)[MT][4], SpShared<MT>& sh) {
+                                          const float (&v4)[MT][4], SpShared<MT, NW>& sh) {
+    static_assert(NW >= 4 * MT, "one thread per output and row");
+    constexpr int NH = NW / (4 * MT);
 #pragma unroll
     for (int m = 0; m < MT; ++m)
         *reinterpret_cast<float4*>(&sh.red[wave][m][4 * lane]) = make_float4(v4[m][0], v4[m][1], v4[m][2], v4[m][3]);
     __syncthreads();
     const int t = threadIdx.x;
     const int o = t % kVTile;                 // lane-major slot: lane o / 4, sum o % 4
-    const int m = MT == 1 ? 0 : t / kVTile;
-    const int half = MT == 1 ? t / kVTile : 0;
-    const bool own = half == 0;
+    const int r = t / kVTile;
+    const int m = MT == 1 ? 0 : r % MT;
+    const int h = r / MT;                     // thread group
+    const bool own = h == 0;
     float sum = 0.f;
     if (own) {
 #pragma unroll
-        for (int w = 0; w < sp::kWaves; ++w) sum += sh.red[w][m][o];
+        for (int w = 0; w < NW; ++w) sum += sh.red[w][m][o];
     }
     const size_t n = (size_t)vt * kVTile + sp_out(o >> 2, o & 3);
     if (S == 1) {
@@ -936,27 +943,32 @@ __device__ __forceinline__ void sp_finish(const RunArgs& a, int vt, int slice, i
     __syncthreads();
     if (sh.flag == 0u) return;
 
-    // last to arrive: slices s0 .. s1 - 1 of this thread, 16 loads in flight
-    const int per = MT == 1 ? (S + 1) / 2 : S;
-    const int s0 = half * per;
+    // last to arrive: group h adds slices s0 .. s1 - 1, 16 loads in flight
+    const int per = (S + NH - 1) / NH;
+    const int s0 = h * per;
     const int s1 = s0 + per < S ? s0 + per : S;
     float tot = 0.f;
-    for (int sb = s0; sb < s1; sb += 16) {
-        float v[16];
+    if (h < NH) {
+        for (int sb = s0; sb < s1; sb += 16) {
+            float v[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int sl = sb + i < s1 ? sb + i : sb;
-            const uint32_t off = tile_base + (((uint32_t)sl * MT + m) * kVTile + o) * 4u;
-            v[i] = u2f(__builtin_amdgcn_raw_buffer_load_b32(prs, off, 0, kCacheSC1));
+            for (int i = 0; i < 16; ++i) {
+                const int sl = sb + i < s1 ? sb + i : sb;
+                const uint32_t off = tile_base + (((uint32_t)sl * MT + m) * kVTile + o) * 4u;
+                v[i] = u2f(__builtin_amdgcn_raw_buffer_load_b32(prs, off, 0, kCacheSC1));
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (sb + i < s1) tot += v[i];
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (sb + i < s1) tot += v[i];
     }
-    if (MT == 1) {  // add the second half's sum to the first's
-        if (!own) sh.red[0][0][o] = tot;
+    if constexpr (NH > 1) {  // add the other groups' sums to group 0's, in group order
+        if (h >= 1 && h < NH) sh.red[h][m][o] = tot;
         __syncthreads();
-        if (own) tot += sh.red[0][0][o];
+        if (own) {
+#pragma unroll
+            for (int hh = 1; hh < NH; ++hh) tot += sh.red[hh][m][o];
+        }
     }
     if (own && m < a.M) {
         if (a.out_f32) static_cast<float*>(a.y)[(size_t)m * a.ldy + n] = tot;
@@ -970,7 +982,7 @@ __device__ __forceinline__ void sp_finish(const RunArgs& a, int vt, int slice, i
 template <int MT, bool DENSE, bool MASK>
 __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_sp(RunArgs a) {
     __shared__ uint32_t s_md[sp::kGCap][kVTile];
-    __shared__ SpShared<MT> sh;
+    __shared__ SpShared<MT, sp::kWaves> sh;
 
     const int T = a.tiles;
     const int vt = blockIdx.x % T;
@@ -1003,7 +1015,7 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
     if (count == 0) {  // nothing listed: y = +0
         if (slice == 0) {
             const float z[MT][4] = {};
-            sp_finish<MT>(a, vt, 0, 1, wave, lane, z, sh);
+            sp_finish<MT, sp::kWaves>(a, vt, 0, 1, wave, lane, z, sh);
         }
         return;
     }
@@ -1078,7 +1090,7 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
     // 4. the chunk, 5. the sums
     float v4[MT][4] = {};
     if (nv > 0) sp_chunk<MT>(w, xw, kk, valid, s_md, sp::kGCap, mdh, gF, staged, blk, lane, v4);
-    sp_finish<MT>(a, vt, slice, S, wave, lane, v4, sh);
+    sp_finish<MT, sp::kWaves>(a, vt, slice, S, wave, lane, v4, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1105,21 +1117,28 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
 // with the gathering routine while the others compute; it reads only the
 // activations.
 
-constexpr int kFsMaxPairs = 4;   // 64 columns over 8 slots: at most 4 pairs per lane
+constexpr int kFsCols = kGroup;                // columns per wavefront: one quantization group
+constexpr int kFsMaxPairs = kFsCols / 16;       // column pairs per lane with every column active
+// wavefronts per workgroup (one row, two rows); a workgroup owns W groups
+template <int MT>
+struct FsCfg {
+    static constexpr int W = MT == 1 ? 8 : 8;
+    static constexpr int kSeg = W * kFsCols;    // columns per workgroup
+};
 
 template <int MT>
 struct FsShared {
-    uint32_t zc[sp::kWaves][kVTile / 2];            // per wavefront: (1024 + z, 1024 + 16 z) of output pairs
-    __align__(16) float sc[sp::kWaves][kVTile];     // ... scale of output sp_out(l, d) at 4 l + d (1/16 folded in for odd)
-    __align__(16) int k[sp::kWaves][64];            // ... its active columns
-    __align__(16) uint16_t xs[sp::kWaves][MT][64];  // ... and their masked activations
+    uint32_t zc[FsCfg<MT>::W][kVTile / 2];                  // per wavefront: (1024 + z, 1024 + 16 z) of output pairs
+    __align__(16) float sc[FsCfg<MT>::W][kVTile];           // ... scale of output sp_out(l, d) at 4 l + d (1/16 folded in for odd)
+    __align__(16) int k[FsCfg<MT>::W][kFsCols];             // ... its active columns
+    __align__(16) uint16_t xs[FsCfg<MT>::W][MT][kFsCols];   // ... and their masked activations
 };
 
 template <int MT>
 union FsLds {
     struct {
         FsShared<MT> f;
-        SpShared<MT> sh;
+        SpShared<MT, FsCfg<MT>::W> sh;
     } g;
     GatherShared gl;
 };
@@ -1160,7 +1179,7 @@ __device__ __forceinline__ void fs_block(FsShared<MT>& fs, int wave, int lane, i
     u32x4 w[2 * NP];
 #pragma unroll
     for (int pr = 0; pr < NP; ++pr) {
-        const int p = 2 * NP * slot + 2 * pr;          // even, at most 62: 8-byte aligned pairs
+        const int p = 2 * NP * slot + 2 * pr;          // even, below kFsCols: 8-byte aligned pairs
         const int2 k2 = *reinterpret_cast<const int2*>(&fs.k[wave][p]);
         const bool ok0 = p < nact, ok1 = p + 1 < nact;
         const int k0 = ok0 ? k2.x : kfirst, k1 = ok1 ? k2.y : kfirst;
@@ -1252,12 +1271,13 @@ __device__ __forceinline__ void fs_block(FsShared<MT>& fs, int wave, int lane, i
 }
 
 template <int MT>
-__global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_fs(RunArgs a) {
+__global__ __launch_bounds__(FsCfg<MT>::W * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fs(RunArgs a) {
     __shared__ FsLds<MT> lds;
     int bid = blockIdx.x;
     if (a.idx_out) {  // block 0 writes the list
         if (bid == 0) {
-            gather_body<sp::kWaves>(a.x, a.M, a.K, a.ldx, a.tc, a.idx_out, a.count_out, lds.gl);
+            constexpr int WL = FsCfg<MT>::W >= 16 ? 16 : FsCfg<MT>::W >= 8 ? 8 : 4;
+            gather_body<WL>(a.x, a.M, a.K, a.ldx, a.tc, a.idx_out, a.count_out, lds.gl);
             return;
         }
         --bid;
@@ -1273,45 +1293,61 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
     const int slot = lane >> 3, blk = lane & 7;
     const int K = a.K;
     const int Gk = K / kGroup;
-    const int kw = seg * sp::kSeg + wave * 64;     // this wavefront's first column
-    const bool has = kw < K;                       // K is a multiple of 128: all 64 or none
+    const int kw = seg * FsCfg<MT>::kSeg + wave * kFsCols;  // this wavefront's first column
+    const bool has = kw < K;                       // K is a multiple of 128: all of the group or none
     const int g = (has ? kw : 0) / kGroup;
 
     const int tt = vt >> 1, hh = vt & 1;
     const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
     const uint32_t* __restrict__ mdh = a.md + (size_t)tt * Gk * (2 * kVTile) + hh * kVTile;
 
-    // 1. activations (one per lane and row; a wavefront past K reads column
-    //    lane and ignores it, so the load is unconditional)
-    uint32_t xr[MT];
+    // 1. activations (two per lane and row; a wavefront past K reads its
+    //    first columns and ignores them, so the loads are unconditional)
+    constexpr int H = kFsCols / 64;
+    uint32_t xr[H][MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const int mr = m < a.M ? m : a.M - 1;
-        xr[m] = a.x[(size_t)mr * a.ldx + (has ? kw : 0) + lane];
-    }
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int mr = m < a.M ? m : a.M - 1;
+            xr[h][m] = a.x[(size_t)mr * a.ldx + (has ? kw : 0) + 64 * h + lane];
+        }
 
-    // 2. threshold, rank, compact into this wavefront's LDS rows
-    bool act = false;
-    uint32_t xm[MT];
+    // 2. threshold, rank, compact into this wavefront's LDS rows (no branch
+    //    before the ballots: x is waited for on every path)
+    bool act[H];
+    uint32_t xm[H][MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const int mr = m < a.M ? m : a.M - 1;
-        const bool am = is_active(xr[m], code_of(a.tc, mr)) & has;  // no branch: x is waited for on every path
-        act = act | am;
-        xm[m] = am ? xr[m] : 0u;
+    for (int h = 0; h < H; ++h) {
+        act[h] = false;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int mr = m < a.M ? m : a.M - 1;
+            const bool am = is_active(xr[h][m], code_of(a.tc, mr)) & has;
+            act[h] = act[h] | am;
+            xm[h][m] = am ? xr[h][m] : 0u;
+        }
     }
-    const unsigned long long bal = __ballot(act);
-    const int nact = __popcll(bal);
-    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    int nact = 0;
+    uint32_t rank[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+        const unsigned long long bal = __ballot(act[h]);
+        rank[h] = nact + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        nact += __popcll(bal);
+    }
     const int np = (nact + 15) / 16;
     // the group's scale/zero row (16 bytes per lane), only with work to do;
     // converted after the weight loads are issued
     u32x4 mdv = {0u, 0u, 0u, 0u};
     if (np > 0) mdv = *reinterpret_cast<const u32x4*>(mdh + (size_t)g * (2 * kVTile) + 4 * lane);
-    if (act) {
-        fs.k[wave][rank] = kw + lane;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) fs.xs[wave][m][rank] = (uint16_t)xm[m];
+    for (int h = 0; h < H; ++h) {
+        if (act[h]) {
+            fs.k[wave][rank[h]] = kw + 64 * h + lane;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) fs.xs[wave][m][rank[h]] = (uint16_t)xm[h][m];
+        }
     }
     __builtin_amdgcn_wave_barrier();  // LDS operations of a wavefront complete in order
 
@@ -1323,9 +1359,13 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
         case 2: fs_block<MT, 2>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
         case 3: fs_block<MT, 3>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
         case 4: fs_block<MT, 4>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
+        case 5: fs_block<MT, 5>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
+        case 6: fs_block<MT, 6>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
+        case 7: fs_block<MT, 7>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
+        case 8: fs_block<MT, 8>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
         default: break;
     }
-    sp_finish<MT>(a, vt, seg, S, wave, lane, v4, lds.g.sh);
+    sp_finish<MT, FsCfg<MT>::W>(a, vt, seg, S, wave, lane, v4, lds.g.sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1507,7 +1547,8 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     if (st) return st;
     a.tiles = d->N / kVTile;
     a.slices = slices_for(d, M);   // stride of the partials region
-    a.segs = (d->K + sp::kSeg - 1) / sp::kSeg;
+    const int seg_cols = M == 1 ? FsCfg<1>::kSeg : FsCfg<2>::kSeg;
+    a.segs = (d->K + seg_cols - 1) / seg_cols;
     if (a.segs > 1) {
         if (!ws) return SGEMV_EINVAL;
         if (!aligned(ws, 256)) return SGEMV_EALIGN;
@@ -1529,8 +1570,8 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     a.out_f32 = (flags & SGEMV_OUT_F32) ? 1u : 0u;
     const dim3 grid((unsigned)(a.tiles * a.segs + (idx ? 1 : 0)));  // + the list's workgroup
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (M == 1) hipLaunchKernelGGL((k_fs<1>), grid, dim3(sp::kThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_fs<2>), grid, dim3(sp::kThreads), 0, s, a);
+    if (M == 1) hipLaunchKernelGGL((k_fs<1>), grid, dim3(FsCfg<1>::W * 64), 0, s, a);
+    else hipLaunchKernelGGL((k_fs<2>), grid, dim3(FsCfg<2>::W * 64), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         g_last_hip_error = (int)e;
