@@ -227,3 +227,36 @@ class PackedMatrix:
         self.workspace = torch.zeros(max(sgemv_workspace_bytes(self.desc, max_batch), 256),
                                      dtype=torch.uint8, device=device)
         self.N, self.K = self.desc.N, self.desc.K
+
+
+class FusedProjections:
+    """Projections that read the same activations (q/k/v, gate/up), packed
+    as one matrix with their rows concatenated, so that one call of
+    sgemv_run_fused thresholds x once and computes all of them.  Each
+    projection's N must be a multiple of 512 (the layout tile), so every
+    tile belongs to one projection.  `split(y)` returns the per-projection
+    views of the concatenated output."""
+
+    def __init__(self, parts, device="cuda", max_batch: int = 2):
+        names = [p[0] for p in parts]
+        if len(set(names)) != len(names):
+            raise ValueError("projection names must be unique")
+        Ks = {np.asarray(p[1]).shape[1] for p in parts}
+        if len(Ks) != 1:
+            raise ValueError("fused projections must share K")
+        self.offsets = {}
+        start = 0
+        for name, q, _, _ in parts:
+            n = np.asarray(q).shape[0]
+            if n % SGEMV_TILE_N:
+                raise ValueError(f"{name}: N = {n} is not a multiple of {SGEMV_TILE_N}")
+            self.offsets[name] = (start, n)
+            start += n
+        q = np.concatenate([np.asarray(p[1], dtype=np.uint8) for p in parts])
+        s = np.concatenate([np.asarray(p[2]).view(np.uint16) for p in parts])
+        z = np.concatenate([np.asarray(p[3]).view(np.uint16) for p in parts])
+        self.matrix = PackedMatrix(q, s, z, device=device, max_batch=max_batch)
+        self.N, self.K = self.matrix.N, self.matrix.K
+
+    def split(self, y):
+        return {name: y[..., a:a + n] for name, (a, n) in self.offsets.items()}

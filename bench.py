@@ -207,6 +207,65 @@ def main():
                 [lambda i: sgemv.sgemv_run_fused(desc, copies[i % R], Xd, ts, Y, ws, idx, cnt)], steps, warmup)
         return res
 
+    def measure_layer(steps, warmup):
+        """Llama-3-8B-shaped decode layer at 50 % on every projection input:
+        q/k/v and gate/up packed as one matrix each (4 fused launches), each
+        projection on its own (7 fused launches), and the two-launch path
+        (4 gathers + 7 runs)."""
+        wl = synth.workload("layer-8b")
+        P = {p.name: p for p in wl.projections}
+        W = {n: synth.quantized_weights(P[n].weight_seed, P[n].N, P[n].K, P[n].sigma) for n in P}
+        X = {k: synth.activation(*v) for k, v in wl.inputs.items()}
+        T = {k: synth.percentile_threshold(v, 0.5) for k, v in X.items()}
+        Xd = {k: torch.from_numpy(v).to(dev) for k, v in X.items()}
+        groups = [("qkv", ("q", "k", "v"), "x_attn"), ("o", ("o",), "x_o"),
+                  ("gate_up", ("gate", "up"), "x_mlp"), ("down", ("down",), "x_down")]
+        fused = {g: sgemv.FusedProjections([(n, *W[n]) for n in names], device=dev, max_batch=1)
+                 for g, names, _ in groups}
+        single = {n: sgemv.PackedMatrix(*W[n], device=dev, max_batch=1) for n in P}
+        total = sum(f.matrix.desc.total_bytes for f in fused.values())
+        RL = max(2, -(-ROTATE_BYTES // total))
+        fcopies = {g: [f.matrix.blob] + [f.matrix.blob.clone() for _ in range(RL - 1)] for g, f in fused.items()}
+        scopies = {n: [m.blob] + [m.blob.clone() for _ in range(RL - 1)] for n, m in single.items()}
+        Y = {g: torch.empty(f.N, dtype=torch.float16, device=dev) for g, f in fused.items()}
+        Ys = {n: torch.empty(m.N, dtype=torch.float16, device=dev) for n, m in single.items()}
+        lidx = torch.zeros(14336, dtype=torch.int32, device=dev)
+        lcnt = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def fz(g, xin):
+            f = fused[g]
+            return lambda i: sgemv.sgemv_run_fused(f.matrix.desc, fcopies[g][i % RL], Xd[xin], [T[xin]], Y[g],
+                                                   f.matrix.workspace, lidx, lcnt)
+
+        def sz(n):
+            m, xin = single[n], P[n].input_name
+            return lambda i: sgemv.sgemv_run_fused(m.desc, scopies[n][i % RL], Xd[xin], [T[xin]], Ys[n],
+                                                   m.workspace, lidx, lcnt)
+
+        def gz(xin):
+            return lambda i: sgemv.sgemv_gather_indices(Xd[xin], [T[xin]], lidx, lcnt)
+
+        def rz(n):
+            m, xin = single[n], P[n].input_name
+            return lambda i: sgemv.sgemv_run(m.desc, scopies[n][i % RL], Xd[xin], lidx, lcnt, Ys[n], m.workspace)
+
+        fused_us = graph_time([fz(g, xin) for g, _, xin in groups], steps, warmup)
+        sep_us = graph_time([sz(n) for n in P], steps, warmup)
+        split = []
+        for g, names, xin in groups:
+            split.append(gz(xin))
+            split += [rz(n) for n in names]
+        split_us = graph_time(split, steps, warmup)
+        nbytes = 0
+        for g, names, xin in groups:
+            f = fused[g]
+            A = int(np.count_nonzero(np.abs(X[xin].astype(np.float32)) >= np.float32(T[xin])))
+            nbytes += fused_bytes(A, f.K // 128, f.N, f.K)
+        del fcopies, scopies
+        return {"projections_packed_by_input_us": fused_us, "launches": 4,
+                "each_projection_fused_us": sep_us, "two_launch_path_us": split_us,
+                "bytes": nbytes, "GBps": nbytes / (fused_us * 1e-6) / 1e9}
+
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -221,6 +280,7 @@ def main():
     main_res = measure_fused(0.5, args.steps, args.warmup, latency=not args.quick)
     sweep = {"fused_p50": main_res}
     batched = []
+    layer = None
     if not args.quick:
         for p in (0.7, 0.9):
             sweep[f"fused_p{int(p * 100)}"] = measure_fused(p, args.steps, args.warmup)
@@ -233,6 +293,7 @@ def main():
             sweep[k]["speedup_vs_dense_int4"] = dense_us / sweep[k]["us_per_step"]
         for M in (1, 2, 4, 8, 16):
             batched.append(measure_batched(M, max(20, args.steps // 4), max(5, args.warmup // 4)))
+        layer = measure_layer(max(20, args.steps // 4), max(5, args.warmup // 4))
 
     # ---------------- HBM traffic from committed counters ----------------
     traffic = None
@@ -284,6 +345,7 @@ def main():
         "cpu_baseline": cpu,
         "sweep": sweep,
         "batched_p70": batched,
+        "layer_8b_p50": layer,
     }
     print(json.dumps(out))
 

@@ -219,3 +219,16 @@ def test_workspace_bytes():
 def test_strerror():
     for st in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(sgemv.strerror(st), str) and sgemv.strerror(st)
+
+
+def test_fused_projections_rejects_bad_parts():
+    """Packing checks of the projection helper fire before any device work."""
+    q, s, z = synth.random_int4_problem(3, 512, 256)
+    q2, s2, z2 = synth.random_int4_problem(4, 256, 256)
+    with pytest.raises(ValueError):      # N not a multiple of the tile
+        sgemv.FusedProjections([("a", q, s, z), ("b", q2, s2, z2)], device="cpu")
+    q3, s3, z3 = synth.random_int4_problem(5, 512, 384)
+    with pytest.raises(ValueError):      # different K
+        sgemv.FusedProjections([("a", q, s, z), ("b", q3, s3, z3)], device="cpu")
+    with pytest.raises(ValueError):      # duplicate names
+        sgemv.FusedProjections([("a", q, s, z), ("a", q, s, z)], device="cpu")
