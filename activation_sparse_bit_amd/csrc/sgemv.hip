@@ -218,11 +218,14 @@ __global__ __launch_bounds__(1024) void k_gather(const uint16_t* __restrict__ x,
 // applied once per (pass, output); the 16 of the high nibbles at the end.
 //
 // Reduction.  Wavefronts are added by a fixed-order LDS tree.  Slices
-// publish their sums with write-through (sc1) stores, wait for the stores to
-// complete, and count themselves on a per-half-tile atomic counter; the
-// workgroup that arrives last reads every slice's sums (sc1 loads), adds
-// them in slice order and writes y, then resets the counter.  The result
-// does not depend on which workgroup arrives last.
+// publish their sums with device-scope (sc1) stores, which write through the
+// XCD's L2, wait for the stores to complete, and count themselves on a
+// per-half-tile atomic counter; the workgroup that arrives last reads every
+// slice's sums with device-scope loads, which do not return another XCD's
+// stale copy, adds them in slice order and writes y, then resets the
+// counter.  No whole-L2 write-back or invalidation is needed (as full
+// device-scope fences would do, at about 1.7 us per call).  The result does
+// not depend on which workgroup arrives last.
 
 constexpr int kVTile = 256;            // outputs per workgroup (half a layout tile)
 constexpr int kHalfRun = kVTile / 2;   // bytes of one column for those outputs
@@ -1369,6 +1372,380 @@ __global__ __launch_bounds__(FsCfg<MT>::W * 64) __attribute__((amdgpu_waves_per_
 }
 
 // ---------------------------------------------------------------------------
+// fused threshold + union + sparse GEMV for 3 to 16 rows, on the matrix cores
+// ---------------------------------------------------------------------------
+//
+// With many rows the work per weight is one multiply-add per row, a dense
+// contraction over the listed columns, so it goes to v_mfma_f32_16x16x16_f16:
+// the MFMA's rows are 16 outputs, its columns the (up to) 16 batch rows, its
+// depth 16 listed columns.  Workgroup (half tile vt, segment seg) owns
+// columns seg * 1024 .., its wavefront w the group seg * 8 + w, so every
+// wavefront needs one scale per output.  A wavefront
+//   1. loads its 128 activations of every row (lane: row lane / 4, 32
+//      columns), thresholds them per row, ORs the masks over the rows (the
+//      union), and compacts the union's columns and the rows' masked
+//      activations into its own LDS rows;
+//   2. stages its group's zero codes and scales in LDS in "storage order"
+//      (below) and issues the 32-byte weight loads of all its chunks;
+//   3. per chunk of 16 listed columns: lane (column l / 4, quarter l % 4)
+//      dequantizes 64 outputs exactly to fp16 (q - z, or 16 (q - z) for high
+//      nibbles) and writes them to LDS column-major; the A operands come back
+//      with the transposing LDS read ds_read_b64_tr_b16, the B operand (16
+//      rows x 16 columns of activations) with one 8-byte read per lane;
+//   4. scales each output once (1/16 folded in for high nibbles).
+// The workgroup adds its wavefronts in a fixed LDS tree and the segments of
+// a half tile are added by the last workgroup to arrive, in segment order.
+//
+// Storage order: a dword of weights holds outputs 8d .. 8d + 7; the nibble
+// extraction yields them as the pairs (0,4) (1,5) (2,6) (3,7), so storage
+// index s holds output 8 (s / 8) + {0, 4, 1, 5, 2, 6, 3, 7}[s % 8].
+
+namespace fm {
+constexpr int kWaves = 8;
+constexpr int kCols = kGroup;            // one group per wavefront
+constexpr int kSeg = kWaves * kCols;     // columns per workgroup
+constexpr int kRows = 16;                // batch rows (the MFMA's N), padded with zeros
+constexpr int kCh = 16;                  // listed columns per MFMA step (its K)
+constexpr int kMaxCh = kCols / kCh;
+constexpr int kOutFloats = kRows * kVTile;   // one workgroup's sums
+// LDS row strides, padded so that the 16-byte tile writes, the transposing
+// reads and the row-wise accesses spread over the banks
+constexpr int kAStride = kVTile + 8;      // halves per dequantized column
+constexpr int kXStride = kCols + 8;       // halves per activation row
+constexpr int kFStride = kVTile + 8;      // floats per row of the final sums
+}  // namespace fm
+
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef short s4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int fm_out_of(int s) {  // output of storage index s
+    const int j = s & 7;
+    return (s & ~7) + ((j & 1) ? 4 : 0) + (j >> 1);
+}
+__device__ __forceinline__ int fm_store_of(int n) {  // storage index of output n
+    const int j = n & 7;
+    return (n & ~7) + ((j & 3) << 1) + (j >> 2);
+}
+
+struct FmWave {
+    __align__(16) _Float16 a[fm::kCh][fm::kAStride];     // one chunk's dequantized columns, storage order
+    __align__(16) uint16_t xc[fm::kRows][fm::kXStride];  // masked activations by column
+    __align__(16) int k[fm::kCols];                      // the wavefront's union columns
+    __align__(16) _Float16 zc[kVTile];                   // 1024 + z (1024 + 16 z for odd outputs), storage order
+    __align__(16) float sc[kVTile];                      // s (s / 16 for odd outputs), storage order
+};
+
+union FmLds {
+    FmWave w[fm::kWaves];
+    float red[fm::kWaves - 1][fm::kOutFloats];           // wavefront sums 1..7
+    float fin[fm::kRows][fm::kFStride];                  // the workgroup's sums, [row][storage index]
+    GatherShared gl;
+};
+
+__global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fm(RunArgs a) {
+    __shared__ FmLds lds;
+    __shared__ uint32_t last_flag;
+    int bid = blockIdx.x;
+    if (a.idx_out) {  // block 0 writes the list
+        if (bid == 0) {
+            gather_body<fm::kWaves>(a.x, a.M, a.K, a.ldx, a.tc, a.idx_out, a.count_out, lds.gl);
+            return;
+        }
+        --bid;
+    }
+    const int T = a.tiles;
+    const int vt = bid % T;
+    const int seg = bid / T;
+    const int S = a.segs;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int K = a.K;
+    const int Gk = K / kGroup;
+    const int kw = seg * fm::kSeg + wave * fm::kCols;
+    const bool has = kw < K;                       // K is a multiple of 128: the whole group or none
+    const int g = (has ? kw : 0) / kGroup;
+    FmWave& fw = lds.w[wave];
+
+    const int tt = vt >> 1, hh = vt & 1;
+    const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
+    const uint32_t* __restrict__ mdh = a.md + (size_t)tt * Gk * (2 * kVTile) + hh * kVTile;
+
+    // 1. activations: lane (row xm = lane / 4, quarter xq = lane % 4) loads
+    //    32 columns; rows past M read row M - 1 and are masked out
+    const int xm = lane >> 2, xq = lane & 3;
+    const int xmr = xm < a.M ? xm : a.M - 1;
+    uint4 xv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        xv[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)xmr * a.ldx + (has ? kw : 0) + 32 * xq + 8 * i);
+    const u32x4 mdv = *reinterpret_cast<const u32x4*>(mdh + (size_t)g * (2 * kVTile) + 4 * lane);
+
+    const uint32_t code = code_of(a.tc, xmr);
+    const bool row_ok = has && xm < a.M;
+    uint32_t am = 0;
+    uint32_t xw[16];   // the lane's 32 activations, two per word
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xw[4 * i + e] = w4[e];
+            am |= (uint32_t)is_active(w4[e] & 0xFFFFu, code) << (8 * i + 2 * e);
+            am |= (uint32_t)is_active(w4[e] >> 16, code) << (8 * i + 2 * e + 1);
+        }
+    }
+    am = row_ok ? am : 0u;
+    // union over the 16 rows: lanes with the same quarter differ in lane bits
+    // 2..5; rotations by 4 and 8 inside rows of 16 lanes, then the row swaps
+    uint32_t un = am;
+    un |= __builtin_amdgcn_update_dpp(0u, un, 0x124 /* row_ror:4 */, 0xF, 0xF, false);
+    un |= __builtin_amdgcn_update_dpp(0u, un, 0x128 /* row_ror:8 */, 0xF, 0xF, false);
+    {
+        const auto r16 = __builtin_amdgcn_permlane16_swap(un, un, false, false);
+        un = r16[0] | r16[1];
+        const auto r32 = __builtin_amdgcn_permlane32_swap(un, un, false, false);
+        un = r32[0] | r32[1];
+    }
+    uint32_t U[4], base[4];
+    int nact = 0;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+        U[qq] = (uint32_t)__builtin_amdgcn_readlane((int)un, qq);
+        base[qq] = (uint32_t)nact;
+        nact += __popc(U[qq]);
+    }
+    const int nch = (nact + fm::kCh - 1) / fm::kCh;
+
+    // 2a. the union's columns, two per lane
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = 2 * lane + h;
+        const uint32_t Uq = U[c >> 5];
+        const uint32_t bit = 1u << (c & 31);
+        if (Uq & bit) fw.k[base[c >> 5] + __popc(Uq & (bit - 1u))] = kw + c;
+    }
+    // 2b. the lane's row's activations by column, zero where inactive for the row
+    {
+        uint32_t mw[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t lo = ((am >> (2 * j)) & 1u) ? (xw[j] & 0xFFFFu) : 0u;
+            const uint32_t hi = ((am >> (2 * j + 1)) & 1u) ? (xw[j] & 0xFFFF0000u) : 0u;
+            mw[j] = lo | hi;
+        }
+        u32x4* dst = reinterpret_cast<u32x4*>(&fw.xc[xm][32 * xq]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = (u32x4){mw[4 * i], mw[4 * i + 1], mw[4 * i + 2], mw[4 * i + 3]};
+    }
+    // 2c. zero codes and scales of outputs 4 lane .. 4 lane + 3, storage order
+    {
+        const uint32_t mw[4] = {mdv.x, mdv.y, mdv.z, mdv.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int n = 4 * lane + r;
+            const half2_t sz = as_h2(mw[r]);
+            const int st = fm_store_of(n);
+            fw.zc[st] = (r & 1) ? (_Float16)(sz.y * (_Float16)16.0f + (_Float16)1024.0f)
+                                : (_Float16)(sz.y + (_Float16)1024.0f);
+            fw.sc[st] = (r & 1) ? (float)sz.x * 0.0625f : (float)sz.x;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();  // LDS operations of a wavefront complete in order
+
+    // 3. chunks: lane (column cp = lane / 4, quarter cq = lane % 4)
+    f4_t D[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) D[b] = (f4_t){0.f, 0.f, 0.f, 0.f};
+    if (nch > 0) {
+        const int cp = lane >> 2, cq = lane & 3;
+        // every chunk's loads are issued (chunks past the list re-read the first
+        // column), so that chunk c waits only for its own two loads
+        u32x4 wl[fm::kMaxCh][2];
+        const int kfirst = fw.k[0];
+#pragma unroll
+        for (int c = 0; c < fm::kMaxCh; ++c) {
+            const int pos = c * fm::kCh + cp;
+            int k = pos < nact ? fw.k[pos] : kfirst;
+            k = (unsigned)k < (unsigned)K ? k : K - 1;
+            const u32x4* src = reinterpret_cast<const u32x4*>(wcol + (size_t)k * (2 * kHalfRun) + 32 * cq);
+            wl[c][0] = __builtin_nontemporal_load(src);
+            wl[c][1] = __builtin_nontemporal_load(src + 1);
+        }
+        // zero-code pairs of the lane's 64 storage positions 64 cq ..
+        uint32_t zp[32];
+        {
+            const u32x4* zs = reinterpret_cast<const u32x4*>(&fw.zc[64 * cq]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u32x4 u = zs[i];
+                zp[4 * i] = u.x; zp[4 * i + 1] = u.y; zp[4 * i + 2] = u.z; zp[4 * i + 3] = u.w;
+            }
+        }
+        const uint32_t vmagic = 0x64006400u | __builtin_amdgcn_mbcnt_lo(0u, 0u);  // per-lane (VGPR) copy
+        const int bm = lane & 15, bk = lane >> 4;      // B operand: batch row, depth quarter
+        // B operands of every chunk: activations of batch row bm at positions
+        // c * 16 + 4 bk .. + 3 (all LDS reads issued together)
+        uint2 Bx[fm::kMaxCh];
+        {
+            int kc[fm::kMaxCh][4];
+#pragma unroll
+            for (int c = 0; c < fm::kMaxCh; ++c) {
+                const int4 k4 = *reinterpret_cast<const int4*>(&fw.k[c * fm::kCh + 4 * bk]);
+                kc[c][0] = k4.x - kw; kc[c][1] = k4.y - kw; kc[c][2] = k4.z - kw; kc[c][3] = k4.w - kw;
+            }
+#pragma unroll
+            for (int c = 0; c < fm::kMaxCh; ++c) {
+                uint32_t xbv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int p = c * fm::kCh + 4 * bk + j;
+                    const int cc = (unsigned)kc[c][j] < (unsigned)fm::kCols ? kc[c][j] : 0;
+                    const uint32_t v = fw.xc[bm][cc];
+                    xbv[j] = p < nact ? v : 0u;
+                }
+                Bx[c] = make_uint2(xbv[0] | (xbv[1] << 16), xbv[2] | (xbv[3] << 16));
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < fm::kMaxCh; ++c) {
+            if (c < nch) {
+                // dequantize 64 outputs of column (c, cp) into storage order
+                const uint32_t dw[8] = {wl[c][0].x, wl[c][0].y, wl[c][0].z, wl[c][0].w,
+                                        wl[c][1].x, wl[c][1].y, wl[c][1].z, wl[c][1].w};
+                uint32_t outw[32];
+#pragma unroll
+                for (int d = 0; d < 8; ++d) {
+                    const uint32_t Dv = dw[d], D8 = dw[d] >> 8;
+                    const half2_t h0 = as_h2(and_or(Dv, 0x000F000Fu, vmagic)) - as_h2(zp[4 * d]);      // outputs 0, 4
+                    const half2_t h1 = as_h2(and_or(Dv, 0x00F000F0u, vmagic)) - as_h2(zp[4 * d + 1]);  // 16 x (1, 5)
+                    const half2_t h2 = as_h2(and_or(D8, 0x000F000Fu, vmagic)) - as_h2(zp[4 * d + 2]);  // 2, 6
+                    const half2_t h3 = as_h2(and_or(D8, 0x00F000F0u, vmagic)) - as_h2(zp[4 * d + 3]);  // 16 x (3, 7)
+                    outw[4 * d] = __builtin_bit_cast(uint32_t, h0);
+                    outw[4 * d + 1] = __builtin_bit_cast(uint32_t, h1);
+                    outw[4 * d + 2] = __builtin_bit_cast(uint32_t, h2);
+                    outw[4 * d + 3] = __builtin_bit_cast(uint32_t, h3);
+                }
+                u32x4* dst = reinterpret_cast<u32x4*>(&fw.a[cp][64 * cq]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    dst[i] = (u32x4){outw[4 * i], outw[4 * i + 1], outw[4 * i + 2], outw[4 * i + 3]};
+                __builtin_amdgcn_wave_barrier();
+                const h4_t B = __builtin_bit_cast(h4_t, Bx[c]);
+                // A: 16 outputs x 16 columns per block, transposed out of LDS; all
+                // 16 reads in flight before the first product
+                s4_t ar[16];
+#pragma unroll
+                for (int b = 0; b < 16; ++b)
+                    ar[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s4_t*)&fw.a[4 * (lane >> 4) + ((lane & 15) >> 2)][16 * b + 4 * (lane & 3)]);
+                __builtin_amdgcn_sched_barrier(0);  // keep the 16 reads ahead of the products
+#pragma unroll
+                for (int b = 0; b < 16; ++b)
+                    D[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4_t, ar[b]), B, D[b], 0, 0, 0);
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
+        // 4. one scale per output (storage rows 16 b + 4 (lane / 16) + e)
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+            const float4 s4 = *reinterpret_cast<const float4*>(&fw.sc[16 * b + 4 * (lane >> 4)]);
+            D[b].x *= s4.x; D[b].y *= s4.y; D[b].z *= s4.z; D[b].w *= s4.w;
+        }
+    }
+
+    // 5. wavefronts: 1..7 store their sums, wavefront 0 adds them in order
+    __syncthreads();   // every wavefront is done with its own LDS rows
+    if (wave >= 1) {
+#pragma unroll
+        for (int b = 0; b < 16; ++b)
+            *reinterpret_cast<f4_t*>(&lds.red[wave - 1][(64 * b + lane) * 4]) = D[b];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        for (int w = 0; w < fm::kWaves - 1; ++w) {
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+                const f4_t u = *reinterpret_cast<const f4_t*>(&lds.red[w][(64 * b + lane) * 4]);
+                D[b][0] += u[0]; D[b][1] += u[1]; D[b][2] += u[2]; D[b][3] += u[3];
+            }
+        }
+    }
+    __syncthreads();   // the stores above are read; lds.fin may overlap them
+    // the sums as [row][storage index]: D[b][e] of wavefront 0 is row lane % 16,
+    // storage 16 b + 4 (lane / 16) + e
+    if (wave == 0) {
+#pragma unroll
+        for (int b = 0; b < 16; ++b)
+            *reinterpret_cast<float4*>(&lds.fin[lane & 15][16 * b + 4 * (lane >> 4)]) =
+                make_float4(D[b].x, D[b].y, D[b].z, D[b].w);
+    }
+    __syncthreads();
+
+    // 6. thread t: row t / 32, storage 8 (t % 32) .. + 7
+    const int t = threadIdx.x;
+    const int om = t >> 5, os = 8 * (t & 31);
+    float v[8];
+    {
+        const float4 u0 = *reinterpret_cast<const float4*>(&lds.fin[om][os]);
+        const float4 u1 = *reinterpret_cast<const float4*>(&lds.fin[om][os + 4]);
+        v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w; v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+    }
+    auto store_y = [&](const float (&val)[8]) {
+        if (om >= a.M) return;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const size_t n = (size_t)vt * kVTile + fm_out_of(os + j);
+            if (a.out_f32) static_cast<float*>(a.y)[(size_t)om * a.ldy + n] = val[j];
+            else static_cast<_Float16*>(a.y)[(size_t)om * a.ldy + n] = (_Float16)val[j];
+        }
+    };
+    if (S == 1) {
+        store_y(v);
+        return;
+    }
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc(a.partials, (short)0, (int)a.partial_bytes, 0x00020000);
+    const uint32_t tile_base = (uint32_t)vt * a.slices * fm::kOutFloats * 4u;
+    const uint32_t my = ((uint32_t)om * kVTile + os) * 4u;
+    __builtin_amdgcn_raw_buffer_store_b128((u32x4){f2u(v[0]), f2u(v[1]), f2u(v[2]), f2u(v[3])}, prs,
+                                           tile_base + (uint32_t)seg * fm::kOutFloats * 4u + my, 0, kCacheSC1);
+    __builtin_amdgcn_raw_buffer_store_b128((u32x4){f2u(v[4]), f2u(v[5]), f2u(v[6]), f2u(v[7])}, prs,
+                                           tile_base + (uint32_t)seg * fm::kOutFloats * 4u + my + 16u, 0, kCacheSC1);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores acknowledged
+    __syncthreads();                // ... and every thread's, before the count
+    if (t == 0) {
+        const uint32_t old =
+            __hip_atomic_fetch_add(&a.counters[vt * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = (old == (uint32_t)(S - 1)) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (last_flag == 0u) return;
+
+    // last to arrive: every segment's sums, in segment order, 16 segments in flight
+    float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int sb = 0; sb < S; sb += 16) {
+        u32x4 u[16][2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int sl = sb + i < S ? sb + i : sb;
+            const uint32_t off = tile_base + (uint32_t)sl * fm::kOutFloats * 4u + my;
+            u[i][0] = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, kCacheSC1);
+            u[i][1] = __builtin_amdgcn_raw_buffer_load_b128(prs, off + 16u, 0, kCacheSC1);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (sb + i < S) {
+                tot[0] += u2f(u[i][0].x); tot[1] += u2f(u[i][0].y); tot[2] += u2f(u[i][0].z); tot[3] += u2f(u[i][0].w);
+                tot[4] += u2f(u[i][1].x); tot[5] += u2f(u[i][1].y); tot[6] += u2f(u[i][1].z); tot[7] += u2f(u[i][1].w);
+            }
+        }
+    }
+    store_y(tot);
+    if (t == 0) __hip_atomic_store(&a.counters[vt * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 constexpr int kTargetWGs = 256;   // about one workgroup per CU
@@ -1443,6 +1820,16 @@ size_t ws_partial_bytes(const sgemv_desc* d, int mt) {
     const int tiles = d->N / kVTile;
     const int s = slices_for(d, mt);
     return s > 1 ? (size_t)tiles * s * mt * kVTile * sizeof(float) : 0;
+}
+
+// Partial sums of the fused call with M rows: one or two rows use the
+// list-driven layout (slices_for stride), 3 to 16 rows 16 rows per 1024-column
+// segment.
+size_t ws_fused_bytes(const sgemv_desc* d, int M) {
+    if (M <= 2) return ws_partial_bytes(d, M);
+    const int tiles = d->N / kVTile;
+    const int segs = (d->K + fm::kSeg - 1) / fm::kSeg;
+    return segs > 1 ? (size_t)tiles * segs * fm::kOutFloats * sizeof(float) : 0;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -1535,7 +1922,7 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     if (!packed || !x || !y || !thr) return SGEMV_EINVAL;
     if ((idx == nullptr) != (count == nullptr)) return SGEMV_EINVAL;
     if (flags & ~SGEMV_OUT_F32) return SGEMV_EINVAL;
-    if (M < 1 || M > 2) return SGEMV_ESIZE;
+    if (M < 1 || M > SGEMV_MAX_BATCH) return SGEMV_ESIZE;
     if (ldx < d->K || ldy < d->N) return SGEMV_ESIZE;
     if (ldx % 8 || ldy % 8) return SGEMV_EALIGN;
     if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16)) return SGEMV_EALIGN;
@@ -1546,9 +1933,14 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     st = fill_codes(thr, M, a.tc);
     if (st) return st;
     a.tiles = d->N / kVTile;
-    a.slices = slices_for(d, M);   // stride of the partials region
-    const int seg_cols = M == 1 ? FsCfg<1>::kSeg : FsCfg<2>::kSeg;
-    a.segs = (d->K + seg_cols - 1) / seg_cols;
+    if (M <= 2) {
+        a.slices = slices_for(d, M);   // stride of the partials region
+        const int seg_cols = M == 1 ? FsCfg<1>::kSeg : FsCfg<2>::kSeg;
+        a.segs = (d->K + seg_cols - 1) / seg_cols;
+    } else {
+        a.segs = (d->K + fm::kSeg - 1) / fm::kSeg;
+        a.slices = a.segs;
+    }
     if (a.segs > 1) {
         if (!ws) return SGEMV_EINVAL;
         if (!aligned(ws, 256)) return SGEMV_EALIGN;
@@ -1562,7 +1954,7 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     a.count_out = count;
     a.counters = static_cast<uint32_t*>(ws);
     a.partials = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ws_counters_bytes(a.tiles)) : nullptr;
-    a.partial_bytes = (uint32_t)ws_partial_bytes(d, M);
+    a.partial_bytes = (uint32_t)ws_fused_bytes(d, M);
     a.K = d->K;
     a.ldx = ldx;
     a.ldy = ldy;
@@ -1571,7 +1963,8 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     const dim3 grid((unsigned)(a.tiles * a.segs + (idx ? 1 : 0)));  // + the list's workgroup
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (M == 1) hipLaunchKernelGGL((k_fs<1>), grid, dim3(FsCfg<1>::W * 64), 0, s, a);
-    else hipLaunchKernelGGL((k_fs<2>), grid, dim3(FsCfg<2>::W * 64), 0, s, a);
+    else if (M == 2) hipLaunchKernelGGL((k_fs<2>), grid, dim3(FsCfg<2>::W * 64), 0, s, a);
+    else hipLaunchKernelGGL(k_fm, grid, dim3(fm::kWaves * 64), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         g_last_hip_error = (int)e;
@@ -1628,9 +2021,13 @@ extern "C" int sgemv_run_batched(const sgemv_desc* d, const void* packed, const 
 extern "C" size_t sgemv_workspace_bytes(const sgemv_desc* d, int32_t M) {
     if (check_desc(d) != SGEMV_OK || M < 1 || M > SGEMV_MAX_BATCH) return 0;
     const int tiles = d->N / kVTile;
-    size_t part = 0;  // enough for every batch size up to M
+    size_t part = 0;  // enough for every call with up to M rows
     for (int mt = 1; mt <= pow2_ceil(M); mt *= 2) {
         const size_t b = ws_partial_bytes(d, mt);
+        part = b > part ? b : part;
+    }
+    for (int m = 1; m <= M; ++m) {
+        const size_t b = ws_fused_bytes(d, m);
         part = b > part ? b : part;
     }
     return ws_counters_bytes(tiles) + part;

@@ -16,8 +16,8 @@
  *   sgemv_run             device: y = W . x over the listed columns (M = 1)
  *   sgemv_run_batched     device: M <= 16 rows over the union list, each row
  *                         masked by its own threshold
- *   sgemv_run_fused       device: threshold, compact and GEMV in one launch
- *                         (M <= 2), the list optional
+ *   sgemv_run_fused       device: threshold, union, compact and GEMV in one
+ *                         launch (M <= 16), the list optional
  *
  * Weights.  W is [N][K] (output x input, like a Linear weight), quantized
  * asymmetrically to 4 bits with one fp16 scale s and one fp16 zero-point z
@@ -211,16 +211,20 @@ int sgemv_run_batched(const sgemv_desc* d, const void* packed,
  * sgemv_run_fused - the gathering step and the GEMV in one launch, so that
  * no kernel boundary and no round trip through a global list separate the
  * thresholding from the weight reads (the page's Abstract asks for index
- * gathering with minimal overhead).  Each workgroup thresholds its own
- * 512-column segment, compacts the active columns in LDS and reads only
- * their weight bytes; segments are summed as in sgemv_run.
+ * gathering with minimal overhead).  Each wavefront thresholds one
+ * 128-column group of every row, compacts the columns active in any row in
+ * LDS and reads only their weight bytes; the workgroups of 1024-column
+ * segments are summed as in sgemv_run.
  *   y[m][n] = sum over active k of w^[n][k] * xe[m][k]
  * with xe and the union of active columns as in sgemv_run_batched (with
  * thresholds), which it equals within the same error bound (the order of
  * the fp32 additions differs, so the bits may differ).
  *
- *   M          1 or 2 (ESIZE otherwise; use sgemv_gather_indices and
- *              sgemv_run_batched for more rows)
+ *   M          1..SGEMV_MAX_BATCH.  One or two rows run on the vector
+ *              units; 3 to 16 rows run on the matrix cores
+ *              (v_mfma_f32_16x16x16_f16 over exactly dequantized fp16
+ *              q - z, fp32 accumulation), each row masked by its own
+ *              threshold over the union of the rows' active columns
  *   thresholds host float [M], each finite and >= 0 (required)
  *   idx, count both NULL, or both device int32 ([K] and [1], 4-byte
  *              aligned): then they receive exactly what

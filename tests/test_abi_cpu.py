@@ -191,7 +191,7 @@ def test_run_fused_validation():
     assert f(pd, FAKE, FAKE, 1, K, tp, FAKE, FAKE, FAKE, N, 2, FAKE, None) == E.SGEMV_EINVAL
     assert f(pd, FAKE, FAKE, 1, K, tp, None, None, FAKE, N, 0, None, None) == E.SGEMV_EINVAL  # no workspace
     assert f(pd, FAKE, FAKE, 0, K, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_ESIZE
-    assert f(pd, FAKE, FAKE, 3, K, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_ESIZE
+    assert f(pd, FAKE, FAKE, 17, K, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_ESIZE
     assert f(pd, FAKE, FAKE, 2, K - 8, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_ESIZE
     assert f(pd, FAKE, FAKE, 2, K + 4, tp, FAKE, FAKE, FAKE, N, 0, FAKE, None) == E.SGEMV_EALIGN
     assert f(pd, FAKE, FAKE, 1, K, tp, FAKE, FAKE, FAKE + 4, N, 0, FAKE, None) == E.SGEMV_EALIGN

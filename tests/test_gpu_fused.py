@@ -168,14 +168,12 @@ def test_fused_deterministic_and_scale_equivariant():
     x = synth.glu_activation(0, K)
     t = synth.percentile_threshold(x, 0.5)
     outs = []
-    for scale in (1.0, 1.0, 2.0):
+    for scale in (1.0, 1.0, 2.0):   # fp32 output: fp16 rounding of subnormal results is not scale-exact
         xs = (x.astype(np.float32) * scale).astype(np.float16)
-        y, _, _ = _fused(pm, xs, [t * scale], want_list=False)
-        outs.append(y.astype(np.float16).view(np.uint16))
-    assert np.array_equal(outs[0], outs[1])
-    y1 = outs[0].view(np.float16).astype(np.float32)
-    y2 = outs[2].view(np.float16).astype(np.float32)
-    assert np.array_equal(y2, 2 * y1)
+        y, _, _ = _fused(pm, xs, [t * scale], want_list=False, dtype=torch.float32)
+        outs.append(y)
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))   # bitwise repeatable
+    assert np.array_equal(outs[2], 2 * outs[0])                               # exact doubling
 
 
 def test_fused_agrees_with_gather_and_run():
@@ -197,3 +195,89 @@ def test_fused_agrees_with_gather_and_run():
     assert int(cnt.item()) == c_f and np.array_equal(idx.cpu().numpy(), idx_f)
     ys = y.cpu().numpy()
     assert np.max(np.abs(yf[0] - ys)) <= 1e-5 * np.max(np.abs(ys))
+
+
+# ---------------------------------------------------------------------------
+# 3 to 16 rows (matrix-core kernel)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M", [3, 4, 5, 8, 13, 16])
+def test_fused_batched_rows(M):
+    K, N = 14336, 4096
+    q, s, z = G.weights(0, N, K, 0.02)
+    pm = G.packed(0, N, K, 0.02)
+    X = np.stack([synth.glu_activation(m, K) for m in range(M)])
+    ts = [synth.percentile_threshold(X[m], 0.7) for m in range(M)]
+    y, idx, c = _fused(pm, X, ts)
+    _check_list(idx, c, X, ts)
+    rows = G.sample_rows(N, 384, seed=M)
+    y_ref, B, _ = G.oracle_rows(q, s, z, X, ts, rows)
+    G.check_y(y[:, rows], y_ref, B, f"fused M={M}")
+
+
+@pytest.mark.parametrize("K,N", [(128, 512), (640, 512), (1152, 1536), (2176, 1024)])
+def test_fused_batched_ragged(K, N):
+    """K below and not a multiple of the 1024-column segment; every row has
+    its own threshold; fp32 output."""
+    from activation_sparse_bit_amd import sgemv
+    q, s, z = synth.random_int4_problem(K + 2 * N, N, K)
+    pm = sgemv.PackedMatrix(q, s, z, device=G.torch_dev())
+    M = 7
+    X = np.stack([synth.plain_activation(10 + m, K) for m in range(M)])
+    ts = [0.2 * m for m in range(M)]
+    y, idx, c = _fused(pm, X, ts, dtype=torch.float32, ldx=K + 8, ldy=N + 24)
+    _check_list(idx, c, X, ts)
+    y_ref, B, _ = oracle.gemv_masked(q, s, z, X, ts)
+    G.check_y(y, y_ref, B, f"fused M=7 {K}x{N}")
+
+
+def test_fused_batched_dense_fp32_and_empty():
+    K, N = 4096, 4096
+    q, s, z = G.weights(1, N, K, 0.02)
+    pm = G.packed(1, N, K, 0.02)
+    M = 16
+    X = np.stack([synth.plain_activation(20 + m, K) for m in range(M)])
+    y, idx, c = _fused(pm, X, [0.0] * M, dtype=torch.float32)
+    assert c == K and np.array_equal(idx, np.arange(K))
+    rows = G.sample_rows(N, 512, seed=3)
+    y_ref, B = oracle.gemv_dense(q[rows], s[rows], z[rows], X)
+    rel = G.check_y(y[:, rows], y_ref, B, "fused M=16 t=0")
+    assert rel < 2e-6          # products exact, fp32 accumulation only
+    Z = np.zeros((5, K), dtype=np.float16)
+    y, idx, c = _fused(pm, Z, [0.5] * 5)
+    assert c == 0 and np.all(y == 0) and not np.any(np.signbit(y))
+
+
+def test_fused_batched_deterministic_and_scale_equivariant():
+    K, N = 14336, 4096
+    pm = G.packed(0, N, K, 0.02)
+    M = 8
+    X = np.stack([synth.glu_activation(m, K) for m in range(M)])
+    ts = [synth.percentile_threshold(X[m], 0.7) for m in range(M)]
+    outs = []
+    for scale in (1.0, 1.0, 2.0):   # fp32 output: fp16 rounding of subnormal results is not scale-exact
+        Xs = (X.astype(np.float32) * scale).astype(np.float16)
+        y, _, _ = _fused(pm, Xs, [t * scale for t in ts], want_list=False, dtype=torch.float32)
+        outs.append(y)
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))   # bitwise repeatable
+    assert np.array_equal(outs[2], 2 * outs[0])                               # exact doubling
+
+
+def test_fused_batched_agrees_with_run_batched():
+    """Same rows through gather + run_batched: same list, outputs within fp32
+    reassociation of each other."""
+    from activation_sparse_bit_amd import sgemv
+    K, N, M = 14336, 4096, 8
+    pm = G.packed(0, N, K, 0.02)
+    X = np.stack([synth.glu_activation(m, K) for m in range(M)])
+    ts = [synth.percentile_threshold(X[m], 0.7) for m in range(M)]
+    yf, idx_f, c_f = _fused(pm, X, ts, dtype=torch.float32)
+    xd = G.to_dev(X)
+    idx = torch.full((K,), -7, dtype=torch.int32, device=G.torch_dev())
+    cnt = torch.zeros(1, dtype=torch.int32, device=G.torch_dev())
+    Y = torch.empty((M, N), dtype=torch.float32, device=G.torch_dev())
+    sgemv.sgemv_gather_indices(xd, ts, idx, cnt)
+    sgemv.sgemv_run_batched(pm.desc, pm.blob, xd, ts, idx, cnt, Y, pm.workspace)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == c_f and np.array_equal(idx.cpu().numpy(), idx_f)
+    ys = Y.cpu().numpy()
+    assert np.max(np.abs(yf - ys)) <= 1e-5 * np.max(np.abs(ys))
