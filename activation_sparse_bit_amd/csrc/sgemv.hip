@@ -123,6 +123,29 @@ struct GatherShared {
     uint32_t wtot[16];
 };
 
+// Union over rows 0..M-1 of the 8-column masks at column col: the rows are
+// loaded RB at a time, all in flight together (rows past M repeat row M - 1,
+// whose mask is already in).
+template <int RB>
+__device__ __forceinline__ uint32_t union_mask8(const uint16_t* __restrict__ x, int M, int ldx, int col,
+                                                const Codes& tc) {
+    uint32_t m8 = 0;
+    for (int m0 = 0; m0 < M; m0 += RB) {
+        uint4 v[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int mr = m0 + r < M ? m0 + r : M - 1;
+            v[r] = *reinterpret_cast<const uint4*>(x + (size_t)mr * ldx + col);
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int mr = m0 + r < M ? m0 + r : M - 1;
+            m8 |= mask8_of(v[r], code_of(tc, mr));
+        }
+    }
+    return m8;
+}
+
 // Wavefronts W and above of the workgroup only join the barrier.
 template <int W>
 __device__ __forceinline__ void gather_body(const uint16_t* __restrict__ x, int M, int K, int ldx, const Codes& tc,
@@ -140,10 +163,9 @@ __device__ __forceinline__ void gather_body(const uint16_t* __restrict__ x, int 
         const int off = s * 512 + lane * 8;
         uint32_t m8 = 0;
         if (off < Kw) {
-            for (int m = 0; m < M; ++m) {
-                const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)m * ldx + base + off);
-                m8 |= mask8_of(v, code_of(tc, m));
-            }
+            m8 = M >= 8 ? union_mask8<8>(x, M, ldx, base + off, tc)
+               : M >= 4 ? union_mask8<4>(x, M, ldx, base + off, tc)
+                        : union_mask8<1>(x, M, ldx, base + off, tc);
             gs.masks[(base + off) >> 3] = (uint8_t)m8;
         }
         uint32_t pre, tot;
@@ -221,15 +243,24 @@ __global__ __launch_bounds__(1024) void k_gather(const uint16_t* __restrict__ x,
 // publish their sums with device-scope (sc1) stores, which write through the
 // XCD's L2, wait for the stores to complete, and count themselves on a
 // per-half-tile atomic counter; the workgroup that arrives last reads every
-// slice's sums with device-scope loads, which do not return another XCD's
-// stale copy, adds them in slice order and writes y, then resets the
-// counter.  No whole-L2 write-back or invalidation is needed (as full
-// device-scope fences would do, at about 1.7 us per call).  The result does
-// not depend on which workgroup arrives last.
+// slice's sums, adds them in slice order and writes y, then resets the
+// counter.  Its loads must not return a stale L2 copy of another XCD's slice:
+// the one- and two-row kernels use device-scope (sc1) loads, which miss in
+// L2; the many-row kernel, whose last read is up to 16 times larger, takes a
+// device-scope acquire (dropping its XCD's L2 copies) and then uses ordinary
+// loads, which is faster there but slows the one-row kernel, where other
+// workgroups on the XCD are still streaming when it runs.  The writers need
+// no whole-L2 write-back (a device-scope release would cost about 1.7 us per
+// call): their stores write through.  The result does not depend on which
+// workgroup arrives last.
 
 constexpr int kVTile = 256;            // outputs per workgroup (half a layout tile)
 constexpr int kHalfRun = kVTile / 2;   // bytes of one column for those outputs
 constexpr uint32_t kCacheSC1 = 16;     // cache policy: coherent at device scope
+
+// The last workgroup's view of the slices the others published (before
+// ordinary loads of them).
+__device__ __forceinline__ void acquire_slices() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -1376,72 +1407,72 @@ __global__ __launch_bounds__(FsCfg<MT>::W * 64) __attribute__((amdgpu_waves_per_
 // ---------------------------------------------------------------------------
 //
 // With many rows the work per weight is one multiply-add per row, a dense
-// contraction over the listed columns, so it goes to v_mfma_f32_16x16x16_f16:
+// contraction over the listed columns, so it goes to v_mfma_f32_16x16x32_f16:
 // the MFMA's rows are 16 outputs, its columns the (up to) 16 batch rows, its
-// depth 16 listed columns.  Workgroup (half tile vt, segment seg) owns
+// depth 32 listed columns.  Workgroup (half tile vt, segment seg) owns
 // columns seg * 1024 .., its wavefront w the group seg * 8 + w, so every
 // wavefront needs one scale per output.  A wavefront
 //   1. loads its 128 activations of every row (lane: row lane / 4, 32
 //      columns), thresholds them per row, ORs the masks over the rows (the
-//      union), and compacts the union's columns and the rows' masked
-//      activations into its own LDS rows;
-//   2. stages its group's zero codes and scales in LDS in "storage order"
-//      (below) and issues the 32-byte weight loads of all its chunks;
-//   3. per chunk of 16 listed columns: lane (column l / 4, quarter l % 4)
-//      dequantizes 64 outputs exactly to fp16 (q - z, or 16 (q - z) for high
-//      nibbles) and writes them to LDS column-major; the A operands come back
-//      with the transposing LDS read ds_read_b64_tr_b16, the B operand (16
-//      rows x 16 columns of activations) with one 8-byte read per lane;
+//      union), and compacts the union's columns; the rows' masked
+//      activations are kept by column;
+//   2. issues the 16-byte weight loads of all its chunks of 32 listed columns
+//      (8 columns per load instruction, as in the one-row kernels);
+//   3. per chunk: stores the raw weight bytes in LDS (32 columns x 128
+//      bytes), and reads them back with the transposing ds_read_b64_tr_b8:
+//      lane (depth quarter g = lane / 16, i = lane % 16) receives byte i of the
+//      block of 16 bytes b of 8 consecutive listed columns, that is the low
+//      nibbles of output 32 b + 2 i and the high nibbles of output 32 b + 2 i
+//      + 1 for those columns - an A operand row for each.  It dequantizes
+//      them exactly to fp16 in registers (q - z; 16 (q - z) for the high
+//      nibbles) and runs two MFMAs per block;
 //   4. scales each output once (1/16 folded in for high nibbles).
-// The workgroup adds its wavefronts in a fixed LDS tree and the segments of
-// a half tile are added by the last workgroup to arrive, in segment order.
+// The workgroup adds its wavefronts in a fixed order in LDS (every thread a
+// slice of the sums); the segments of a half tile are added by the last
+// workgroup to arrive, in segment order, with only the M rows in use stored.
 //
-// Storage order: a dword of weights holds outputs 8d .. 8d + 7; the nibble
-// extraction yields them as the pairs (0,4) (1,5) (2,6) (3,7), so storage
-// index s holds output 8 (s / 8) + {0, 4, 1, 5, 2, 6, 3, 7}[s % 8].
+// Storage order of the sums: index s = 32 b + 16 p + r holds output
+// 32 b + 2 r + p (p = 0 for low nibbles, 1 for high).
 
 namespace fm {
 constexpr int kWaves = 8;
 constexpr int kCols = kGroup;            // one group per wavefront
 constexpr int kSeg = kWaves * kCols;     // columns per workgroup
 constexpr int kRows = 16;                // batch rows (the MFMA's N), padded with zeros
-constexpr int kCh = 16;                  // listed columns per MFMA step (its K)
+constexpr int kCh = 32;                  // listed columns per MFMA step (its K)
 constexpr int kMaxCh = kCols / kCh;
 constexpr int kOutFloats = kRows * kVTile;   // one workgroup's sums
 // LDS row strides, padded so that the 16-byte tile writes, the transposing
 // reads and the row-wise accesses spread over the banks
-constexpr int kAStride = kVTile + 8;      // halves per dequantized column
+constexpr int kRStride = kHalfRun + 16;   // bytes per staged weight column
 constexpr int kXStride = kCols + 8;       // halves per activation row
-constexpr int kFStride = kVTile + 8;      // floats per row of the final sums
 }  // namespace fm
 
-typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
-typedef short s4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef int i2_t __attribute__((ext_vector_type(2)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int fm_out_of(int s) {  // output of storage index s
-    const int j = s & 7;
-    return (s & ~7) + ((j & 1) ? 4 : 0) + (j >> 1);
+    return (s & ~31) + 2 * (s & 15) + ((s >> 4) & 1);
 }
 __device__ __forceinline__ int fm_store_of(int n) {  // storage index of output n
-    const int j = n & 7;
-    return (n & ~7) + ((j & 3) << 1) + (j >> 2);
+    return (n & ~31) + 16 * (n & 1) + ((n & 31) >> 1);
 }
 
 struct FmWave {
-    __align__(16) _Float16 a[fm::kCh][fm::kAStride];     // one chunk's dequantized columns, storage order
+    __align__(16) uint8_t r[fm::kCh][fm::kRStride];      // one chunk's raw weight bytes
     __align__(16) uint16_t xc[fm::kRows][fm::kXStride];  // masked activations by column
     __align__(16) int k[fm::kCols];                      // the wavefront's union columns
-    __align__(16) _Float16 zc[kVTile];                   // 1024 + z (1024 + 16 z for odd outputs), storage order
+    __align__(16) uint32_t zc[kVTile / 2];               // per weight byte: (1024 + z, 1024 + 16 z)
     __align__(16) float sc[kVTile];                      // s (s / 16 for odd outputs), storage order
 };
 
 union FmLds {
     FmWave w[fm::kWaves];
-    float red[fm::kWaves - 1][fm::kOutFloats];           // wavefront sums 1..7
-    float fin[fm::kRows][fm::kFStride];                  // the workgroup's sums, [row][storage index]
+    float red[fm::kWaves][fm::kOutFloats];               // every wavefront's sums
     GatherShared gl;
 };
+
 
 __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fm(RunArgs a) {
     __shared__ FmLds lds;
@@ -1538,180 +1569,178 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[i] = (u32x4){mw[4 * i], mw[4 * i + 1], mw[4 * i + 2], mw[4 * i + 3]};
     }
-    // 2c. zero codes and scales of outputs 4 lane .. 4 lane + 3, storage order
+    // 2c. zero codes of the weight bytes 2 lane, 2 lane + 1 (outputs 4 lane ..
+    //     4 lane + 3) and their scales in storage order
     {
         const uint32_t mw[4] = {mdv.x, mdv.y, mdv.z, mdv.w};
+        uint32_t zpair[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const half2_t se = as_h2(mw[2 * h]), so = as_h2(mw[2 * h + 1]);
+            const half2_t zp = (half2_t){(_Float16)(se.y + (_Float16)1024.0f),
+                                         (_Float16)(so.y * (_Float16)16.0f + (_Float16)1024.0f)};
+            zpair[h] = __builtin_bit_cast(uint32_t, zp);
+        }
+        *reinterpret_cast<uint2*>(&fw.zc[2 * lane]) = make_uint2(zpair[0], zpair[1]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int n = 4 * lane + r;
             const half2_t sz = as_h2(mw[r]);
-            const int st = fm_store_of(n);
-            fw.zc[st] = (r & 1) ? (_Float16)(sz.y * (_Float16)16.0f + (_Float16)1024.0f)
-                                : (_Float16)(sz.y + (_Float16)1024.0f);
-            fw.sc[st] = (r & 1) ? (float)sz.x * 0.0625f : (float)sz.x;
+            fw.sc[fm_store_of(4 * lane + r)] = (r & 1) ? (float)sz.x * 0.0625f : (float)sz.x;
         }
     }
     __builtin_amdgcn_wave_barrier();  // LDS operations of a wavefront complete in order
 
-    // 3. chunks: lane (column cp = lane / 4, quarter cq = lane % 4)
-    f4_t D[16];
+    // 3. chunks of 32 listed columns
+    f4_t D[16];   // [2 b + p]: output block b (32 outputs), nibble p
 #pragma unroll
     for (int b = 0; b < 16; ++b) D[b] = (f4_t){0.f, 0.f, 0.f, 0.f};
     if (nch > 0) {
-        const int cp = lane >> 2, cq = lane & 3;
-        // every chunk's loads are issued (chunks past the list re-read the first
-        // column), so that chunk c waits only for its own two loads
-        u32x4 wl[fm::kMaxCh][2];
+        // loads: instruction i of chunk c, lane (lc = lane / 8, lo = lane % 8)
+        // reads bytes 16 lo .. 16 lo + 15 of listed column c * 32 + 8 i + lc;
+        // every chunk's loads are issued (positions past the list re-read the
+        // first column), so that chunk c waits only for its own four
+        const int lc = lane >> 3, lo = lane & 7;
+        u32x4 wl[fm::kMaxCh][4];
         const int kfirst = fw.k[0];
 #pragma unroll
-        for (int c = 0; c < fm::kMaxCh; ++c) {
-            const int pos = c * fm::kCh + cp;
-            int k = pos < nact ? fw.k[pos] : kfirst;
-            k = (unsigned)k < (unsigned)K ? k : K - 1;
-            const u32x4* src = reinterpret_cast<const u32x4*>(wcol + (size_t)k * (2 * kHalfRun) + 32 * cq);
-            wl[c][0] = __builtin_nontemporal_load(src);
-            wl[c][1] = __builtin_nontemporal_load(src + 1);
-        }
-        // zero-code pairs of the lane's 64 storage positions 64 cq ..
-        uint32_t zp[32];
-        {
-            const u32x4* zs = reinterpret_cast<const u32x4*>(&fw.zc[64 * cq]);
+        for (int c = 0; c < fm::kMaxCh; ++c)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const u32x4 u = zs[i];
-                zp[4 * i] = u.x; zp[4 * i + 1] = u.y; zp[4 * i + 2] = u.z; zp[4 * i + 3] = u.w;
+            for (int i = 0; i < 4; ++i) {
+                const int pos = c * fm::kCh + 8 * i + lc;
+                int k = pos < nact ? fw.k[pos] : kfirst;
+                k = (unsigned)k < (unsigned)K ? k : K - 1;
+                wl[c][i] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(wcol + (size_t)k * (2 * kHalfRun)) + lo);
+            }
+        const int g = lane >> 4, li = lane & 15;   // A/B operand: depth quarter, row
+        // zero codes of the lane's A rows: weight byte 16 b + li, b = 0..7
+        uint32_t zq[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) zq[b] = fw.zc[16 * b + li];
+        // B operands of every chunk: activations of batch row li at positions
+        // c * 32 + 8 g .. + 7 (all LDS reads issued together)
+        uint32_t Bx[fm::kMaxCh][4];
+        {
+            int kc[fm::kMaxCh][8];
+#pragma unroll
+            for (int c = 0; c < fm::kMaxCh; ++c) {
+                const int4 k0 = *reinterpret_cast<const int4*>(&fw.k[c * fm::kCh + 8 * g]);
+                const int4 k1 = *reinterpret_cast<const int4*>(&fw.k[c * fm::kCh + 8 * g + 4]);
+                const int kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) kc[c][j] = kv[j] - kw;
+            }
+#pragma unroll
+            for (int c = 0; c < fm::kMaxCh; ++c) {
+                uint32_t xv[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int p = c * fm::kCh + 8 * g + j;
+                    const int cc = (unsigned)kc[c][j] < (unsigned)fm::kCols ? kc[c][j] : 0;
+                    const uint32_t v = fw.xc[li][cc];
+                    xv[j] = p < nact ? v : 0u;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Bx[c][j] = xv[2 * j] | (xv[2 * j + 1] << 16);
             }
         }
         const uint32_t vmagic = 0x64006400u | __builtin_amdgcn_mbcnt_lo(0u, 0u);  // per-lane (VGPR) copy
-        const int bm = lane & 15, bk = lane >> 4;      // B operand: batch row, depth quarter
-        // B operands of every chunk: activations of batch row bm at positions
-        // c * 16 + 4 bk .. + 3 (all LDS reads issued together)
-        uint2 Bx[fm::kMaxCh];
-        {
-            int kc[fm::kMaxCh][4];
-#pragma unroll
-            for (int c = 0; c < fm::kMaxCh; ++c) {
-                const int4 k4 = *reinterpret_cast<const int4*>(&fw.k[c * fm::kCh + 4 * bk]);
-                kc[c][0] = k4.x - kw; kc[c][1] = k4.y - kw; kc[c][2] = k4.z - kw; kc[c][3] = k4.w - kw;
-            }
-#pragma unroll
-            for (int c = 0; c < fm::kMaxCh; ++c) {
-                uint32_t xbv[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int p = c * fm::kCh + 4 * bk + j;
-                    const int cc = (unsigned)kc[c][j] < (unsigned)fm::kCols ? kc[c][j] : 0;
-                    const uint32_t v = fw.xc[bm][cc];
-                    xbv[j] = p < nact ? v : 0u;
-                }
-                Bx[c] = make_uint2(xbv[0] | (xbv[1] << 16), xbv[2] | (xbv[3] << 16));
-            }
-        }
 #pragma unroll
         for (int c = 0; c < fm::kMaxCh; ++c) {
             if (c < nch) {
-                // dequantize 64 outputs of column (c, cp) into storage order
-                const uint32_t dw[8] = {wl[c][0].x, wl[c][0].y, wl[c][0].z, wl[c][0].w,
-                                        wl[c][1].x, wl[c][1].y, wl[c][1].z, wl[c][1].w};
-                uint32_t outw[32];
 #pragma unroll
-                for (int d = 0; d < 8; ++d) {
-                    const uint32_t Dv = dw[d], D8 = dw[d] >> 8;
-                    const half2_t h0 = as_h2(and_or(Dv, 0x000F000Fu, vmagic)) - as_h2(zp[4 * d]);      // outputs 0, 4
-                    const half2_t h1 = as_h2(and_or(Dv, 0x00F000F0u, vmagic)) - as_h2(zp[4 * d + 1]);  // 16 x (1, 5)
-                    const half2_t h2 = as_h2(and_or(D8, 0x000F000Fu, vmagic)) - as_h2(zp[4 * d + 2]);  // 2, 6
-                    const half2_t h3 = as_h2(and_or(D8, 0x00F000F0u, vmagic)) - as_h2(zp[4 * d + 3]);  // 16 x (3, 7)
-                    outw[4 * d] = __builtin_bit_cast(uint32_t, h0);
-                    outw[4 * d + 1] = __builtin_bit_cast(uint32_t, h1);
-                    outw[4 * d + 2] = __builtin_bit_cast(uint32_t, h2);
-                    outw[4 * d + 3] = __builtin_bit_cast(uint32_t, h3);
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<u32x4*>(&fw.r[8 * i + lc][16 * lo]) = wl[c][i];
+                __builtin_amdgcn_wave_barrier();
+                // byte li of block b of columns 8 g .. 8 g + 7, transposed out of LDS
+                i2_t rb[8];
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    rb[b] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) i2_t*)&fw.r[8 * g + (li >> 1)][16 * b + 8 * (li & 1)]);
+                __builtin_amdgcn_sched_barrier(0);  // keep the 8 reads ahead of the products
+                const h8_t B = __builtin_bit_cast(h8_t, (u32x4){Bx[c][0], Bx[c][1], Bx[c][2], Bx[c][3]});
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    const half2_t z2 = as_h2(zq[b]);
+                    const uint32_t dw2[2] = {(uint32_t)rb[b].x, (uint32_t)rb[b].y};
+                    uint32_t ae[4], ao[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        // bytes 2 (j % 2), 2 (j % 2) + 1 of the dword into the low bytes of the halves
+                        const uint32_t Dd = dw2[j >> 1];
+                        const uint32_t b0 = 2 * (j & 1);
+                        const uint32_t P = __builtin_amdgcn_perm(Dd, Dd, (0x0Cu << 24) | ((b0 + 1) << 16) | (0x0Cu << 8) | b0);
+                        const half2_t e = as_h2(and_or(P, 0x000F000Fu, vmagic)) - (half2_t){z2.x, z2.x};  // q - z
+                        const half2_t o = as_h2(and_or(P, 0x00F000F0u, vmagic)) - (half2_t){z2.y, z2.y};  // 16 (q - z)
+                        ae[j] = __builtin_bit_cast(uint32_t, e);
+                        ao[j] = __builtin_bit_cast(uint32_t, o);
+                    }
+                    D[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(h8_t, (u32x4){ae[0], ae[1], ae[2], ae[3]}), B, D[2 * b], 0, 0, 0);
+                    D[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(h8_t, (u32x4){ao[0], ao[1], ao[2], ao[3]}), B, D[2 * b + 1], 0, 0, 0);
                 }
-                u32x4* dst = reinterpret_cast<u32x4*>(&fw.a[cp][64 * cq]);
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    dst[i] = (u32x4){outw[4 * i], outw[4 * i + 1], outw[4 * i + 2], outw[4 * i + 3]};
-                __builtin_amdgcn_wave_barrier();
-                const h4_t B = __builtin_bit_cast(h4_t, Bx[c]);
-                // A: 16 outputs x 16 columns per block, transposed out of LDS; all
-                // 16 reads in flight before the first product
-                s4_t ar[16];
-#pragma unroll
-                for (int b = 0; b < 16; ++b)
-                    ar[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s4_t*)&fw.a[4 * (lane >> 4) + ((lane & 15) >> 2)][16 * b + 4 * (lane & 3)]);
-                __builtin_amdgcn_sched_barrier(0);  // keep the 16 reads ahead of the products
-#pragma unroll
-                for (int b = 0; b < 16; ++b)
-                    D[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4_t, ar[b]), B, D[b], 0, 0, 0);
                 __builtin_amdgcn_wave_barrier();
             }
         }
-        // 4. one scale per output (storage rows 16 b + 4 (lane / 16) + e)
+        // 4. one scale per output: D[2 b + p] row 4 g + e is storage index
+        //    32 b + 16 p + 4 g + e
 #pragma unroll
-        for (int b = 0; b < 16; ++b) {
-            const float4 s4 = *reinterpret_cast<const float4*>(&fw.sc[16 * b + 4 * (lane >> 4)]);
-            D[b].x *= s4.x; D[b].y *= s4.y; D[b].z *= s4.z; D[b].w *= s4.w;
+        for (int bp = 0; bp < 16; ++bp) {
+            const float4 s4 = *reinterpret_cast<const float4*>(&fw.sc[16 * bp + 4 * g]);
+            D[bp].x *= s4.x; D[bp].y *= s4.y; D[bp].z *= s4.z; D[bp].w *= s4.w;
         }
     }
 
-    // 5. wavefronts: 1..7 store their sums, wavefront 0 adds them in order
+    // 5. every wavefront's sums to LDS (lane-major: 16 bytes per lane and
+    //    D block); thread t adds entries 8 t .. 8 t + 7 over the wavefronts in
+    //    order: batch rows m0 = 2 t % 16 and m0 + 1, storage indices s0 .. s0 + 3
     __syncthreads();   // every wavefront is done with its own LDS rows
-    if (wave >= 1) {
 #pragma unroll
-        for (int b = 0; b < 16; ++b)
-            *reinterpret_cast<f4_t*>(&lds.red[wave - 1][(64 * b + lane) * 4]) = D[b];
-    }
+    for (int b = 0; b < 16; ++b)
+        *reinterpret_cast<f4_t*>(&lds.red[wave][(64 * b + lane) * 4]) = D[b];
     __syncthreads();
-    if (wave == 0) {
-        for (int w = 0; w < fm::kWaves - 1; ++w) {
-#pragma unroll
-            for (int b = 0; b < 16; ++b) {
-                const f4_t u = *reinterpret_cast<const f4_t*>(&lds.red[w][(64 * b + lane) * 4]);
-                D[b][0] += u[0]; D[b][1] += u[1]; D[b][2] += u[2]; D[b][3] += u[3];
-            }
-        }
-    }
-    __syncthreads();   // the stores above are read; lds.fin may overlap them
-    // the sums as [row][storage index]: D[b][e] of wavefront 0 is row lane % 16,
-    // storage 16 b + 4 (lane / 16) + e
-    if (wave == 0) {
-#pragma unroll
-        for (int b = 0; b < 16; ++b)
-            *reinterpret_cast<float4*>(&lds.fin[lane & 15][16 * b + 4 * (lane >> 4)]) =
-                make_float4(D[b].x, D[b].y, D[b].z, D[b].w);
-    }
-    __syncthreads();
-
-    // 6. thread t: row t / 32, storage 8 (t % 32) .. + 7
     const int t = threadIdx.x;
-    const int om = t >> 5, os = 8 * (t & 31);
-    float v[8];
-    {
-        const float4 u0 = *reinterpret_cast<const float4*>(&lds.fin[om][os]);
-        const float4 u1 = *reinterpret_cast<const float4*>(&lds.fin[om][os + 4]);
-        v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w; v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
-    }
-    auto store_y = [&](const float (&val)[8]) {
-        if (om >= a.M) return;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const size_t n = (size_t)vt * kVTile + fm_out_of(os + j);
-            if (a.out_f32) static_cast<float*>(a.y)[(size_t)om * a.ldy + n] = val[j];
-            else static_cast<_Float16*>(a.y)[(size_t)om * a.ldy + n] = (_Float16)val[j];
-        }
+    for (int w = 0; w < fm::kWaves; ++w) {
+        const float4 u0 = *reinterpret_cast<const float4*>(&lds.red[w][8 * t]);
+        const float4 u1 = *reinterpret_cast<const float4*>(&lds.red[w][8 * t + 4]);
+        v[0] += u0.x; v[1] += u0.y; v[2] += u0.z; v[3] += u0.w;
+        v[4] += u1.x; v[5] += u1.y; v[6] += u1.z; v[7] += u1.w;
+    }
+    const int l2 = (2 * t) & 63;
+    const int m0 = l2 & 15;
+    const int s0 = 16 * (t >> 5) + 4 * (l2 >> 4);
+    auto put_y = [&](int m, int s, float val) {
+        const size_t n = (size_t)vt * kVTile + fm_out_of(s);
+        if (a.out_f32) static_cast<float*>(a.y)[(size_t)m * a.ldy + n] = val;
+        else static_cast<_Float16*>(a.y)[(size_t)m * a.ldy + n] = (_Float16)val;
     };
-    if (S == 1) {
-        store_y(v);
+    if (S == 1) {  // one segment: these are the outputs
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (m0 < a.M) put_y(m0, s0 + j, v[j]);
+            if (m0 + 1 < a.M) put_y(m0 + 1, s0 + j, v[4 + j]);
+        }
         return;
     }
+
+    // 6. several segments: the workgroup's sums of the M rows go to slot seg
+    //    of the half tile ([row][storage index], device-coherent stores); the
+    //    last workgroup to count adds the slots in segment order
     const __amdgpu_buffer_rsrc_t prs =
         __builtin_amdgcn_make_buffer_rsrc(a.partials, (short)0, (int)a.partial_bytes, 0x00020000);
-    const uint32_t tile_base = (uint32_t)vt * a.slices * fm::kOutFloats * 4u;
-    const uint32_t my = ((uint32_t)om * kVTile + os) * 4u;
-    __builtin_amdgcn_raw_buffer_store_b128((u32x4){f2u(v[0]), f2u(v[1]), f2u(v[2]), f2u(v[3])}, prs,
-                                           tile_base + (uint32_t)seg * fm::kOutFloats * 4u + my, 0, kCacheSC1);
-    __builtin_amdgcn_raw_buffer_store_b128((u32x4){f2u(v[4]), f2u(v[5]), f2u(v[6]), f2u(v[7])}, prs,
-                                           tile_base + (uint32_t)seg * fm::kOutFloats * 4u + my + 16u, 0, kCacheSC1);
+    const uint32_t slot_bytes = (uint32_t)a.M * kVTile * 4u;
+    const uint32_t tile_base = (uint32_t)vt * a.slices * slot_bytes;
+    const uint32_t mine = tile_base + (uint32_t)seg * slot_bytes;
+    if (m0 < a.M)
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){f2u(v[0]), f2u(v[1]), f2u(v[2]), f2u(v[3])}, prs,
+                                               mine + ((uint32_t)m0 * kVTile + s0) * 4u, 0, kCacheSC1);
+    if (m0 + 1 < a.M)
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){f2u(v[4]), f2u(v[5]), f2u(v[6]), f2u(v[7])}, prs,
+                                               mine + ((uint32_t)(m0 + 1) * kVTile + s0) * 4u, 0, kCacheSC1);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's stores acknowledged
     __syncthreads();                // ... and every thread's, before the count
     if (t == 0) {
@@ -1721,27 +1750,34 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     }
     __syncthreads();
     if (last_flag == 0u) return;
+    acquire_slices();
 
-    // last to arrive: every segment's sums, in segment order, 16 segments in flight
-    float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int sb = 0; sb < S; sb += 16) {
-        u32x4 u[16][2];
+    // last to arrive: thread t adds row t / 32, storage 8 (t % 32) .. + 7 of
+    // every slot, in segment order, 16 slots in flight
+    const int om = t >> 5, os = 8 * (t & 31);
+    if (om < a.M) {
+        const uint32_t my = ((uint32_t)om * kVTile + os) * 4u;
+        float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int sb = 0; sb < S; sb += 16) {
+            u32x4 u[16][2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int sl = sb + i < S ? sb + i : sb;
-            const uint32_t off = tile_base + (uint32_t)sl * fm::kOutFloats * 4u + my;
-            u[i][0] = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, kCacheSC1);
-            u[i][1] = __builtin_amdgcn_raw_buffer_load_b128(prs, off + 16u, 0, kCacheSC1);
-        }
+            for (int i = 0; i < 16; ++i) {
+                const int sl = sb + i < S ? sb + i : sb;
+                const uint32_t off = tile_base + (uint32_t)sl * slot_bytes + my;
+                u[i][0] = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, 0);
+                u[i][1] = __builtin_amdgcn_raw_buffer_load_b128(prs, off + 16u, 0, 0);
+            }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (sb + i < S) {
-                tot[0] += u2f(u[i][0].x); tot[1] += u2f(u[i][0].y); tot[2] += u2f(u[i][0].z); tot[3] += u2f(u[i][0].w);
-                tot[4] += u2f(u[i][1].x); tot[5] += u2f(u[i][1].y); tot[6] += u2f(u[i][1].z); tot[7] += u2f(u[i][1].w);
+            for (int i = 0; i < 16; ++i) {
+                if (sb + i < S) {
+                    tot[0] += u2f(u[i][0].x); tot[1] += u2f(u[i][0].y); tot[2] += u2f(u[i][0].z); tot[3] += u2f(u[i][0].w);
+                    tot[4] += u2f(u[i][1].x); tot[5] += u2f(u[i][1].y); tot[6] += u2f(u[i][1].z); tot[7] += u2f(u[i][1].w);
+                }
             }
         }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) put_y(om, os + j, tot[j]);
     }
-    store_y(tot);
     if (t == 0) __hip_atomic_store(&a.counters[vt * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1823,13 +1859,13 @@ size_t ws_partial_bytes(const sgemv_desc* d, int mt) {
 }
 
 // Partial sums of the fused call with M rows: one or two rows use the
-// list-driven layout (slices_for stride), 3 to 16 rows 16 rows per 1024-column
-// segment.
+// list-driven layout (slices_for stride), 3 to 16 rows M x 256 sums per
+// 1024-column segment and half tile.
 size_t ws_fused_bytes(const sgemv_desc* d, int M) {
     if (M <= 2) return ws_partial_bytes(d, M);
     const int tiles = d->N / kVTile;
     const int segs = (d->K + fm::kSeg - 1) / fm::kSeg;
-    return segs > 1 ? (size_t)tiles * segs * fm::kOutFloats * sizeof(float) : 0;
+    return segs > 1 ? (size_t)tiles * segs * M * kVTile * sizeof(float) : 0;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
