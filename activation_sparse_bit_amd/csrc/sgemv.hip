@@ -68,7 +68,9 @@ struct RunArgs {
     Codes tc;
     int32_t* idx_out;        // fused kernel: list output (optional)
     int32_t* count_out;      // fused kernel: count output (optional)
-    int32_t segs;            // fused kernel: 512-column segments
+    int32_t segs;            // fused kernel: column segments
+    uint32_t all_cols;       // fused kernels: every column listed (dense), rows masked unless unmasked
+    uint32_t unmasked;       // fused kernels: activations used as they are (no thresholds)
 };
 
 __device__ __forceinline__ uint32_t code_of(const Codes& c, int m) {
@@ -1305,8 +1307,7 @@ __device__ __forceinline__ void fs_block(FsShared<MT>& fs, int wave, int lane, i
 }
 
 template <int MT>
-__global__ __launch_bounds__(FsCfg<MT>::W * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fs(RunArgs a) {
-    __shared__ FsLds<MT> lds;
+__device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT>& lds) {
     int bid = blockIdx.x;
     if (a.idx_out) {  // block 0 writes the list
         if (bid == 0) {
@@ -1357,10 +1358,11 @@ __global__ __launch_bounds__(FsCfg<MT>::W * 64) __attribute__((amdgpu_waves_per_
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const int mr = m < a.M ? m : a.M - 1;
-            const bool am = is_active(xr[h][m], code_of(a.tc, mr)) & has;
+            const bool am = (a.unmasked || is_active(xr[h][m], code_of(a.tc, mr))) & has;
             act[h] = act[h] | am;
             xm[h][m] = am ? xr[h][m] : 0u;
         }
+        if (a.all_cols) act[h] = has;
     }
     int nact = 0;
     uint32_t rank[H];
@@ -1400,6 +1402,22 @@ __global__ __launch_bounds__(FsCfg<MT>::W * 64) __attribute__((amdgpu_waves_per_
         default: break;
     }
     sp_finish<MT, FsCfg<MT>::W>(a, vt, seg, S, wave, lane, v4, lds.g.sh);
+}
+
+// Two builds of the same kernel: two wavefronts per SIMD (the whole register
+// budget, for grids of at most one workgroup per CU), and four (two
+// workgroups per CU, so that one's loads overlap the other's latency in
+// grids that take several rounds).
+template <int MT>
+__global__ __launch_bounds__(FsCfg<MT>::W * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fs(RunArgs a) {
+    __shared__ FsLds<MT> lds;
+    fs_body<MT>(a, lds);
+}
+
+template <int MT>
+__global__ __launch_bounds__(FsCfg<MT>::W * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_fs4(RunArgs a) {
+    __shared__ FsLds<MT> lds;
+    fs_body<MT>(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1526,6 +1544,7 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
             am |= (uint32_t)is_active(w4[e] >> 16, code) << (8 * i + 2 * e + 1);
         }
     }
+    if (a.unmasked) am = ~0u;
     am = row_ok ? am : 0u;
     // union over the 16 rows: lanes with the same quarter differ in lane bits
     // 2..5; rotations by 4 and 8 inside rows of 16 lanes, then the row swaps
@@ -1538,6 +1557,7 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
         const auto r32 = __builtin_amdgcn_permlane32_swap(un, un, false, false);
         un = r32[0] | r32[1];
     }
+    if (a.all_cols) un = has ? ~0u : 0u;
     uint32_t U[4], base[4];
     int nact = 0;
 #pragma unroll
@@ -1870,6 +1890,10 @@ size_t ws_fused_bytes(const sgemv_desc* d, int M) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Fused one/two-row kernel: grids of at most this many workgroups run in one
+// round (one per CU) with the two-wavefronts-per-SIMD build.
+constexpr int kFsOneRound = 256;
+
 template <int MT, bool DENSE, bool MASK>
 hipError_t launch_run(const RunArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)(a.tiles * a.slices));  // slices: see slices_for
@@ -1892,6 +1916,10 @@ hipError_t launch_mt(int mt, const RunArgs& a, hipStream_t s) {
     }
 }
 
+int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx, const float* thr,
+              int32_t* idx, int32_t* count, void* y, int ldy, uint32_t flags, void* ws, void* stream,
+              bool all_cols = false);
+
 int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx,
                const float* thr, const int32_t* idx, const int32_t* count, void* y, int ldy,
                uint32_t flags, void* ws, void* stream) {
@@ -1906,6 +1934,8 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
     if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16)) return SGEMV_EALIGN;
     if (idx && !aligned(idx, 16)) return SGEMV_EALIGN;
     if (count && !aligned(count, 4)) return SGEMV_EALIGN;
+    if (!idx)   // every column: the fused kernels with the whole list, which stream faster
+        return run_fused(d, packed, x, M, ldx, thr, nullptr, nullptr, y, ldy, flags, ws, stream, true);
 
     const int mt = pow2_ceil(M);
     RunArgs a;
@@ -1940,10 +1970,8 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    const bool dense = (idx == nullptr);
     const bool mask = (thr != nullptr);
-    if (dense) e = mask ? launch_mt<true, true>(mt, a, s) : launch_mt<true, false>(mt, a, s);
-    else e = mask ? launch_mt<false, true>(mt, a, s) : launch_mt<false, false>(mt, a, s);
+    e = mask ? launch_mt<false, true>(mt, a, s) : launch_mt<false, false>(mt, a, s);
     if (e != hipSuccess) {
         g_last_hip_error = (int)e;
         return SGEMV_EHIP;
@@ -1951,11 +1979,14 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
     return SGEMV_OK;
 }
 
+// The fused kernels; with all_cols every column is listed (the dense GEMV,
+// rows masked by their thresholds unless thr is NULL).
 int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx, const float* thr,
-              int32_t* idx, int32_t* count, void* y, int ldy, uint32_t flags, void* ws, void* stream) {
+              int32_t* idx, int32_t* count, void* y, int ldy, uint32_t flags, void* ws, void* stream,
+              bool all_cols) {
     int st = check_desc(d);
     if (st) return st;
-    if (!packed || !x || !y || !thr) return SGEMV_EINVAL;
+    if (!packed || !x || !y || (!thr && !all_cols)) return SGEMV_EINVAL;
     if ((idx == nullptr) != (count == nullptr)) return SGEMV_EINVAL;
     if (flags & ~SGEMV_OUT_F32) return SGEMV_EINVAL;
     if (M < 1 || M > SGEMV_MAX_BATCH) return SGEMV_ESIZE;
@@ -1966,8 +1997,12 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
 
     RunArgs a;
     std::memset(&a, 0, sizeof a);
-    st = fill_codes(thr, M, a.tc);
-    if (st) return st;
+    if (thr) {
+        st = fill_codes(thr, M, a.tc);
+        if (st) return st;
+    }
+    a.all_cols = all_cols ? 1u : 0u;
+    a.unmasked = thr ? 0u : 1u;
     a.tiles = d->N / kVTile;
     if (M <= 2) {
         a.slices = slices_for(d, M);   // stride of the partials region
@@ -1998,8 +2033,11 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     a.out_f32 = (flags & SGEMV_OUT_F32) ? 1u : 0u;
     const dim3 grid((unsigned)(a.tiles * a.segs + (idx ? 1 : 0)));  // + the list's workgroup
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (M == 1) hipLaunchKernelGGL((k_fs<1>), grid, dim3(FsCfg<1>::W * 64), 0, s, a);
-    else if (M == 2) hipLaunchKernelGGL((k_fs<2>), grid, dim3(FsCfg<2>::W * 64), 0, s, a);
+    const bool one_round = a.tiles * a.segs <= kFsOneRound;
+    if (M == 1 && one_round) hipLaunchKernelGGL((k_fs<1>), grid, dim3(FsCfg<1>::W * 64), 0, s, a);
+    else if (M == 1) hipLaunchKernelGGL((k_fs4<1>), grid, dim3(FsCfg<1>::W * 64), 0, s, a);
+    else if (M == 2 && one_round) hipLaunchKernelGGL((k_fs<2>), grid, dim3(FsCfg<2>::W * 64), 0, s, a);
+    else if (M == 2) hipLaunchKernelGGL((k_fs4<2>), grid, dim3(FsCfg<2>::W * 64), 0, s, a);
     else hipLaunchKernelGGL(k_fm, grid, dim3(fm::kWaves * 64), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {

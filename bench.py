@@ -4,8 +4,10 @@ Workload: the Llama-3-8B-shaped down projection, K = 14336 inputs ->
 N = 4096 outputs, int4 group-128 weights ~N(0, 0.02), activation
 x = silu(g) * u with g, u ~N(0, 1), magnitude-thresholded at 50 % (the
 step); 70 % and 90 %, the two-launch path (gather + run), the dense int4
-GEMV and the batched M = 1..16 union variant are measured beside it.
-Synthetic, seeded data.
+GEMV, the batched M = 1..16 union variant, the Llama-3-8B decode layer, a
+2048 x 2048 matrix and the Llama-3-70B MLP shapes (gate 8192 -> 28672, down
+28672 -> 8192 at 50 % and 90 %) are measured beside it.  Synthetic, seeded
+data.
 
 One step = one pass of the hot path on one activation vector: threshold,
 compact into the ascending list of active indices (written, with its
@@ -266,6 +268,43 @@ def main():
                 "each_projection_fused_us": sep_us, "two_launch_path_us": split_us,
                 "bytes": nbytes, "GBps": nbytes / (fused_us * 1e-6) / 1e9}
 
+    def measure_shape(K, N, sigma, j, kind, ps, steps, warmup):
+        """One matrix of another configuration: the fused step at each
+        sparsity (list written) and the dense int4 GEMV, with their
+        algorithmic bytes and the fraction of the HBM peak."""
+        qq, ss, zz = synth.quantized_weights(j, N, K, sigma)
+        dsc, bl = sgemv.sgemv_pack_layout(qq, ss, zz)
+        del qq, ss, zz
+        RR = max(2, -(-ROTATE_BYTES // dsc.total_bytes))
+        bd = torch.from_numpy(bl).to(dev)
+        cps = [bd] + [bd.clone() for _ in range(RR - 1)]
+        w = torch.zeros(max(sgemv.sgemv_workspace_bytes(dsc, 1), 256), dtype=torch.uint8, device=dev)
+        xv = synth.activation(kind, 0, K)
+        xdv = torch.from_numpy(xv).to(dev)
+        iv = torch.zeros(K, dtype=torch.int32, device=dev)
+        cv = torch.zeros(1, dtype=torch.int32, device=dev)
+        yv = torch.empty(N, dtype=torch.float16, device=dev)
+        res = {"K": K, "N": N, "weight_copies_rotated": RR}
+        for pp in ps:
+            t = synth.percentile_threshold(xv, pp)
+            us = graph_time([lambda i: sgemv.sgemv_run_fused(dsc, cps[i % RR], xdv, [t], yv, w, iv, cv)],
+                            steps, warmup)
+            A = int(cv.item())
+            Ag = touched_groups(iv[:A].cpu().numpy())
+            fb = fused_bytes(A, Ag, N, K)
+            res[f"fused_p{int(pp * 100)}"] = {"active": A, "groups_touched": Ag, "us_per_step": us, "bytes": fb,
+                                             "GBps": fb / (us * 1e-6) / 1e9,
+                                             "frac_hbm_peak": fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        dus = graph_time([lambda i: sgemv.sgemv_run(dsc, cps[i % RR], xdv, None, None, yv, w)], steps, warmup)
+        db = K * N // 2 + (K // 128) * N * 4 + K * 2 + N * 2
+        res["dense_int4"] = {"us_per_step": dus, "bytes": db, "GBps": db / (dus * 1e-6) / 1e9,
+                             "frac_hbm_peak": db / (dus * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        for pp in ps:
+            res[f"fused_p{int(pp * 100)}"]["speedup_vs_dense_int4"] = dus / res[f"fused_p{int(pp * 100)}"]["us_per_step"]
+        del cps, bd
+        torch.cuda.empty_cache()
+        return res
+
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -281,6 +320,7 @@ def main():
     sweep = {"fused_p50": main_res}
     batched = []
     layer = None
+    shapes = None
     if not args.quick:
         for p in (0.7, 0.9):
             sweep[f"fused_p{int(p * 100)}"] = measure_fused(p, args.steps, args.warmup)
@@ -294,6 +334,12 @@ def main():
         for M in (1, 2, 4, 8, 16):
             batched.append(measure_batched(M, max(20, args.steps // 4), max(5, args.warmup // 4)))
         layer = measure_layer(max(20, args.steps // 4), max(5, args.warmup // 4))
+        st, wu = max(20, args.steps // 2), max(5, args.warmup // 2)
+        shapes = {
+            "single_2048": measure_shape(2048, 2048, 0.02, 0, "plain", (0.5,), st, wu),
+            "mlp70b_gate_8192_28672": measure_shape(8192, 28672, 0.015, 0, "plain", (0.5, 0.9), st, wu),
+            "mlp70b_down_28672_8192": measure_shape(28672, 8192, 0.015, 2, "glu", (0.5, 0.9), st, wu),
+        }
 
     # ---------------- HBM traffic from committed counters ----------------
     traffic = None
@@ -346,6 +392,7 @@ def main():
         "sweep": sweep,
         "batched_p70": batched,
         "layer_8b_p50": layer,
+        "other_configs": shapes,
     }
     print(json.dumps(out))
 
