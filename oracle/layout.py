@@ -30,6 +30,22 @@ Blob = header (256 bytes) | weight region | metadata region, little-endian:
 
 for tiles t < N/tile_n, columns k < K, bytes j < tile_n/2, groups g < K/128
 and rows i < tile_n.  Padding bytes are zero.
+
+Version 2 (compact metadata) differs only in the metadata region.  The
+zero-points of this format are integers 0..15, so each one needs 4 bits: per
+(tile, group) the run holds the tile_n fp16 scales, then tile_n/2 bytes of
+zero-points, two per byte, even row in the low nibble:
+
+  m_bytes = (K/128)*N*5/2
+  scale        m_off + (t*(K/128) + g)*(5*tile_n/2) + 2i : fp16 bits of
+               s[t*tile_n + i][g]
+  zero-points  m_off + (t*(K/128) + g)*(5*tile_n/2) + 2*tile_n + j
+               = z[t*tile_n + 2j][g] | z[t*tile_n + 2j + 1][g] << 4
+
+It stores the same numbers in 2.5 instead of 4 bytes per row and group, so
+the metadata read per touched group shrinks by 37.5 %; the page's call for a
+layout that serves sparse reads applies to this region as much as to the
+weights.
 """
 from __future__ import annotations
 
@@ -41,17 +57,18 @@ GROUP = 128
 HEADER_BYTES = 256
 MAGIC = b"SGV1"
 VERSION = 1
+VERSION_Z4 = 2
 
 
 def _roundup(v: int, a: int) -> int:
     return (v + a - 1) // a * a
 
 
-def header_fields(N: int, K: int, tile_n: int) -> dict:
+def header_fields(N: int, K: int, tile_n: int, version: int = VERSION) -> dict:
     w_off = HEADER_BYTES
     w_bytes = N * K // 2
     m_off = w_off + _roundup(w_bytes, 256)
-    m_bytes = (K // GROUP) * N * 4
+    m_bytes = (K // GROUP) * N * 4 if version == VERSION else (K // GROUP) * N * 5 // 2
     total = m_off + _roundup(m_bytes, 256)
     return dict(N=N, K=K, group=GROUP, tile_n=tile_n, w_off=w_off,
                 w_bytes=w_bytes, m_off=m_off, m_bytes=m_bytes, total_bytes=total)
@@ -73,13 +90,25 @@ def _check(q, s_bits, z_bits, tile_n):
     return q, s_bits, z_bits, N, K
 
 
-def pack_spec(q, s_bits, z_bits, tile_n: int) -> np.ndarray:
+def zero_codes(z_bits) -> np.ndarray:
+    """Integer values 0..15 of fp16 zero-point bit patterns (raises on any
+    other value)."""
+    zf = np.asarray(z_bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+    if not np.all(np.isfinite(zf)) or np.any(zf != np.rint(zf)) or np.any(zf < 0) or np.any(zf > 15):
+        raise ValueError("zero-points must be integers 0..15")
+    return np.abs(zf).astype(np.uint8)
+
+
+def pack_spec(q, s_bits, z_bits, tile_n: int, version: int = VERSION) -> np.ndarray:
     """Return the blob (uint8 array) for codes ``q`` [N][K] and fp16 bit
-    patterns ``s_bits``, ``z_bits`` [N][K/128]."""
+    patterns ``s_bits``, ``z_bits`` [N][K/128]; version 1 (scale/zero pairs)
+    or 2 (scales, then 4-bit zero-points)."""
+    if version not in (VERSION, VERSION_Z4):
+        raise ValueError("unknown layout version")
     q, s_bits, z_bits, N, K = _check(q, s_bits, z_bits, tile_n)
-    h = header_fields(N, K, tile_n)
+    h = header_fields(N, K, tile_n, version)
     blob = np.zeros(h["total_bytes"], dtype=np.uint8)
-    head = (MAGIC + struct.pack("<I", VERSION)
+    head = (MAGIC + struct.pack("<I", version)
             + struct.pack("<iiii", N, K, GROUP, tile_n)
             + struct.pack("<QQQQQ", h["w_off"], h["w_bytes"], h["m_off"],
                           h["m_bytes"], h["total_bytes"]))
@@ -92,11 +121,20 @@ def pack_spec(q, s_bits, z_bits, tile_n: int) -> np.ndarray:
     blob[h["w_off"]:h["w_off"] + h["w_bytes"]] = byte.reshape(-1)
 
     Gk = K // GROUP
-    pair = np.empty((T, Gk, tile_n, 2), dtype=np.uint16)     # [t][g][i][s|z]
-    pair[..., 0] = s_bits.reshape(T, tile_n, Gk).transpose(0, 2, 1)
-    pair[..., 1] = z_bits.reshape(T, tile_n, Gk).transpose(0, 2, 1)
-    blob[h["m_off"]:h["m_off"] + h["m_bytes"]] = \
-        pair.astype("<u2").reshape(-1).view(np.uint8)
+    if version == VERSION:
+        pair = np.empty((T, Gk, tile_n, 2), dtype=np.uint16)     # [t][g][i][s|z]
+        pair[..., 0] = s_bits.reshape(T, tile_n, Gk).transpose(0, 2, 1)
+        pair[..., 1] = z_bits.reshape(T, tile_n, Gk).transpose(0, 2, 1)
+        blob[h["m_off"]:h["m_off"] + h["m_bytes"]] = \
+            pair.astype("<u2").reshape(-1).view(np.uint8)
+        return blob
+    zc = zero_codes(z_bits)
+    run = np.empty((T, Gk, 5 * tile_n // 2), dtype=np.uint8)   # [t][g][scales | zero bytes]
+    st = s_bits.reshape(T, tile_n, Gk).transpose(0, 2, 1)       # [t][g][i]
+    run[:, :, :2 * tile_n] = np.ascontiguousarray(st).astype("<u2").view(np.uint8).reshape(T, Gk, 2 * tile_n)
+    zt = zc.reshape(T, tile_n, Gk).transpose(0, 2, 1)           # [t][g][i]
+    run[:, :, 2 * tile_n:] = zt[:, :, 0::2] | (zt[:, :, 1::2] << 4)
+    blob[h["m_off"]:h["m_off"] + h["m_bytes"]] = run.reshape(-1)
     return blob
 
 
@@ -122,7 +160,17 @@ def unpack_spec(blob):
     qt[:, :, 0::2] = byte & 0x0F
     qt[:, :, 1::2] = byte >> 4
     q = qt.transpose(0, 2, 1).reshape(N, K)
-    pair = blob[h["m_off"]:h["m_off"] + h["m_bytes"]].view("<u2").reshape(T, Gk, tile_n, 2)
-    s_bits = pair[..., 0].transpose(0, 2, 1).reshape(N, Gk).astype(np.uint16)
-    z_bits = pair[..., 1].transpose(0, 2, 1).reshape(N, Gk).astype(np.uint16)
-    return np.ascontiguousarray(q), s_bits, z_bits, h
+    md = blob[h["m_off"]:h["m_off"] + h["m_bytes"]]
+    if h["version"] == VERSION:
+        pair = md.view("<u2").reshape(T, Gk, tile_n, 2)
+        s_bits = pair[..., 0].transpose(0, 2, 1).reshape(N, Gk).astype(np.uint16)
+        z_bits = pair[..., 1].transpose(0, 2, 1).reshape(N, Gk).astype(np.uint16)
+        return np.ascontiguousarray(q), s_bits, z_bits, h
+    run = md.reshape(T, Gk, 5 * tile_n // 2)
+    s_bits = np.ascontiguousarray(run[:, :, :2 * tile_n]).view("<u2").transpose(0, 2, 1).reshape(N, Gk)
+    zb = run[:, :, 2 * tile_n:]
+    zt = np.empty((T, Gk, tile_n), dtype=np.uint8)
+    zt[:, :, 0::2] = zb & 0x0F
+    zt[:, :, 1::2] = zb >> 4
+    z_bits = zt.transpose(0, 2, 1).reshape(N, Gk).astype(np.float16).view(np.uint16)
+    return np.ascontiguousarray(q), s_bits.astype(np.uint16), np.ascontiguousarray(z_bits), h

@@ -357,8 +357,57 @@ def pin_layout_golden(impl):
     assert hexat(4352, 16) == gd["metadata_bytes_at_m_off"].replace(" ", "")
 
 
+def pin_layout_z4_closed_form(impl):
+    """Version 2: same weight bytes as version 1; per (tile, group) the fp16
+    scales, then the integer zero-points two per byte (even row low)."""
+    for (N, K, Tn) in ((64, 128, 64), (256, 384, 128), (1024, 256, 512)):
+        n = np.arange(N)[:, None]
+        k = np.arange(K)[None, :]
+        q = ((n + 3 * k) % 16).astype(np.uint8)
+        Gk = K // 128
+        g = np.arange(Gk)[None, :]
+        s = ((0x3000 + 7 * n + 13 * g) & 0x7BFF).astype(np.uint16)
+        z = (((n + 5 * g) % 16)).astype(np.float16).view(np.uint16)
+        b2 = np.asarray(impl.pack_spec(q, s, z, Tn, 2))
+        b1 = np.asarray(impl.pack_spec(q, s, z, Tn))
+        h = impl.read_header(b2)
+        m_off = 256 + ((N * K // 2 + 255) // 256) * 256
+        assert h["version"] == 2 and h["m_off"] == m_off and h["m_bytes"] == Gk * N * 5 // 2
+        assert h["total_bytes"] == m_off + (Gk * N * 5 // 2 + 255) // 256 * 256 == len(b2)
+        assert np.array_equal(b2[256:m_off], b1[256:m_off])
+        run = 5 * Tn // 2
+        for t in range(N // Tn):
+            for gg in range(Gk):
+                base = m_off + (t * Gk + gg) * run
+                for i in (0, 1, Tn // 2, Tn - 1):
+                    nn = t * Tn + i
+                    assert int(b2[base + 2 * i]) | int(b2[base + 2 * i + 1]) << 8 == ((0x3000 + 7 * nn + 13 * gg) & 0x7BFF)
+                for j in (0, 1, Tn // 4, Tn // 2 - 1):
+                    nn = t * Tn + 2 * j
+                    assert b2[base + 2 * Tn + j] == ((nn + 5 * gg) % 16) | (((nn + 1 + 5 * gg) % 16) << 4)
+
+
+def pin_layout_z4_roundtrip(impl):
+    rng = np.random.default_rng(29)
+    for Tn in (64, 256, 1024):
+        N, K = 1024, 384
+        q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+        s = rng.integers(0, 0x7C00, size=(N, K // 128)).astype(np.uint16)
+        z = rng.integers(0, 16, size=(N, K // 128)).astype(np.float16).view(np.uint16)
+        q2, s2, z2, h = impl.unpack_spec(impl.pack_spec(q, s, z, Tn, 2))
+        assert h["version"] == 2
+        assert np.array_equal(q, q2) and np.array_equal(s, s2) and np.array_equal(z, z2)
+    bad = np.full((N, K // 128), np.float16(7.5).view(np.uint16), dtype=np.uint16)
+    try:
+        impl.pack_spec(q, s, bad, 512, 2)
+    except ValueError:
+        return
+    raise AssertionError("a zero-point that is not an integer 0..15 was packed in 4 bits")
+
+
 ALL_PINS = [pin_select_bruteforce, pin_select_golden, pin_gemv_exact_rational,
             pin_gemv_q_equals_z, pin_gemv_one_hot, pin_gemv_constant_group,
             pin_gemv_scale_equivariance, pin_gemv_matches_matrix_product,
             pin_batched_rows, pin_dequantize, pin_layout_closed_form,
-            pin_layout_roundtrip, pin_layout_golden]
+            pin_layout_roundtrip, pin_layout_golden, pin_layout_z4_closed_form,
+            pin_layout_z4_roundtrip]

@@ -33,6 +33,10 @@ MUTANTS = [
      "qt = q.reshape(tile_n, T, K).transpose(1, 2, 0)", "tile rows interleaved"),
     ("layout.py", "pair[..., 0] = s_bits", "pair[..., 0] = z_bits", "metadata order"),
     ("layout.py", "struct.pack(\"<iiii\", N, K, GROUP, tile_n)", "struct.pack(\"<iiii\", K, N, GROUP, tile_n)", "header N/K"),
+    ("layout.py", "run[:, :, 2 * tile_n:] = zt[:, :, 0::2] | (zt[:, :, 1::2] << 4)",
+     "run[:, :, 2 * tile_n:] = (zt[:, :, 0::2] << 4) | zt[:, :, 1::2]", "compact zero-point nibble order"),
+    ("layout.py", "zt = zc.reshape(T, tile_n, Gk).transpose(0, 2, 1)",
+     "zt = zc.reshape(T, Gk, tile_n)", "compact zero-points not transposed to [t][g][i]"),
 ]
 
 
