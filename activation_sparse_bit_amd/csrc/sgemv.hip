@@ -34,7 +34,8 @@
 
 #include "sgemv.h"
 
-extern "C" int sgemv_layout_fill_desc(int32_t N, int32_t K, int32_t tile_n, sgemv_desc* d);
+extern "C" int sgemv_layout_fill_desc(int32_t N, int32_t K, int32_t tile_n, uint32_t version,
+                                      sgemv_desc* d);
 
 namespace {
 
@@ -54,7 +55,8 @@ struct Codes {
 
 struct RunArgs {
     const uint8_t* w;        // weight region of the blob
-    const uint32_t* md;      // metadata region: one (s | z << 16) word per (tile, group, row)
+    const uint8_t* md;       // metadata region (layout version 1 or 2)
+    uint32_t md_z4;          // version 2: fp16 scales, then 4-bit zero-points
     const uint16_t* x;       // fp16 bits [M][ldx]
     const int32_t* idx;      // listed columns (unused when dense)
     const int32_t* count;    // number of listed columns (device)
@@ -266,6 +268,55 @@ __device__ __forceinline__ void acquire_slices() { __builtin_amdgcn_fence(__ATOM
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Scale/zero metadata of one half tile (256 outputs), in either version of
+// the layout: version 1 holds one (s, z) pair of fp16 bit patterns per output
+// and group (kTileN * 4 bytes per tile and group); version 2 holds the fp16
+// scales, then the integer zero-points as 4-bit codes, two per byte
+// (kTileN * 5 / 2 bytes).  md_words4 returns the version-1 words
+// (s bits | z bits << 16) of outputs o .. o + 3 (o a multiple of 4) either
+// way, so the kernels after it are the same for both.
+struct MdHalf {
+    const uint8_t* tile;   // the tile's metadata (group 0)
+    uint32_t h;            // which half of the tile
+    uint32_t z4;           // version 2
+};
+
+// The version is a template parameter of every kernel: the handle's z4 is
+// then a constant, and the branches below fold away after inlining.
+template <bool Z4>
+__device__ __forceinline__ MdHalf md_half(const RunArgs& a, int t, int h) {
+    const size_t run = Z4 ? (size_t)kTileN * 5 / 2 : (size_t)kTileN * 4;   // bytes per group
+    return MdHalf{a.md + (size_t)t * (a.K / kGroup) * run, (uint32_t)h, Z4 ? 1u : 0u};
+}
+
+// The loads (md_raw4: version-1 words, or (four scales, four zero codes, 0)
+// for version 2) and the conversion (md_cook4) are separate, so that a
+// kernel can issue the loads early and convert where it uses the values.
+__device__ __forceinline__ u32x4 md_raw4(const MdHalf& m, int g, int o) {
+    if (!m.z4)
+        return *reinterpret_cast<const u32x4*>(m.tile + ((size_t)g * (2 * kVTile) + m.h * kVTile + o) * 4);
+    const uint8_t* run = m.tile + (size_t)g * (kTileN * 5 / 2);
+    const int i = (int)m.h * kVTile + o;                 // row within the tile
+    const uint2 sv = *reinterpret_cast<const uint2*>(run + 2 * i);
+    const uint32_t zv = *reinterpret_cast<const uint16_t*>(run + 2 * kTileN + i / 2);
+    return (u32x4){sv.x, sv.y, zv, 0u};
+}
+
+__device__ __forceinline__ u32x4 md_cook4(const u32x4& r, uint32_t z4) {
+    if (!z4) return r;
+    // zero-point z (0..15) as fp16: (1024 + z) - 1024, exactly, two per word
+    const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    const uint32_t zv = r.z;
+    const uint32_t za = __builtin_bit_cast(
+        uint32_t, as_h2(0x64006400u | (zv & 0xFu) | ((zv & 0xF0u) << 12)) - k1024);
+    const uint32_t zb = __builtin_bit_cast(
+        uint32_t, as_h2(0x64006400u | ((zv >> 8) & 0xFu) | ((zv & 0xF000u) << 4)) - k1024);
+    return (u32x4){(r.x & 0xFFFFu) | (za << 16), (r.x >> 16) | (za & 0xFFFF0000u),
+                   (r.y & 0xFFFFu) | (zb << 16), (r.y >> 16) | (zb & 0xFFFF0000u)};
+}
+
+__device__ __forceinline__ u32x4 md_words4(const MdHalf& m, int g, int o) { return md_cook4(md_raw4(m, g, o), m.z4); }
+
 // Wavefronts per workgroup: two per SIMD for few rows; four in all for
 // many rows, whose accumulators fill the register file.
 template <int MT>
@@ -274,8 +325,8 @@ struct Waves {
 };
 
 // Scale/zero words of this lane's 4 outputs for one group.
-__device__ __forceinline__ void load_md4(const uint32_t* __restrict__ grp, int lane, uint32_t (&md)[4]) {
-    const uint4 v = reinterpret_cast<const uint4*>(grp)[lane];
+__device__ __forceinline__ void load_md4(const MdHalf& mh, int g, int lane, uint32_t (&md)[4]) {
+    const u32x4 v = md_words4(mh, g, 4 * lane);
     md[0] = v.x; md[1] = v.y; md[2] = v.z; md[3] = v.w;
 }
 
@@ -301,7 +352,7 @@ struct Chunk {
 
 struct WaveCtx {
     const uint8_t* wcol;      // weights of this half tile: column k at + k * 256
-    const uint32_t* mdh;      // metadata of this half tile: group g at + g * 512 words
+    MdHalf mdh;               // metadata of this half tile
     int lane, K, p1;          // the wavefront's list positions end at p1
     uint32_t vmagic;          // 0x64006400 (two fp16 1024.0) held in a VGPR
 };
@@ -364,8 +415,8 @@ __device__ __forceinline__ void data_load(const RunArgs& a, const WaveCtx& wc, i
         ch.w[i] = __builtin_nontemporal_load(col + wc.lane);
     }
     const int g1 = ch.gA + 1 <= ch.gZ ? ch.gA + 1 : ch.gZ;
-    load_md4(wc.mdh + (size_t)ch.gA * (2 * kVTile), wc.lane, ch.md0);
-    load_md4(wc.mdh + (size_t)g1 * (2 * kVTile), wc.lane, ch.md1);
+    load_md4(wc.mdh, ch.gA, wc.lane, ch.md0);
+    load_md4(wc.mdh, g1, wc.lane, ch.md1);
     // x: one vector load per staged row; lane L fetches column L % 16,
     // whose index it already holds
     const int c = wc.lane & (kChunk - 1);
@@ -468,7 +519,7 @@ __device__ __forceinline__ void chunk_compute(float (&y)[MT][4], const RunArgs& 
         if (pos == 0) continue;
         uint32_t md[4];
         if (d == 2) {
-            load_md4(wc.mdh + (size_t)(ch.gA + 2) * (2 * kVTile), wc.lane, md);
+            load_md4(wc.mdh, ch.gA + 2, wc.lane, md);
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) md[r] = d ? ch.md1[r] : ch.md0[r];
@@ -497,7 +548,7 @@ __device__ __forceinline__ void chunk_compute(float (&y)[MT][4], const RunArgs& 
             pos &= (1u << ch.nv) - 1u;
             if (pos != 0) {
                 uint32_t md[4];
-                load_md4(wc.mdh + (size_t)g * (2 * kVTile), wc.lane, md);
+                load_md4(wc.mdh, g, wc.lane, md);
                 uint32_t pm[kChunk / 2];
                 pair_masks(pos, pm);
                 chunk_pass(y, ch, md, pm, xs, wc.vmagic);
@@ -551,7 +602,7 @@ __device__ __forceinline__ void wg_tree(float (&v)[MT][4], float (*red)[MT][kVTi
     }
 }
 
-template <int MT, bool DENSE, bool MASK>
+template <int MT, bool DENSE, bool MASK, bool Z4>
 __global__ __launch_bounds__(Waves<MT>::kN * 64) void k_run(RunArgs a) {
     constexpr int kWaves = Waves<MT>::kN;
     __shared__ float red[kWaves / 2][MT][kVTile];
@@ -602,7 +653,7 @@ __global__ __launch_bounds__(Waves<MT>::kN * 64) void k_run(RunArgs a) {
         const int t = vt >> 1, h = vt & 1;
         WaveCtx wc;
         wc.wcol = a.w + (size_t)t * K * (2 * kHalfRun) + h * kHalfRun;
-        wc.mdh = a.md + (size_t)t * Gk * (2 * kVTile) + h * kVTile;
+        wc.mdh = md_half<Z4>(a, t, h);
         wc.lane = lane;
         wc.K = K;
         wc.p1 = wc1 * kChunk < count ? wc1 * kChunk : count;
@@ -783,7 +834,7 @@ __device__ __forceinline__ uint32_t sp_zc(uint32_t sz_word, int odd) {
 
 // Pairs (1024 + z | s) of 8 outputs 8d .. 8d + 7 of the lane's block for
 // group g: from the rows gF .. gF + gcap - 1 staged in LDS, else from HBM.
-__device__ __forceinline__ void sp_md8(const uint32_t (*s_md)[kVTile], int gcap, const uint32_t* mdh, int gF,
+__device__ __forceinline__ void sp_md8(const uint32_t (*s_md)[kVTile], int gcap, const MdHalf& mdh, int gF,
                                        int staged, int g, int blk, int d, uint32_t (&md)[8]) {
     if (staged) {
         int gi = g - gF;  // a list that is not ascending gives wrong results, never a stray access
@@ -793,8 +844,7 @@ __device__ __forceinline__ void sp_md8(const uint32_t (*s_md)[kVTile], int gcap,
         md[0] = u.x; md[1] = u.y; md[2] = u.z; md[3] = u.w;
         md[4] = v.x; md[5] = v.y; md[6] = v.z; md[7] = v.w;
     } else {
-        const u32x4* src = reinterpret_cast<const u32x4*>(mdh + (size_t)g * (2 * kVTile) + blk * sp::kOut + 8 * d);
-        const u32x4 u = src[0], v = src[1];
+        const u32x4 u = md_words4(mdh, g, blk * sp::kOut + 8 * d), v = md_words4(mdh, g, blk * sp::kOut + 8 * d + 4);
         const uint32_t raw[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int r = 0; r < 8; ++r) md[r] = sp_zc(raw[r], r & 1);
@@ -808,29 +858,26 @@ __device__ __forceinline__ void sp_md8(const uint32_t (*s_md)[kVTile], int gcap,
 struct SpMdRaw {
     u32x4 v[2];
 };
-__device__ __forceinline__ void sp_md_issue(const uint32_t* mdh, int gF, int ng, SpMdRaw& r) {
+__device__ __forceinline__ void sp_md_issue(const MdHalf& mdh, int gF, int ng, SpMdRaw& r) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int e = threadIdx.x + i * sp::kThreads;
-        if (e < ng * (kVTile / 4))
-            r.v[i] = *reinterpret_cast<const u32x4*>(mdh + (size_t)(gF + e / (kVTile / 4)) * (2 * kVTile) +
-                                                     4 * (e % (kVTile / 4)));
+        if (e < ng * (kVTile / 4)) r.v[i] = md_raw4(mdh, gF + e / (kVTile / 4), 4 * (e % (kVTile / 4)));
     }
 }
 __device__ __forceinline__ void sp_md_put(uint32_t (*s_md)[kVTile], int e, u32x4 raw) {
     *reinterpret_cast<u32x4*>(&s_md[e / (kVTile / 4)][4 * (e % (kVTile / 4))]) =
         (u32x4){sp_zc(raw.x, 0), sp_zc(raw.y, 1), sp_zc(raw.z, 0), sp_zc(raw.w, 1)};
 }
-__device__ __forceinline__ void sp_md_store(uint32_t (*s_md)[kVTile], const uint32_t* mdh, int gF, int ng,
+__device__ __forceinline__ void sp_md_store(uint32_t (*s_md)[kVTile], const MdHalf& mdh, int gF, int ng,
                                             const SpMdRaw& r) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int e = threadIdx.x + i * sp::kThreads;
-        if (e < ng * (kVTile / 4)) sp_md_put(s_md, e, r.v[i]);
+        if (e < ng * (kVTile / 4)) sp_md_put(s_md, e, md_cook4(r.v[i], mdh.z4));
     }
     for (int e = threadIdx.x + 2 * sp::kThreads; e < ng * (kVTile / 4); e += sp::kThreads)
-        sp_md_put(s_md, e, *reinterpret_cast<const u32x4*>(mdh + (size_t)(gF + e / (kVTile / 4)) * (2 * kVTile) +
-                                                          4 * (e % (kVTile / 4))));
+        sp_md_put(s_md, e, md_words4(mdh, gF + e / (kVTile / 4), 4 * (e % (kVTile / 4))));
 }
 
 // One chunk of a wavefront: lane (slot, blk) holds listed columns kk[0..3]
@@ -841,7 +888,7 @@ __device__ __forceinline__ void sp_md_store(uint32_t (*s_md)[kVTile], const uint
 template <int MT>
 __device__ __forceinline__ void sp_chunk(const u32x4 (&w)[4], const uint32_t (&xw)[MT][4], const int (&kk)[4],
                                          uint32_t valid, const uint32_t (*s_md)[kVTile], int gcap,
-                                         const uint32_t* mdh, int gF, int staged, int blk, int lane,
+                                         const MdHalf& mdh, int gF, int staged, int blk, int lane,
                                          float (&v4)[MT][4]) {
     const uint32_t vmagic = 0x64006400u | __builtin_amdgcn_mbcnt_lo(0u, 0u);  // per-lane (VGPR) copy
 #pragma unroll
@@ -1015,7 +1062,7 @@ __device__ __forceinline__ void sp_finish(const RunArgs& a, int vt, int slice, i
 
 // List-driven kernel: the list positions of the workgroup are
 // slice * 256 .. slice * 256 + 255 (one chunk per wavefront).
-template <int MT, bool DENSE, bool MASK>
+template <int MT, bool DENSE, bool MASK, bool Z4>
 __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_sp(RunArgs a) {
     __shared__ uint32_t s_md[sp::kGCap][kVTile];
     __shared__ SpShared<MT, sp::kWaves> sh;
@@ -1060,7 +1107,7 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
 
     const int tt = vt >> 1, hh = vt & 1;
     const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
-    const uint32_t* __restrict__ mdh = a.md + (size_t)tt * Gk * (2 * kVTile) + hh * kVTile;
+    const MdHalf mdh = md_half<Z4>(a, tt, hh);
 
     // groups of the workgroup's first and last position
     int gF, gL;
@@ -1208,7 +1255,7 @@ __device__ __forceinline__ void fs_pair8(uint32_t Ad, uint32_t Bd, const uint32_
 template <int MT, int NP>
 __device__ __forceinline__ void fs_block(FsShared<MT>& fs, int wave, int lane, int slot, int blk, int nact,
                                          int K, const uint8_t* __restrict__ wcol, const u32x4& mdv,
-                                         float (&v4)[MT][4]) {
+                                         uint32_t z4, float (&v4)[MT][4]) {
     const int kfirst = fs.k[wave][0];
     int kk[2 * NP];
     uint32_t xp[NP][MT];
@@ -1235,7 +1282,8 @@ __device__ __forceinline__ void fs_block(FsShared<MT>& fs, int wave, int lane, i
         // the group row: lane l holds outputs 4l .. 4l + 3; zero codes as two
         // (even, odd) pairs, scales at the lane and sum that will own them
         // after the slot sums
-        const half2_t s01 = as_h2(mdv.x), s11 = as_h2(mdv.y), s21 = as_h2(mdv.z), s31 = as_h2(mdv.w);
+        const u32x4 mw = md_cook4(mdv, z4);
+        const half2_t s01 = as_h2(mw.x), s11 = as_h2(mw.y), s21 = as_h2(mw.z), s31 = as_h2(mw.w);
         const half2_t zp0 = (half2_t){(_Float16)(s01.y + (_Float16)1024.0f),
                                       (_Float16)(s11.y * (_Float16)16.0f + (_Float16)1024.0f)};
         const half2_t zp1 = (half2_t){(_Float16)(s21.y + (_Float16)1024.0f),
@@ -1306,7 +1354,7 @@ __device__ __forceinline__ void fs_block(FsShared<MT>& fs, int wave, int lane, i
     }
 }
 
-template <int MT>
+template <int MT, bool Z4>
 __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT>& lds) {
     int bid = blockIdx.x;
     if (a.idx_out) {  // block 0 writes the list
@@ -1334,7 +1382,7 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT>& lds) {
 
     const int tt = vt >> 1, hh = vt & 1;
     const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
-    const uint32_t* __restrict__ mdh = a.md + (size_t)tt * Gk * (2 * kVTile) + hh * kVTile;
+    const MdHalf mdh = md_half<Z4>(a, tt, hh);
 
     // 1. activations (two per lane and row; a wavefront past K reads its
     //    first columns and ignores them, so the loads are unconditional)
@@ -1376,7 +1424,7 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT>& lds) {
     // the group's scale/zero row (16 bytes per lane), only with work to do;
     // converted after the weight loads are issued
     u32x4 mdv = {0u, 0u, 0u, 0u};
-    if (np > 0) mdv = *reinterpret_cast<const u32x4*>(mdh + (size_t)g * (2 * kVTile) + 4 * lane);
+    if (np > 0) mdv = md_raw4(mdh, g, 4 * lane);
 #pragma unroll
     for (int h = 0; h < H; ++h) {
         if (act[h]) {
@@ -1391,14 +1439,14 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT>& lds) {
     //      pair waits only for its own loads)
     float v4[MT][4] = {};
     switch (np) {
-        case 1: fs_block<MT, 1>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
-        case 2: fs_block<MT, 2>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
-        case 3: fs_block<MT, 3>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
-        case 4: fs_block<MT, 4>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
-        case 5: fs_block<MT, 5>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
-        case 6: fs_block<MT, 6>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
-        case 7: fs_block<MT, 7>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
-        case 8: fs_block<MT, 8>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, v4); break;
+        case 1: fs_block<MT, 1>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 2: fs_block<MT, 2>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 3: fs_block<MT, 3>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 4: fs_block<MT, 4>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 5: fs_block<MT, 5>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 6: fs_block<MT, 6>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 7: fs_block<MT, 7>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 8: fs_block<MT, 8>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
         default: break;
     }
     sp_finish<MT, FsCfg<MT>::W>(a, vt, seg, S, wave, lane, v4, lds.g.sh);
@@ -1408,16 +1456,16 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT>& lds) {
 // budget, for grids of at most one workgroup per CU), and four (two
 // workgroups per CU, so that one's loads overlap the other's latency in
 // grids that take several rounds).
-template <int MT>
+template <int MT, bool Z4>
 __global__ __launch_bounds__(FsCfg<MT>::W * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fs(RunArgs a) {
     __shared__ FsLds<MT> lds;
-    fs_body<MT>(a, lds);
+    fs_body<MT, Z4>(a, lds);
 }
 
-template <int MT>
+template <int MT, bool Z4>
 __global__ __launch_bounds__(FsCfg<MT>::W * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_fs4(RunArgs a) {
     __shared__ FsLds<MT> lds;
-    fs_body<MT>(a, lds);
+    fs_body<MT, Z4>(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1492,6 +1540,7 @@ union FmLds {
 };
 
 
+template <bool Z4>
 __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fm(RunArgs a) {
     __shared__ FmLds lds;
     __shared__ uint32_t last_flag;
@@ -1518,7 +1567,7 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
 
     const int tt = vt >> 1, hh = vt & 1;
     const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
-    const uint32_t* __restrict__ mdh = a.md + (size_t)tt * Gk * (2 * kVTile) + hh * kVTile;
+    const MdHalf mdh = md_half<Z4>(a, tt, hh);
 
     // 1. activations: lane (row xm = lane / 4, quarter xq = lane % 4) loads
     //    32 columns; rows past M read row M - 1 and are masked out
@@ -1528,7 +1577,7 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         xv[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)xmr * a.ldx + (has ? kw : 0) + 32 * xq + 8 * i);
-    const u32x4 mdv = *reinterpret_cast<const u32x4*>(mdh + (size_t)g * (2 * kVTile) + 4 * lane);
+    const u32x4 mdv = md_raw4(mdh, g, 4 * lane);   // converted where it is used
 
     const uint32_t code = code_of(a.tc, xmr);
     const bool row_ok = has && xm < a.M;
@@ -1592,7 +1641,8 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     // 2c. zero codes of the weight bytes 2 lane, 2 lane + 1 (outputs 4 lane ..
     //     4 lane + 3) and their scales in storage order
     {
-        const uint32_t mw[4] = {mdv.x, mdv.y, mdv.z, mdv.w};
+        const u32x4 mc = md_cook4(mdv, mdh.z4);
+        const uint32_t mw[4] = {mc.x, mc.y, mc.z, mc.w};
         uint32_t zpair[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -1860,7 +1910,8 @@ int check_desc(const sgemv_desc* d) {
     if (d->tile_n < 64 || d->tile_n > 1024 || (d->tile_n & (d->tile_n - 1)) || d->N % d->tile_n)
         return SGEMV_ESIZE;
     sgemv_desc ref;
-    sgemv_layout_fill_desc(d->N, d->K, d->tile_n, &ref);
+    if (d->version != SGEMV_LAYOUT_PAIRS && d->version != SGEMV_LAYOUT_Z4) return SGEMV_EINVAL;
+    sgemv_layout_fill_desc(d->N, d->K, d->tile_n, d->version, &ref);
     if (d->w_off != ref.w_off || d->w_bytes != ref.w_bytes || d->m_off != ref.m_off ||
         d->m_bytes != ref.m_bytes || d->total_bytes != ref.total_bytes)
         return SGEMV_EINVAL;
@@ -1894,25 +1945,25 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // round (one per CU) with the two-wavefronts-per-SIMD build.
 constexpr int kFsOneRound = 256;
 
-template <int MT, bool DENSE, bool MASK>
+template <int MT, bool DENSE, bool MASK, bool Z4>
 hipError_t launch_run(const RunArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)(a.tiles * a.slices));  // slices: see slices_for
     if (MT <= 2) {
-        hipLaunchKernelGGL((k_sp<(MT <= 2 ? MT : 1), DENSE, MASK>), grid, dim3(sp::kWaves * 64), 0, s, a);
+        hipLaunchKernelGGL((k_sp<(MT <= 2 ? MT : 1), DENSE, MASK, Z4>), grid, dim3(sp::kWaves * 64), 0, s, a);
     } else {
-        hipLaunchKernelGGL((k_run<MT, DENSE, MASK>), grid, dim3(Waves<MT>::kN * 64), 0, s, a);
+        hipLaunchKernelGGL((k_run<MT, DENSE, MASK, Z4>), grid, dim3(Waves<MT>::kN * 64), 0, s, a);
     }
     return hipGetLastError();
 }
 
-template <bool DENSE, bool MASK>
+template <bool DENSE, bool MASK, bool Z4>
 hipError_t launch_mt(int mt, const RunArgs& a, hipStream_t s) {
     switch (mt) {
-        case 1: return launch_run<1, DENSE, MASK>(a, s);
-        case 2: return launch_run<2, DENSE, MASK>(a, s);
-        case 4: return launch_run<4, DENSE, MASK>(a, s);
-        case 8: return launch_run<8, DENSE, MASK>(a, s);
-        default: return launch_run<16, DENSE, MASK>(a, s);
+        case 1: return launch_run<1, DENSE, MASK, Z4>(a, s);
+        case 2: return launch_run<2, DENSE, MASK, Z4>(a, s);
+        case 4: return launch_run<4, DENSE, MASK, Z4>(a, s);
+        case 8: return launch_run<8, DENSE, MASK, Z4>(a, s);
+        default: return launch_run<16, DENSE, MASK, Z4>(a, s);
     }
 }
 
@@ -1953,7 +2004,8 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
     }
     const uint8_t* blob = static_cast<const uint8_t*>(packed);
     a.w = blob + d->w_off;
-    a.md = reinterpret_cast<const uint32_t*>(blob + d->m_off);
+    a.md = blob + d->m_off;
+    a.md_z4 = d->version == SGEMV_LAYOUT_Z4 ? 1u : 0u;
     a.x = static_cast<const uint16_t*>(x);
     a.idx = idx;
     a.count = count;
@@ -1971,7 +2023,8 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     const bool mask = (thr != nullptr);
-    e = mask ? launch_mt<false, true>(mt, a, s) : launch_mt<false, false>(mt, a, s);
+    if (a.md_z4) e = mask ? launch_mt<false, true, true>(mt, a, s) : launch_mt<false, false, true>(mt, a, s);
+    else e = mask ? launch_mt<false, true, false>(mt, a, s) : launch_mt<false, false, false>(mt, a, s);
     if (e != hipSuccess) {
         g_last_hip_error = (int)e;
         return SGEMV_EHIP;
@@ -1981,6 +2034,15 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
 
 // The fused kernels; with all_cols every column is listed (the dense GEMV,
 // rows masked by their thresholds unless thr is NULL).
+template <bool Z4>
+void launch_fused(int M, bool one_round, dim3 grid, const RunArgs& a, hipStream_t s) {
+    if (M == 1 && one_round) hipLaunchKernelGGL((k_fs<1, Z4>), grid, dim3(FsCfg<1>::W * 64), 0, s, a);
+    else if (M == 1) hipLaunchKernelGGL((k_fs4<1, Z4>), grid, dim3(FsCfg<1>::W * 64), 0, s, a);
+    else if (M == 2 && one_round) hipLaunchKernelGGL((k_fs<2, Z4>), grid, dim3(FsCfg<2>::W * 64), 0, s, a);
+    else if (M == 2) hipLaunchKernelGGL((k_fs4<2, Z4>), grid, dim3(FsCfg<2>::W * 64), 0, s, a);
+    else hipLaunchKernelGGL(k_fm<Z4>, grid, dim3(fm::kWaves * 64), 0, s, a);
+}
+
 int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx, const float* thr,
               int32_t* idx, int32_t* count, void* y, int ldy, uint32_t flags, void* ws, void* stream,
               bool all_cols) {
@@ -2018,7 +2080,8 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     }
     const uint8_t* blob = static_cast<const uint8_t*>(packed);
     a.w = blob + d->w_off;
-    a.md = reinterpret_cast<const uint32_t*>(blob + d->m_off);
+    a.md = blob + d->m_off;
+    a.md_z4 = d->version == SGEMV_LAYOUT_Z4 ? 1u : 0u;
     a.x = static_cast<const uint16_t*>(x);
     a.y = y;
     a.idx_out = idx;
@@ -2034,11 +2097,8 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     const dim3 grid((unsigned)(a.tiles * a.segs + (idx ? 1 : 0)));  // + the list's workgroup
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool one_round = a.tiles * a.segs <= kFsOneRound;
-    if (M == 1 && one_round) hipLaunchKernelGGL((k_fs<1>), grid, dim3(FsCfg<1>::W * 64), 0, s, a);
-    else if (M == 1) hipLaunchKernelGGL((k_fs4<1>), grid, dim3(FsCfg<1>::W * 64), 0, s, a);
-    else if (M == 2 && one_round) hipLaunchKernelGGL((k_fs<2>), grid, dim3(FsCfg<2>::W * 64), 0, s, a);
-    else if (M == 2) hipLaunchKernelGGL((k_fs4<2>), grid, dim3(FsCfg<2>::W * 64), 0, s, a);
-    else hipLaunchKernelGGL(k_fm, grid, dim3(fm::kWaves * 64), 0, s, a);
+    if (a.md_z4) launch_fused<true>(M, one_round, grid, a, s);
+    else launch_fused<false>(M, one_round, grid, a, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         g_last_hip_error = (int)e;

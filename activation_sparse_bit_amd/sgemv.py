@@ -24,9 +24,11 @@ SGEMV_EHIP = -5
 SGEMV_OUT_F32 = 1
 SGEMV_GROUP = 128
 SGEMV_TILE_N = 512
+SGEMV_LAYOUT_PAIRS = 1    # layout version 1: (s, z) fp16 pairs
+SGEMV_LAYOUT_Z4 = 2       # layout version 2: fp16 scales, 4-bit zero-points
 SGEMV_MAX_BATCH = 16
 
-EXPORTED = ["sgemv_pack_layout", "sgemv_desc_from_header", "sgemv_gather_indices",
+EXPORTED = ["sgemv_pack_layout", "sgemv_pack_layout_z4", "sgemv_desc_from_header", "sgemv_gather_indices",
             "sgemv_run", "sgemv_run_batched", "sgemv_run_fused", "sgemv_workspace_bytes",
             "sgemv_strerror", "sgemv_last_hip_error"]
 
@@ -41,7 +43,8 @@ class Desc(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int32), ("K", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("w_off", ctypes.c_uint64),
                 ("w_bytes", ctypes.c_uint64), ("m_off", ctypes.c_uint64),
-                ("m_bytes", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64)]
+                ("m_bytes", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
+                ("version", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -63,6 +66,8 @@ def lib():
     pd = ctypes.POINTER(Desc)
     L.sgemv_pack_layout.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, sz, pd]
     L.sgemv_pack_layout.restype = ctypes.c_int
+    L.sgemv_pack_layout_z4.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, sz, pd]
+    L.sgemv_pack_layout_z4.restype = ctypes.c_int
     L.sgemv_desc_from_header.argtypes = [vp, sz, pd]
     L.sgemv_desc_from_header.restype = ctypes.c_int
     L.sgemv_gather_indices.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
@@ -124,7 +129,7 @@ def _thresholds(t, M):
 # ---------------------------------------------------------------------------
 # the device and host calls
 # ---------------------------------------------------------------------------
-def sgemv_pack_layout(q, scales_f16, zeros_f16, tile_n: int = SGEMV_TILE_N):
+def sgemv_pack_layout(q, scales_f16, zeros_f16, tile_n: int = SGEMV_TILE_N, _which: str = "sgemv_pack_layout"):
     """Pack int4 codes q (uint8 [N][K]) and fp16 bit patterns of scales and
     zero-points (uint16 [N][K/128]) into a blob.  Returns (Desc, uint8 blob)."""
     q = np.ascontiguousarray(q, dtype=np.uint8)
@@ -140,13 +145,18 @@ def sgemv_pack_layout(q, scales_f16, zeros_f16, tile_n: int = SGEMV_TILE_N):
     if s.shape != (N, K // SGEMV_GROUP) or z.shape != (N, K // SGEMV_GROUP):
         raise ValueError("scales/zeros must be [N][K/128]")
     d = Desc()
-    _check(lib().sgemv_pack_layout(None, None, None, N, K, SGEMV_GROUP, tile_n, None, 0,
-                                   ctypes.byref(d)), "sgemv_pack_layout(size)")
+    fn = getattr(lib(), _which)
+    _check(fn(None, None, None, N, K, SGEMV_GROUP, tile_n, None, 0, ctypes.byref(d)), f"{_which}(size)")
     blob = np.empty(d.total_bytes, dtype=np.uint8)
-    _check(lib().sgemv_pack_layout(_ptr(q), _ptr(s), _ptr(z), N, K, SGEMV_GROUP, tile_n,
-                                   _ptr(blob), blob.nbytes, ctypes.byref(d)),
-           "sgemv_pack_layout")
+    _check(fn(_ptr(q), _ptr(s), _ptr(z), N, K, SGEMV_GROUP, tile_n, _ptr(blob), blob.nbytes, ctypes.byref(d)),
+           _which)
     return d, blob
+
+
+def sgemv_pack_layout_z4(q, scales_f16, zeros_f16, tile_n: int = SGEMV_TILE_N):
+    """As sgemv_pack_layout, with the compact metadata of layout version 2
+    (fp16 scales, then the integer zero-points in 4 bits)."""
+    return sgemv_pack_layout(q, scales_f16, zeros_f16, tile_n, _which="sgemv_pack_layout_z4")
 
 
 def sgemv_desc_from_header(blob) -> Desc:
@@ -220,9 +230,11 @@ def sgemv_last_hip_error() -> int:
 class PackedMatrix:
     """A packed matrix on the device with its workspace (torch tensors)."""
 
-    def __init__(self, q, scales_f16, zeros_f16, device="cuda", max_batch: int = SGEMV_MAX_BATCH):
+    def __init__(self, q, scales_f16, zeros_f16, device="cuda", max_batch: int = SGEMV_MAX_BATCH,
+                 z4: bool = False):
         import torch
-        self.desc, blob = sgemv_pack_layout(q, scales_f16, zeros_f16)
+        pack = sgemv_pack_layout_z4 if z4 else sgemv_pack_layout
+        self.desc, blob = pack(q, scales_f16, zeros_f16)
         self.blob = torch.from_numpy(blob).to(device)
         self.workspace = torch.zeros(max(sgemv_workspace_bytes(self.desc, max_batch), 256),
                                      dtype=torch.uint8, device=device)
@@ -237,7 +249,7 @@ class FusedProjections:
     tile belongs to one projection.  `split(y)` returns the per-projection
     views of the concatenated output."""
 
-    def __init__(self, parts, device="cuda", max_batch: int = 2):
+    def __init__(self, parts, device="cuda", max_batch: int = 2, z4: bool = False):
         names = [p[0] for p in parts]
         if len(set(names)) != len(names):
             raise ValueError("projection names must be unique")
@@ -255,7 +267,7 @@ class FusedProjections:
         q = np.concatenate([np.asarray(p[1], dtype=np.uint8) for p in parts])
         s = np.concatenate([np.asarray(p[2]).view(np.uint16) for p in parts])
         z = np.concatenate([np.asarray(p[3]).view(np.uint16) for p in parts])
-        self.matrix = PackedMatrix(q, s, z, device=device, max_batch=max_batch)
+        self.matrix = PackedMatrix(q, s, z, device=device, max_batch=max_batch, z4=z4)
         self.N, self.K = self.matrix.N, self.matrix.K
 
     def split(self, y):

@@ -60,10 +60,12 @@ def gather_bytes(K: int, A: int, M: int = 1) -> int:
     return M * K * 2 + A * 4 + 4
 
 
-def fused_bytes(A: int, Ag: int, N: int, K: int, M: int = 1, with_list: bool = True) -> int:
-    """One fused step: weight columns and metadata as above, every
+def fused_bytes(A: int, Ag: int, N: int, K: int, M: int = 1, with_list: bool = True, z4: bool = False) -> int:
+    """One fused step: weight columns and metadata as above (2.5 instead of
+    4 bytes per output and touched group with the compact metadata), every
     activation once, the list and count (when written) and the output."""
-    return A * N // 2 + Ag * N * 4 + M * K * 2 + (A * 4 + 4 if with_list else 0) + M * N * 2
+    md = Ag * N * 5 // 2 if z4 else Ag * N * 4
+    return A * N // 2 + md + M * K * 2 + (A * 4 + 4 if with_list else 0) + M * N * 2
 
 
 def touched_groups(idx: np.ndarray) -> int:
@@ -167,6 +169,26 @@ def main():
         if latency:
             out["single_call_latency_us"] = eager_latency(f)
         return out
+
+    def measure_fused_z4(ps, steps, warmup):
+        """The step on the same matrix packed with compact metadata (layout
+        version 2: fp16 scales, 4-bit zero-points)."""
+        d2, b2 = sgemv.sgemv_pack_layout_z4(q, s, z)
+        R2 = max(2, -(-ROTATE_BYTES // d2.total_bytes))
+        bd = torch.from_numpy(b2).to(dev)
+        cps = [bd] + [bd.clone() for _ in range(R2 - 1)]
+        res = {}
+        for p in ps:
+            t = synth.percentile_threshold(x, p)
+            us = graph_time([lambda i: sgemv.sgemv_run_fused(d2, cps[i % R2], xd, [t], y, ws, idx, cnt)],
+                            steps, warmup)
+            A, Ag = list_now()
+            fb = fused_bytes(A, Ag, N_DOWN, K_DOWN, z4=True)
+            res[f"fused_p{int(p * 100)}_z4"] = {"p": p, "active": A, "groups_touched": Ag, "us_per_step": us,
+                                               "bytes": fb, "GBps": fb / (us * 1e-6) / 1e9,
+                                               "frac_hbm_peak": fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        del cps, bd
+        return res
 
     def measure_split(p, steps, warmup, dense=False):
         t = synth.percentile_threshold(x, p)
@@ -325,6 +347,7 @@ def main():
         for p in (0.7, 0.9):
             sweep[f"fused_p{int(p * 100)}"] = measure_fused(p, args.steps, args.warmup)
         sweep["fused_p50_no_list"] = measure_fused(0.5, args.steps, args.warmup, with_list=False)
+        sweep.update(measure_fused_z4((0.5, 0.9), args.steps, args.warmup))
         for p in (0.5, 0.7, 0.9):
             sweep[f"split_p{int(p * 100)}"] = measure_split(p, args.steps, args.warmup)
         sweep["dense_int4"] = measure_split(0.0, args.steps, args.warmup, dense=True)

@@ -11,6 +11,7 @@
  * this library provides one call for each, plus the batched variant:
  *
  *   sgemv_pack_layout     host: int4 codes + fp16 scale/zero -> packed blob
+ *                         (sgemv_pack_layout_z4: the same with 4-bit zeros)
  *   sgemv_gather_indices  device: threshold x, emit the ascending list of
  *                         active indices and its length
  *   sgemv_run             device: y = W . x over the listed columns (M = 1)
@@ -66,8 +67,10 @@ typedef struct sgemv_desc {
     uint64_t w_off;        /* byte offset of the weight region (= 256)     */
     uint64_t w_bytes;      /* N*K/2                                        */
     uint64_t m_off;        /* byte offset of the scale/zero region         */
-    uint64_t m_bytes;      /* (K/128)*N*4                                  */
+    uint64_t m_bytes;      /* (K/128)*N*4, or (K/128)*N*5/2 for version 2  */
     uint64_t total_bytes;  /* size of the whole blob                       */
+    uint32_t version;      /* SGEMV_LAYOUT_PAIRS or SGEMV_LAYOUT_Z4        */
+    uint32_t reserved;     /* 0                                            */
 } sgemv_desc;
 
 enum sgemv_status {
@@ -85,6 +88,8 @@ enum sgemv_status {
 #define SGEMV_MAX_N       (1 << 20)
 #define SGEMV_TILE_N      512   /* the tile width the device kernels run   */
 #define SGEMV_OUT_F32     1u    /* flag: y is fp32 instead of fp16         */
+#define SGEMV_LAYOUT_PAIRS 1u   /* layout version 1: (s, z) fp16 pairs     */
+#define SGEMV_LAYOUT_Z4    2u   /* layout version 2: fp16 s, 4-bit z       */
 
 /*
  * sgemv_pack_layout - re-lay int4 weights so that each active input index
@@ -127,9 +132,34 @@ int sgemv_pack_layout(const uint8_t* q, const uint16_t* scales_f16,
                       int32_t group, int32_t tile_n, void* out,
                       size_t out_capacity, sgemv_desc* desc_out);
 
+/*
+ * sgemv_pack_layout_z4 - the same layout with compact metadata (version 2).
+ *
+ * The weight region is byte for byte that of sgemv_pack_layout.  The
+ * zero-points are integers 0..15, so they take 4 bits: the run of one
+ * (tile, group) pair holds the tile_n fp16 scales, then tile_n/2 bytes of
+ * zero-points, two per byte.  Same numbers, 2.5 instead of 4 bytes per row
+ * and group: this carries the page's sparsity-consistent layout (Abstract)
+ * to the metadata, which every touched group still reads in full.
+ *
+ *   header as above with version 2 and m_bytes = (K/128)*N*5/2
+ *   scale       m_off + (t*(K/128) + g)*(5*tile_n/2) + 2i : fp16 bits of
+ *               s[t*tile_n + i][g] (little-endian u16)
+ *   zero-points m_off + (t*(K/128) + g)*(5*tile_n/2) + 2*tile_n + j
+ *               = z[t*tile_n + 2j][g] | z[t*tile_n + 2j + 1][g] << 4
+ *
+ * Arguments, ownership and errors as for sgemv_pack_layout.  Every device
+ * call takes either version (desc->version) and computes bit for bit the
+ * same y from both.
+ */
+int sgemv_pack_layout_z4(const uint8_t* q, const uint16_t* scales_f16,
+                         const uint16_t* zeros_f16, int32_t N, int32_t K,
+                         int32_t group, int32_t tile_n, void* out,
+                         size_t out_capacity, sgemv_desc* desc_out);
+
 /* Parse and check the 64-byte header of a blob held in host memory (for a
- * blob that was saved and reloaded).  EINVAL on a bad magic, version or
- * inconsistent offsets. */
+ * blob that was saved and reloaded; version 1 or 2).  EINVAL on a bad magic,
+ * version or inconsistent offsets. */
 int sgemv_desc_from_header(const void* header, size_t bytes, sgemv_desc* desc_out);
 
 /*

@@ -19,7 +19,7 @@ def declared_functions():
     with open(os.path.join(ROOT, "include", "sgemv.h")) as f:
         src = f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(sgemv_[a-z_]+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(sgemv_[a-z_0-9]+)\s*\(", src, flags=re.M)))
 
 
 def test_exports_every_declared_symbol():
@@ -42,6 +42,29 @@ def test_packer_matches_spec(N, K, tile):
         assert getattr(d, k) == v, k
     d2 = sgemv.sgemv_desc_from_header(blob)
     assert d2.as_dict() == d.as_dict()
+
+
+@pytest.mark.parametrize("N,K,tile", [(512, 128, 512), (1024, 384, 512), (512, 256, 64),
+                                      (2048, 256, 1024), (4096, 1024, 512)])
+def test_packer_z4_matches_spec(N, K, tile):
+    """Layout version 2 (4-bit zero-points) byte for byte against the spec,
+    and its weight region equal to version 1's."""
+    q, s, z = synth.random_int4_problem(N * 5 + K, N, K)
+    d, blob = sgemv.sgemv_pack_layout_z4(q, s, z, tile)
+    ref = oracle.pack_spec(q, s, z, tile, 2)
+    assert blob.shape == ref.shape and np.array_equal(blob, ref)
+    for k, v in oracle.header_fields(N, K, tile, 2).items():
+        assert getattr(d, k) == v, k
+    assert d.version == sgemv.SGEMV_LAYOUT_Z4
+    d1, blob1 = sgemv.sgemv_pack_layout(q, s, z, tile)
+    assert d1.version == sgemv.SGEMV_LAYOUT_PAIRS
+    assert np.array_equal(blob[d.w_off:d.m_off], blob1[d1.w_off:d1.m_off])
+    d2 = sgemv.sgemv_desc_from_header(blob)
+    assert d2.as_dict() == d.as_dict()
+    # a negative zero zero-point is the integer 0
+    z0 = z.copy(); z0[0, 0] = 0x8000
+    _, b0 = sgemv.sgemv_pack_layout_z4(q, s, z0, tile)
+    assert b0[d.m_off + 2 * tile] & 0x0F == 0
 
 
 def test_packer_quantized_weights():
