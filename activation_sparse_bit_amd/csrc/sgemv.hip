@@ -73,6 +73,10 @@ struct RunArgs {
     int32_t segs;            // fused kernel: column segments
     uint32_t all_cols;       // fused kernels: every column listed (dense), rows masked unless unmasked
     uint32_t unmasked;       // fused kernels: activations used as they are (no thresholds)
+    int32_t gblocks;         // many-row fused kernel: workgroups that build the list (0 without one)
+    int32_t grange;          // ... columns per such workgroup (a multiple of 128)
+    int32_t* gscratch;       // ... their lists, at the first column of each range ([K])
+    uint32_t* gsync;         // ... [0]: arrival counter, [16 + j]: length of list j
 };
 
 __device__ __forceinline__ uint32_t code_of(const Codes& c, int m) {
@@ -150,11 +154,14 @@ __device__ __forceinline__ uint32_t union_mask8(const uint16_t* __restrict__ x, 
     return m8;
 }
 
-// Wavefronts W and above of the workgroup only join the barrier.
-template <int W>
+// Wavefronts W and above of the workgroup only join the barrier.  The
+// entries written are kbase + column (x points at column kbase); with COH
+// the list and count are stored device-coherent (written through), for a
+// workgroup on another XCD to read.
+template <int W, bool COH = false>
 __device__ __forceinline__ void gather_body(const uint16_t* __restrict__ x, int M, int K, int ldx, const Codes& tc,
                                             int32_t* __restrict__ idx, int32_t* __restrict__ count,
-                                            GatherShared& gs) {
+                                            GatherShared& gs, int kbase = 0) {
     static_assert(W == 4 || W == 8 || W == 16, "K / W must stay a multiple of 8");
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -186,7 +193,10 @@ __device__ __forceinline__ void gather_body(const uint16_t* __restrict__ x, int 
         wbase += (w < wave) ? t : 0u;
         grand += t;
     }
-    if (threadIdx.x == 0) *count = (int32_t)grand;
+    if (threadIdx.x == 0) {
+        if (COH) __hip_atomic_store(count, (int32_t)grand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else *count = (int32_t)grand;
+    }
 
     uint32_t running = wbase;
     for (int s = 0; s * 512 < Kw; ++s) {
@@ -197,7 +207,8 @@ __device__ __forceinline__ void gather_body(const uint16_t* __restrict__ x, int 
         uint32_t pos = running + pre;
         while (m8) {
             const int b = __builtin_ctz(m8);
-            idx[pos++] = base + off + b;
+            if (COH) __hip_atomic_store(&idx[pos++], kbase + base + off + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else idx[pos++] = kbase + base + off + b;
             m8 &= m8 - 1u;
         }
         running += tot;
@@ -1545,12 +1556,61 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     __shared__ FmLds lds;
     __shared__ uint32_t last_flag;
     int bid = blockIdx.x;
-    if (a.idx_out) {  // block 0 writes the list
-        if (bid == 0) {
-            gather_body<fm::kWaves>(a.x, a.M, a.K, a.ldx, a.tc, a.idx_out, a.count_out, lds.gl);
+    if (a.idx_out) {  // blocks 0 .. gblocks - 1 write the list
+        const int G = a.gblocks;
+        if (bid < G) {
+            if (G == 1) {
+                gather_body<fm::kWaves>(a.x, a.M, a.K, a.ldx, a.tc, a.idx_out, a.count_out, lds.gl);
+                return;
+            }
+            // list of columns k0 .. k0 + kr - 1 into the scratch at k0, and its length
+            const int k0 = bid * a.grange;
+            const int kr = a.K - k0 < a.grange ? a.K - k0 : a.grange;
+            gather_body<fm::kWaves, true>(a.x + k0, a.M, kr, a.ldx, a.tc, a.gscratch + k0,
+                                          reinterpret_cast<int32_t*>(a.gsync) + 16 + bid, lds.gl, k0);
+            __builtin_amdgcn_s_waitcnt(0);  // this thread's stores acknowledged
+            __syncthreads();                // ... and every thread's, before the count
+            if (threadIdx.x == 0) {
+                const uint32_t old = __hip_atomic_fetch_add(a.gsync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last_flag = (old == (uint32_t)(G - 1)) ? 1u : 0u;
+            }
+            __syncthreads();
+            if (last_flag == 0u) return;
+            // the last to arrive joins the lists in range order
+            int len[8], pre[8], tot = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                len[j] = j < G ? __hip_atomic_load(reinterpret_cast<int32_t*>(a.gsync) + 16 + j, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : 0;
+                pre[j] = tot;
+                tot += len[j];
+            }
+            // thread t moves list positions t, t + 512, ..., 16 loads in flight
+            constexpr int kT = fm::kWaves * 64;
+            for (int p0 = threadIdx.x; p0 < tot; p0 += 16 * kT) {
+                int v[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int p = p0 + i * kT;
+                    int j = 0;
+#pragma unroll
+                    for (int r = 1; r < 8; ++r) j += (r < G && p >= pre[r]) ? 1 : 0;
+                    const int src = j * a.grange + (p - pre[j]);
+                    v[i] = p < tot ? __hip_atomic_load(a.gscratch + src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                   : 0;
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (p0 + i * kT < tot) a.idx_out[p0 + i * kT] = v[i];
+            }
+            if (threadIdx.x == 0) {
+                *a.count_out = tot;
+                __hip_atomic_store(a.gsync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
             return;
         }
-        --bid;
+        bid -= G;
     }
     const int T = a.tiles;
     const int vt = bid % T;
@@ -1923,6 +1983,14 @@ int check_desc(const sgemv_desc* d) {
 // different half tiles go to different cache lines (and L2 channels).
 size_t ws_counters_bytes(int tiles) { return (size_t)tiles * kCounterStride * 4; }
 
+// The many-row fused call's list workgroups: a 256-byte line (their arrival
+// counter and list lengths), then a K-entry scratch list.
+size_t ws_gather_bytes(const sgemv_desc* d) { return 256 + ((size_t)d->K * 4 + 255) / 256 * 256; }
+
+// Workspace: counters, the list workgroups' region, then the partial sums
+// (whose size depends on the largest batch).
+size_t ws_head_bytes(const sgemv_desc* d) { return ws_counters_bytes(d->N / kVTile) + ws_gather_bytes(d); }
+
 size_t ws_partial_bytes(const sgemv_desc* d, int mt) {
     const int tiles = d->N / kVTile;
     const int s = slices_for(d, mt);
@@ -2011,8 +2079,7 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
     a.count = count;
     a.y = y;
     a.counters = static_cast<uint32_t*>(ws);
-    a.partials = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ws_counters_bytes(a.tiles))
-                    : nullptr;
+    a.partials = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ws_head_bytes(d)) : nullptr;
     a.partial_bytes = (uint32_t)pbytes;
     a.K = d->K;
     a.ldx = ldx;
@@ -2087,14 +2154,26 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     a.idx_out = idx;
     a.count_out = count;
     a.counters = static_cast<uint32_t*>(ws);
-    a.partials = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ws_counters_bytes(a.tiles)) : nullptr;
+    a.partials = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ws_head_bytes(d)) : nullptr;
+    if (ws) {
+        a.gsync = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + ws_counters_bytes(a.tiles));
+        a.gscratch = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + ws_counters_bytes(a.tiles) + 256);
+    }
+    // list workgroups of the many-row kernel: about 64 KiB of activations each, at most 8
+    a.gblocks = idx ? 1 : 0;
+    if (idx && M > 2 && ws) {
+        long g = ((long)M * d->K * 2 + 65535) / 65536;
+        g = g < 1 ? 1 : (g > 8 ? 8 : g);
+        a.grange = (int)((d->K / kGroup + g - 1) / g) * kGroup;
+        a.gblocks = (d->K + a.grange - 1) / a.grange;
+    }
     a.partial_bytes = (uint32_t)ws_fused_bytes(d, M);
     a.K = d->K;
     a.ldx = ldx;
     a.ldy = ldy;
     a.M = M;
     a.out_f32 = (flags & SGEMV_OUT_F32) ? 1u : 0u;
-    const dim3 grid((unsigned)(a.tiles * a.segs + (idx ? 1 : 0)));  // + the list's workgroup
+    const dim3 grid((unsigned)(a.tiles * a.segs + a.gblocks));  // + the list's workgroups
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool one_round = a.tiles * a.segs <= kFsOneRound;
     if (a.md_z4) launch_fused<true>(M, one_round, grid, a, s);
@@ -2164,7 +2243,7 @@ extern "C" size_t sgemv_workspace_bytes(const sgemv_desc* d, int32_t M) {
         const size_t b = ws_fused_bytes(d, m);
         part = b > part ? b : part;
     }
-    return ws_counters_bytes(tiles) + part;
+    return ws_head_bytes(d) + part;
 }
 
 extern "C" const char* sgemv_strerror(int status) {
