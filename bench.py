@@ -151,6 +151,28 @@ def main():
             ms.append(a.elapsed_time(b))
         return float(np.mean(ms) * 1000.0)
 
+    def cold_latency(launch, n=20):
+        """Single calls with the caches cold: a 1 GiB scratch write before
+        each (so neither L2 nor the Infinity Cache holds anything of the
+        call), then HIP events around the call.  Returns p10/p50/p90 in
+        microseconds."""
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        ms = []
+        for i in range(n + 2):
+            scratch.fill_(i & 0xFF)
+            a, b = ev(), ev()
+            cur = torch.cuda.current_stream()
+            a.record(cur)
+            launch(i)
+            b.record(cur)
+            torch.cuda.synchronize()
+            if i >= 2:
+                ms.append(a.elapsed_time(b) * 1000.0)
+        del scratch
+        torch.cuda.empty_cache()
+        q = np.percentile(ms, [10, 50, 90])
+        return {"p10": float(q[0]), "p50": float(q[1]), "p90": float(q[2]), "calls": n}
+
     def list_now():
         c = int(cnt.item())
         lst = idx[:c].cpu().numpy()
@@ -168,6 +190,7 @@ def main():
                "GBps": fb / (us * 1e-6) / 1e9, "frac_hbm_peak": fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
         if latency:
             out["single_call_latency_us"] = eager_latency(f)
+            out["cold_single_call_us"] = cold_latency(f)
         return out
 
     def measure_fused_z4(ps, steps, warmup):
