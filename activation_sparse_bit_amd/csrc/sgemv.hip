@@ -12,21 +12,26 @@
 //   k_gather   one 1024-thread workgroup: per-lane 8-element masks from
 //              16-byte loads, wavefront ballots and mbcnt for in-wave ranks,
 //              an LDS scan across the 16 wavefronts, ordered index writes.
-//   k_sp       one or two activation rows (the decode case): every
-//              wavefront takes 32 list positions of one half tile (256
-//              outputs) and loads them at once with 16-byte loads that
-//              cover 8 listed columns per instruction.
-//   k_run      3 to 16 rows: each wavefront walks a contiguous run of list
-//              positions of one half tile, every lane reading 2 bytes
-//              (4 outputs) of each listed column, with the next chunk's
-//              loads in flight while it computes the current one.
-// Both GEMV kernels dequantize exactly in fp16 (magic-number nibble
-// extraction, q - z in fp16) and accumulate with v_dot2_f32_f16 in fp32,
-// applying the group scale once per (group, output).  Lanes, wavefronts and
-// workgroups are combined in fixed orders (the last workgroup of a half tile
-// to arrive adds the others' published sums in slice order), so the result
-// is bitwise reproducible.  No MFMA: a matrix-vector product is bound by HBM
-// bandwidth and by the dequantization arithmetic, not by multiply-adds.
+//   k_gstart   where each quantization group's entries start in a given
+//              list (for the many-row kernel over that list).
+//   k_sp       one or two rows over a given list: every wavefront takes 32
+//              list positions of one half tile (256 outputs) and loads them
+//              at once with 16-byte loads that cover 8 listed columns per
+//              instruction.
+//   k_fs, k_fs4  one or two rows, fused: threshold, compaction and GEMV in
+//              one launch, one quantization group per wavefront (k_fs4: the
+//              128-register build for grids of several rounds); with every
+//              column listed, also the dense GEMV.
+//   k_fm       3 to 16 rows, fused (or over a given list): the union of the
+//              rows' active columns, exact fp16 dequantization in registers
+//              and v_mfma_f32_16x16x32_f16 on the matrix cores.
+// The vector kernels dequantize exactly in fp16 (magic-number nibble
+// extraction, q - z in fp16) and accumulate with v_dot2_f32_f16 in fp32; the
+// matrix kernel feeds the same exact values to the MFMA.  The group scale is
+// applied once per (group, output).  Lanes, wavefronts and workgroups are
+// combined in fixed orders (the last workgroup of a half tile to arrive adds
+// the others' published sums in segment order), so the result is bitwise
+// reproducible.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -44,8 +49,6 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 constexpr int kTileN = SGEMV_TILE_N;  // outputs per tile
 constexpr int kGroup = SGEMV_GROUP;
 constexpr int kCounterStride = 64;   // uint32 words between arrival counters
-constexpr int kChunk = 16;            // list positions a wavefront loads at once
-constexpr int kColBytes = kTileN / 2; // bytes of one column within one tile
 
 thread_local int g_last_hip_error = 0;
 
@@ -77,6 +80,9 @@ struct RunArgs {
     int32_t grange;          // ... columns per such workgroup (a multiple of 128)
     int32_t* gscratch;       // ... their lists, at the first column of each range ([K])
     uint32_t* gsync;         // ... [0]: arrival counter, [16 + j]: length of list j
+    const int32_t* lidx;     // many-row fused kernel over a given list (NULL: the list is computed)
+    const int32_t* lcount;   // ... its length
+    const int32_t* gstart;   // ... position of each group's first entry ([K/128 + 1], k_gstart)
 };
 
 __device__ __forceinline__ uint32_t code_of(const Codes& c, int m) {
@@ -222,25 +228,43 @@ __global__ __launch_bounds__(1024) void k_gather(const uint16_t* __restrict__ x,
     gather_body<16>(x, M, K, ldx, tc, idx, count, gs);
 }
 
+// Start of each quantization group's entries in an ascending list:
+// start[g] = the first position whose column is >= 128 g, start[K/128] =
+// count.  Thread p compares entries p - 1 and p and writes the starts of the
+// groups in between, so every entry is written for an ascending list (one
+// that is not gives wrong starts, never a stray access; the readers clamp).
+__global__ __launch_bounds__(256) void k_gstart(const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
+                                                int K, int32_t* __restrict__ start) {
+    const int Gk = K / kGroup;
+    int c = *count;
+    c = c < 0 ? 0 : (c > K ? K : c);
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    if (c == 0) {
+        for (int s = p; s <= Gk; s += gridDim.x * 256) start[s] = 0;
+        return;
+    }
+    if (p >= c) return;
+    auto grp = [&](int q) {
+        int k = idx[q];
+        k = k < 0 ? 0 : (k >= K ? K - 1 : k);
+        return k / kGroup;
+    };
+    const int g = grp(p);
+    const int gp = p > 0 ? grp(p - 1) : -1;
+    for (int s = gp + 1; s <= g; ++s) start[s] = p;
+    if (p == c - 1)
+        for (int s = g + 1; s <= Gk; ++s) start[s] = c;
+}
+
 // ---------------------------------------------------------------------------
 // sparse / dense GEMV
 // ---------------------------------------------------------------------------
 //
-// Work split.  A workgroup owns 256 outputs: one half of a 512-output layout
-// tile, whose part of every column run is 128 contiguous bytes (one cache
-// line).  The grid is (N / 256 half tiles) x S slices, S set by the host so
-// that the grid is about one workgroup per CU.  At run time the listed
-// positions are cut into chunks of 16; a half tile's chunks are divided
-// evenly among its S' = min(S, chunks) slices and, inside a workgroup,
-// among its wavefronts, so every wavefront owns a contiguous run of list
-// positions whatever the sparsity.  Lane l owns outputs 4l .. 4l+3 of the
-// half tile and reads 2 bytes of each listed column.
-//
-// Pipeline.  A wavefront keeps the data of its next chunk and the list
-// entries of the chunk after it in flight while it computes the current
-// one.  Every load is issued unconditionally (past the end of the run it
-// re-reads the last chunk, which the caches serve), so each wait counts
-// exactly the loads issued after the data it needs.
+// Every kernel works on half tiles: a workgroup owns 256 outputs, one half
+// of a 512-output layout tile, whose part of every column run is 128
+// contiguous bytes (one cache line).  The list-driven kernel (one or two
+// rows over a given list), the fused one- and two-row kernels and the fused
+// many-row kernel each describe their work split below.
 //
 // Arithmetic.  For two listed columns a, b the two 4-bit codes of one output
 // are placed in the low mantissa bits of 0x6400 (= 1024.0 in fp16), which
@@ -330,432 +354,10 @@ __device__ __forceinline__ u32x4 md_words4(const MdHalf& m, int g, int o) { retu
 
 // Wavefronts per workgroup: two per SIMD for few rows; four in all for
 // many rows, whose accumulators fill the register file.
-template <int MT>
-struct Waves {
-    static constexpr int kN = MT <= 4 ? 8 : 4;
-};
-
-// Scale/zero words of this lane's 4 outputs for one group.
-__device__ __forceinline__ void load_md4(const MdHalf& mh, int g, int lane, uint32_t (&md)[4]) {
-    const u32x4 v = md_words4(mh, g, 4 * lane);
-    md[0] = v.x; md[1] = v.y; md[2] = v.z; md[3] = v.w;
-}
-
-// Rows of x staged per lane: lane L holds row (L / 16) + 4 j of listed
-// column L % 16 in xv[j].
-template <int MT>
-struct XRows {
-    static constexpr int kPerLane = MT <= 4 ? 1 : MT / 4;
-    static constexpr int kLanes = MT < 4 ? MT * kChunk : 64;
-};
-
-template <int MT>
-struct Chunk {
-    int j0;                    // first list position
-    int nv;                    // valid positions
-    int gA, gZ;                // groups of the first and last valid position
-    uint32_t codes;            // 2 bits per position: min(group - gA, 3)
-    uint32_t w[kChunk];        // this lane's 2 bytes of each column (low half)
-    uint32_t md0[4];           // metadata of group gA
-    uint32_t md1[4];           // metadata of group gA + 1 (gA when the chunk has one group)
-    uint32_t xv[XRows<MT>::kPerLane];  // staged x values (fp16 bits)
-};
-
-struct WaveCtx {
-    const uint8_t* wcol;      // weights of this half tile: column k at + k * 256
-    MdHalf mdh;               // metadata of this half tile
-    int lane, K, p1;          // the wavefront's list positions end at p1
-    uint32_t vmagic;          // 0x64006400 (two fp16 1024.0) held in a VGPR
-};
-
-// The 16 list entries of a chunk in one VGPR: lane L holds entry
-// j0 + L % 16.  j0 is a multiple of 16 below K and K is a multiple of 128,
-// so the entries are inside the K-entry list.
-struct Idx {
-    int v;
-};
-
-template <bool DENSE>
-__device__ __forceinline__ void idx_load(const RunArgs& a, int j0, int lane, Idx& ix) {
-    if (DENSE) return;
-    ix.v = a.idx[j0 + (lane & (kChunk - 1))];
-}
-
-// The chunk's listed columns, clamped and padded: positions past nv repeat
-// the last valid column.
-template <bool DENSE>
-__device__ __forceinline__ void chunk_columns(const Idx& ix, int j0, int nv, int K, int (&kk)[kChunk]) {
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-        int k;
-        if (DENSE) {
-            k = j0 + (i < nv ? i : nv - 1);
-        } else {
-            k = __builtin_amdgcn_readlane(ix.v, i);
-            k = (i == 0 || i < nv) ? k : kk[i > 0 ? i - 1 : 0];
-            k = (unsigned)k < (unsigned)K ? k : K - 1;
-        }
-        kk[i] = __builtin_amdgcn_readfirstlane(k);
-    }
-}
-
-// Issue every load of one chunk: 16 weight half-runs, the scale/zero words
-// of its first two groups, and the activations.
-template <int MT, bool DENSE, bool MASK>
-__device__ __forceinline__ void data_load(const RunArgs& a, const WaveCtx& wc, int j0, const Idx& ix,
-                                          Chunk<MT>& ch) {
-    const int K = wc.K;
-    int nv = wc.p1 - j0;
-    nv = nv > kChunk ? kChunk : nv;
-    ch.j0 = j0;
-    ch.nv = nv;
-    int kk[kChunk];
-    chunk_columns<DENSE>(ix, j0, nv, K, kk);
-    ch.gA = kk[0] >> 7;
-    ch.gZ = kk[kChunk - 1] >> 7;
-    uint32_t codes = 0;
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-        const int d = (kk[i] >> 7) - ch.gA;
-        codes |= (uint32_t)(d < 3 ? d : 3) << (2 * i);
-    }
-    ch.codes = codes;
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-        const uint16_t* col = reinterpret_cast<const uint16_t*>(wc.wcol + (size_t)kk[i] * (2 * kHalfRun));
-        ch.w[i] = __builtin_nontemporal_load(col + wc.lane);
-    }
-    const int g1 = ch.gA + 1 <= ch.gZ ? ch.gA + 1 : ch.gZ;
-    load_md4(wc.mdh, ch.gA, wc.lane, ch.md0);
-    load_md4(wc.mdh, g1, wc.lane, ch.md1);
-    // x: one vector load per staged row; lane L fetches column L % 16,
-    // whose index it already holds
-    const int c = wc.lane & (kChunk - 1);
-    int kc = DENSE ? j0 + c : ix.v;
-    kc = (unsigned)kc < (unsigned)K ? kc : K - 1;
-#pragma unroll
-    for (int j = 0; j < XRows<MT>::kPerLane; ++j) {
-        const int m = (wc.lane >> 4) + 4 * j;
-        const bool ok = wc.lane < XRows<MT>::kLanes && m < a.M && c < nv;
-        const int mr = ok ? m : 0;
-        const int kr = ok ? kc : 0;
-        uint32_t v = a.x[(size_t)mr * a.ldx + kr];
-        if (MASK && !is_active(v, code_of(a.tc, mr))) v = 0;
-        ch.xv[j] = ok ? v : 0u;
-    }
-}
-
 // (R & mask) | magic: with the magic held in a VGPR the compiler can use one
 // v_and_or_b32 (a VOP3 instruction on this target takes no literal).
 __device__ __forceinline__ uint32_t and_or(uint32_t r, uint32_t mask, uint32_t vmagic) {
     return (r & mask) | vmagic;
-}
-
-// One pass over the 8 column pairs of a chunk for one group: x is masked to
-// the positions of that group (pmask), so every pair uses the same scale
-// and zero-point.  Byte i of a lane's half-run holds its outputs 2i (low
-// nibble) and 2i+1 (high nibble).
-template <int MT>
-__device__ __forceinline__ void chunk_pass(float (&y)[MT][4], const Chunk<MT>& ch, const uint32_t (&md)[4],
-                                           const uint32_t (&pmask)[kChunk / 2],
-                                           const uint16_t (*xs)[kChunk], uint32_t vmagic) {
-    half2_t zc[4];
-    float sc[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const half2_t v = as_h2(md[r]);
-        sc[r] = (float)v.x;
-        const _Float16 z = (r & 1) ? (_Float16)(v.y * (_Float16)16.0f) : v.y;
-        zc[r] = (half2_t){z, z} + (half2_t){(_Float16)1024.0f, (_Float16)1024.0f};
-    }
-    float acc[MT][4];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[m][r] = 0.f;
-#pragma unroll
-    for (int p = 0; p < kChunk / 2; ++p) {
-        uint32_t xp[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) xp[m] = reinterpret_cast<const uint32_t*>(&xs[m][0])[p] & pmask[p];
-        const uint32_t A = ch.w[2 * p], B = ch.w[2 * p + 1];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            // byte i of A and of B into the low bytes of the two halves
-            const uint32_t sel = (0x0Cu << 24) | ((uint32_t)i << 16) | (0x0Cu << 8) | (4u + i);
-            const uint32_t R = __builtin_amdgcn_perm(A, B, sel);
-            const half2_t lo = as_h2(and_or(R, 0x000F000Fu, vmagic)) - zc[2 * i];      // q - z
-            const half2_t hi = as_h2(and_or(R, 0x00F000F0u, vmagic)) - zc[2 * i + 1];  // 16 (q - z)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                acc[m][2 * i] = __builtin_amdgcn_fdot2(lo, as_h2(xp[m]), acc[m][2 * i], false);
-                acc[m][2 * i + 1] = __builtin_amdgcn_fdot2(hi, as_h2(xp[m]), acc[m][2 * i + 1], false);
-            }
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) y[m][r] = __builtin_fmaf(sc[r], acc[m][r], y[m][r]);
-}
-
-// Pair masks for the positions whose bit is set in pos (bit i = position i).
-__device__ __forceinline__ void pair_masks(uint32_t pos, uint32_t (&pm)[kChunk / 2]) {
-#pragma unroll
-    for (int p = 0; p < kChunk / 2; ++p)
-        pm[p] = ((pos >> (2 * p)) & 1u ? 0x0000FFFFu : 0u) | ((pos >> (2 * p + 1)) & 1u ? 0xFFFF0000u : 0u);
-}
-
-// Positions (bit mask) whose 2-bit group code equals d.
-__device__ __forceinline__ uint32_t code_positions(uint32_t codes, uint32_t d, int nv) {
-    uint32_t pos = 0;
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) pos |= (((codes >> (2 * i)) & 3u) == d ? 1u : 0u) << i;
-    return pos & ((1u << nv) - 1u);
-}
-
-template <int MT, bool DENSE>
-__device__ __forceinline__ void chunk_compute(float (&y)[MT][4], const RunArgs& a, const WaveCtx& wc,
-                                              const Chunk<MT>& ch, uint16_t (*xs)[kChunk]) {
-    // this wavefront's private LDS slice: xs[m][c] = x of row m, column c
-#pragma unroll
-    for (int j = 0; j < XRows<MT>::kPerLane; ++j) {
-        const int m = (wc.lane >> 4) + 4 * j;
-        if (wc.lane < XRows<MT>::kLanes && m < MT) xs[m][wc.lane & (kChunk - 1)] = (uint16_t)ch.xv[j];
-    }
-    __builtin_amdgcn_wave_barrier();  // LDS operations of a wavefront complete in order
-    // groups gA, gA+1, gA+2: metadata prefetched (the third loaded here)
-    for (int d = 0; d <= 2; ++d) {
-        const uint32_t pos = code_positions(ch.codes, (uint32_t)d, ch.nv);
-        if (pos == 0) continue;
-        uint32_t md[4];
-        if (d == 2) {
-            load_md4(wc.mdh, ch.gA + 2, wc.lane, md);
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) md[r] = d ? ch.md1[r] : ch.md0[r];
-        }
-        uint32_t pm[kChunk / 2];
-        pair_masks(pos, pm);
-        chunk_pass(y, ch, md, pm, xs, wc.vmagic);
-    }
-    // a chunk spanning more than three groups (very sparse lists): the
-    // remaining groups one by one, with the list entries read again
-    if (code_positions(ch.codes, 3u, ch.nv) != 0) {
-        Idx ix;
-        idx_load<DENSE>(a, ch.j0, wc.lane, ix);
-        int kk[kChunk];
-        chunk_columns<DENSE>(ix, ch.j0, ch.nv, wc.K, kk);
-        int g = ch.gA + 3;
-        while (g <= ch.gZ) {
-            uint32_t pos = 0;
-            int gnext = ch.gZ + 1;
-#pragma unroll
-            for (int i = 0; i < kChunk; ++i) {
-                const int gi = kk[i] >> 7;
-                pos |= (gi == g ? 1u : 0u) << i;
-                gnext = (gi > g && gi < gnext) ? gi : gnext;
-            }
-            pos &= (1u << ch.nv) - 1u;
-            if (pos != 0) {
-                uint32_t md[4];
-                load_md4(wc.mdh, g, wc.lane, md);
-                uint32_t pm[kChunk / 2];
-                pair_masks(pos, pm);
-                chunk_pass(y, ch, md, pm, xs, wc.vmagic);
-            }
-            g = gnext;
-        }
-    }
-    // all reads of the slice are done before the next chunk overwrites it
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
-
-template <int MT>
-__device__ __forceinline__ void store_y(const RunArgs& a, int vt, int lane, const float (&v)[MT][4]) {
-    const int n0 = vt * kVTile + lane * 4;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        if (m >= a.M) break;
-        if (a.out_f32) {
-            *reinterpret_cast<float4*>(static_cast<float*>(a.y) + (size_t)m * a.ldy + n0) =
-                make_float4(v[m][0], v[m][1], v[m][2], v[m][3]);
-        } else {
-            const half2_t p0 = (half2_t){(_Float16)v[m][0], (_Float16)v[m][1]};
-            const half2_t p1 = (half2_t){(_Float16)v[m][2], (_Float16)v[m][3]};
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + (size_t)m * a.ldy + n0) =
-                make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
-        }
-    }
-}
-
-// Fixed-order tree over the workgroup's wavefronts; wavefront 0 ends with
-// the sum.  Must be reached by every wavefront.
-template <int MT>
-__device__ __forceinline__ void wg_tree(float (&v)[MT][4], float (*red)[MT][kVTile], int wave, int lane) {
-#pragma unroll
-    for (int h = Waves<MT>::kN / 2; h >= 1; h /= 2) {
-        if (wave >= h && wave < 2 * h) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                *reinterpret_cast<float4*>(&red[wave - h][m][lane * 4]) = make_float4(v[m][0], v[m][1], v[m][2], v[m][3]);
-        }
-        __syncthreads();
-        if (wave < h) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const float4 u = *reinterpret_cast<const float4*>(&red[wave][m][lane * 4]);
-                v[m][0] += u.x; v[m][1] += u.y; v[m][2] += u.z; v[m][3] += u.w;
-            }
-        }
-        __syncthreads();
-    }
-}
-
-template <int MT, bool DENSE, bool MASK, bool Z4>
-__global__ __launch_bounds__(Waves<MT>::kN * 64) void k_run(RunArgs a) {
-    constexpr int kWaves = Waves<MT>::kN;
-    __shared__ float red[kWaves / 2][MT][kVTile];
-    __shared__ uint16_t xs[kWaves][MT][kChunk];
-    __shared__ uint32_t last_flag;
-
-    const int T = a.tiles;
-    const int vt = blockIdx.x % T;         // half tile
-    const int slice = blockIdx.x / T;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int K = a.K;
-    const int Gk = K / kGroup;
-
-    int count;
-    if (DENSE) {
-        count = K;
-    } else {
-        count = __builtin_amdgcn_readfirstlane(*a.count);
-        count = count < 0 ? 0 : (count > K ? K : count);
-    }
-    if (count == 0) {  // nothing listed: y = +0
-        if (slice == 0 && wave == 0) {
-            float z[MT][4];
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) z[m][r] = 0.f;
-            store_y(a, vt, lane, z);
-        }
-        return;
-    }
-    const int nch = (count + kChunk - 1) / kChunk;        // chunks of 16 positions
-    const int S = a.slices < nch ? a.slices : nch;       // slices in use
-    if (slice >= S) return;
-    const int c0 = (int)((long long)nch * slice / S);
-    const int c1 = (int)((long long)nch * (slice + 1) / S);
-    const int wc0 = c0 + (c1 - c0) * wave / kWaves;
-    const int wc1 = c0 + (c1 - c0) * (wave + 1) / kWaves;
-
-    float y[MT][4];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y[m][r] = 0.f;
-
-    if (wc1 > wc0) {
-        const int t = vt >> 1, h = vt & 1;
-        WaveCtx wc;
-        wc.wcol = a.w + (size_t)t * K * (2 * kHalfRun) + h * kHalfRun;
-        wc.mdh = md_half<Z4>(a, t, h);
-        wc.lane = lane;
-        wc.K = K;
-        wc.p1 = wc1 * kChunk < count ? wc1 * kChunk : count;
-        wc.vmagic = 0x64006400u | __builtin_amdgcn_mbcnt_lo(0u, 0u);  // per-lane (VGPR) copy
-
-        // Loads are issued in the order idx(c+2), data(c+1), so that the data
-        // of a chunk only ever waits for its own, older, list entries.
-        const int cl = wc1 - 1;
-        Idx I0, I1;
-        Chunk<MT> A, B;
-        idx_load<DENSE>(a, wc0 * kChunk, lane, I0);
-        idx_load<DENSE>(a, min(wc0 + 1, cl) * kChunk, lane, I1);
-        data_load<MT, DENSE, MASK>(a, wc, wc0 * kChunk, I0, A);
-        for (int c = wc0; c < wc1; c += 2) {
-            idx_load<DENSE>(a, min(c + 2, cl) * kChunk, lane, I0);
-            data_load<MT, DENSE, MASK>(a, wc, min(c + 1, cl) * kChunk, I1, B);
-            chunk_compute<MT, DENSE>(y, a, wc, A, xs[wave]);
-            idx_load<DENSE>(a, min(c + 3, cl) * kChunk, lane, I1);
-            data_load<MT, DENSE, MASK>(a, wc, min(c + 2, cl) * kChunk, I0, A);
-            if (c + 1 < wc1) chunk_compute<MT, DENSE>(y, a, wc, B, xs[wave]);
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            y[m][1] *= 0.0625f;  // the 16 of the high nibbles
-            y[m][3] *= 0.0625f;
-        }
-    }
-
-    wg_tree(y, red, wave, lane);
-
-    if (S == 1) {
-        if (wave == 0) store_y(a, vt, lane, y);
-        return;
-    }
-
-    // publish this slice's sums (write-through), then count the arrival
-    const __amdgpu_buffer_rsrc_t prs =
-        __builtin_amdgcn_make_buffer_rsrc(a.partials, (short)0, (int)a.partial_bytes, 0x00020000);
-    const uint32_t tile_base = (uint32_t)vt * a.slices * MT * kVTile * 4u;
-    if (wave == 0) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const uint32_t off = tile_base + ((uint32_t)slice * MT + m) * kVTile * 4u + lane * 16u;
-            const u32x4 v = {__float_as_uint(y[m][0]), __float_as_uint(y[m][1]),
-                             __float_as_uint(y[m][2]), __float_as_uint(y[m][3])};
-            __builtin_amdgcn_raw_buffer_store_b128(v, prs, off, 0, kCacheSC1);
-        }
-        __builtin_amdgcn_s_waitcnt(0);  // stores acknowledged before the count
-        uint32_t old = 0;
-        if (lane == 0)
-            old = __hip_atomic_fetch_add(&a.counters[vt * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        old = __builtin_amdgcn_readfirstlane(old);
-        if (lane == 0) last_flag = (old == (uint32_t)(S - 1)) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (last_flag == 0u) return;
-
-    // last to arrive: wavefront w adds slices w, w + kWaves, ... in order;
-    // the loads of up to four slices are issued together
-    float tot[MT][4];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) tot[m][r] = 0.f;
-    for (int sl0 = wave; sl0 < S; sl0 += 4 * kWaves) {
-        u32x4 u[4][MT];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int sl = sl0 + q * kWaves;
-            const int sc = sl < S ? sl : sl0;
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const uint32_t off = tile_base + ((uint32_t)sc * MT + m) * kVTile * 4u + lane * 16u;
-                u[q][m] = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, kCacheSC1);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (sl0 + q * kWaves >= S) break;
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                tot[m][0] += __uint_as_float(u[q][m].x); tot[m][1] += __uint_as_float(u[q][m].y);
-                tot[m][2] += __uint_as_float(u[q][m].z); tot[m][3] += __uint_as_float(u[q][m].w);
-            }
-        }
-    }
-    wg_tree(tot, red, wave, lane);
-    if (wave == 0) {
-        store_y(a, vt, lane, tot);
-        if (lane == 0) __hip_atomic_store(&a.counters[vt * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1542,6 +1144,7 @@ struct FmWave {
     __align__(16) int k[fm::kCols];                      // the wavefront's union columns
     __align__(16) uint32_t zc[kVTile / 2];               // per weight byte: (1024 + z, 1024 + 16 z)
     __align__(16) float sc[kVTile];                      // s (s / 16 for odd outputs), storage order
+    uint32_t lm[4];                                      // a given list's columns of the group, as a mask
 };
 
 union FmLds {
@@ -1667,6 +1270,22 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
         un = r32[0] | r32[1];
     }
     if (a.all_cols) un = has ? ~0u : 0u;
+    if (a.lidx) {  // a given list: the group's entries are the union (the rows stay masked by t)
+        if (lane < 4) fw.lm[lane] = 0u;
+        __builtin_amdgcn_wave_barrier();
+        int c = __builtin_amdgcn_readfirstlane(*a.lcount);
+        c = c < 0 ? 0 : (c > K ? K : c);
+        int s0 = has ? a.gstart[g] : 0, s1 = has ? a.gstart[g + 1] : 0;
+        s0 = s0 < 0 ? 0 : (s0 > c ? c : s0);
+        s1 = s1 < s0 ? s0 : (s1 > c ? c : s1);
+        s1 = s1 - s0 > fm::kCols ? s0 + fm::kCols : s1;
+        for (int e = lane; e < s1 - s0; e += 64) {
+            const int cc = a.lidx[s0 + e] - kw;
+            if ((unsigned)cc < (unsigned)fm::kCols) atomicOr(&fw.lm[cc >> 5], 1u << (cc & 31));
+        }
+        __builtin_amdgcn_wave_barrier();
+        un = fw.lm[lane & 3];  // word q at lane q, as the union above
+    }
     uint32_t U[4], base[4];
     int nact = 0;
 #pragma unroll
@@ -1914,7 +1533,6 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-constexpr int kTargetWGs = 256;   // about one workgroup per CU
 
 int pow2_ceil(int m) {
     int p = 1;
@@ -1924,14 +1542,9 @@ int pow2_ceil(int m) {
 
 // Slices per tile: enough workgroups to cover the chip, never more slices
 // than 16-position chunks in a full list.
-int slices_for(const sgemv_desc* d, int mt) {
-    if (mt <= 2) return (d->K + sp::kPos - 1) / sp::kPos;  // one workgroup per 256 list positions
-    const int tiles = d->N / kVTile;
-    int s = (kTargetWGs + tiles / 2) / tiles;
-    if (s < 1) s = 1;
-    const int maxs = d->K / kChunk;
-    return s > maxs ? maxs : s;
-}
+// Slices of the list-driven kernel (one or two rows): one workgroup per 256
+// list positions.
+int slices_for(const sgemv_desc* d, int) { return (d->K + sp::kPos - 1) / sp::kPos; }
 
 float half_value(uint32_t b) {
     const int e = (b >> 10) & 0x1F;
@@ -1985,7 +1598,13 @@ size_t ws_counters_bytes(int tiles) { return (size_t)tiles * kCounterStride * 4;
 
 // The many-row fused call's list workgroups: a 256-byte line (their arrival
 // counter and list lengths), then a K-entry scratch list.
-size_t ws_gather_bytes(const sgemv_desc* d) { return 256 + ((size_t)d->K * 4 + 255) / 256 * 256; }
+size_t ws_gather_bytes(const sgemv_desc* d) {
+    return 256 + ((size_t)d->K * 4 + 255) / 256 * 256 + ((size_t)(d->K / kGroup + 1) * 4 + 255) / 256 * 256;
+}
+int32_t* ws_gstart(const sgemv_desc* d, void* ws) {   // the group starts of a given list
+    return reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + ws_counters_bytes(d->N / kVTile) + 256 +
+                                      ((size_t)d->K * 4 + 255) / 256 * 256);
+}
 
 // Workspace: counters, the list workgroups' region, then the partial sums
 // (whose size depends on the largest batch).
@@ -2013,31 +1632,23 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // round (one per CU) with the two-wavefronts-per-SIMD build.
 constexpr int kFsOneRound = 256;
 
+// The list-driven kernel, one or two rows (3 and more rows over a given list
+// run on the fused many-row kernel).
 template <int MT, bool DENSE, bool MASK, bool Z4>
 hipError_t launch_run(const RunArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)(a.tiles * a.slices));  // slices: see slices_for
-    if (MT <= 2) {
-        hipLaunchKernelGGL((k_sp<(MT <= 2 ? MT : 1), DENSE, MASK, Z4>), grid, dim3(sp::kWaves * 64), 0, s, a);
-    } else {
-        hipLaunchKernelGGL((k_run<MT, DENSE, MASK, Z4>), grid, dim3(Waves<MT>::kN * 64), 0, s, a);
-    }
+    hipLaunchKernelGGL((k_sp<MT, DENSE, MASK, Z4>), grid, dim3(sp::kWaves * 64), 0, s, a);
     return hipGetLastError();
 }
 
 template <bool DENSE, bool MASK, bool Z4>
 hipError_t launch_mt(int mt, const RunArgs& a, hipStream_t s) {
-    switch (mt) {
-        case 1: return launch_run<1, DENSE, MASK, Z4>(a, s);
-        case 2: return launch_run<2, DENSE, MASK, Z4>(a, s);
-        case 4: return launch_run<4, DENSE, MASK, Z4>(a, s);
-        case 8: return launch_run<8, DENSE, MASK, Z4>(a, s);
-        default: return launch_run<16, DENSE, MASK, Z4>(a, s);
-    }
+    return mt == 1 ? launch_run<1, DENSE, MASK, Z4>(a, s) : launch_run<2, DENSE, MASK, Z4>(a, s);
 }
 
 int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx, const float* thr,
               int32_t* idx, int32_t* count, void* y, int ldy, uint32_t flags, void* ws, void* stream,
-              bool all_cols = false);
+              bool all_cols = false, const int32_t* lidx = nullptr, const int32_t* lcount = nullptr);
 
 int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx,
                const float* thr, const int32_t* idx, const int32_t* count, void* y, int ldy,
@@ -2055,6 +1666,23 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
     if (count && !aligned(count, 4)) return SGEMV_EALIGN;
     if (!idx)   // every column: the fused kernels with the whole list, which stream faster
         return run_fused(d, packed, x, M, ldx, thr, nullptr, nullptr, y, ldy, flags, ws, stream, true);
+    if (M > 2) {  // 3..16 rows over a given list: its group starts, then the many-row fused kernel
+        if (thr) {  // every argument is checked before the first launch
+            Codes c;
+            st = fill_codes(thr, M, c);
+            if (st) return st;
+        }
+        if (!ws) return SGEMV_EINVAL;
+        if (!aligned(ws, 256)) return SGEMV_EALIGN;
+        hipLaunchKernelGGL(k_gstart, dim3((unsigned)((d->K + 255) / 256)), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), idx, count, (int)d->K, ws_gstart(d, ws));
+        const hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) {
+            g_last_hip_error = (int)e0;
+            return SGEMV_EHIP;
+        }
+        return run_fused(d, packed, x, M, ldx, thr, nullptr, nullptr, y, ldy, flags, ws, stream, false, idx, count);
+    }
 
     const int mt = pow2_ceil(M);
     RunArgs a;
@@ -2112,10 +1740,10 @@ void launch_fused(int M, bool one_round, dim3 grid, const RunArgs& a, hipStream_
 
 int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx, const float* thr,
               int32_t* idx, int32_t* count, void* y, int ldy, uint32_t flags, void* ws, void* stream,
-              bool all_cols) {
+              bool all_cols, const int32_t* lidx, const int32_t* lcount) {
     int st = check_desc(d);
     if (st) return st;
-    if (!packed || !x || !y || (!thr && !all_cols)) return SGEMV_EINVAL;
+    if (!packed || !x || !y || (!thr && !all_cols && !lidx)) return SGEMV_EINVAL;
     if ((idx == nullptr) != (count == nullptr)) return SGEMV_EINVAL;
     if (flags & ~SGEMV_OUT_F32) return SGEMV_EINVAL;
     if (M < 1 || M > SGEMV_MAX_BATCH) return SGEMV_ESIZE;
@@ -2131,6 +1759,12 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
         if (st) return st;
     }
     a.all_cols = all_cols ? 1u : 0u;
+    if (lidx) {   // list mode (many rows): the group starts, written by k_gstart before
+        if (!ws) return SGEMV_EINVAL;
+        a.lidx = lidx;
+        a.lcount = lcount;
+        a.gstart = ws_gstart(d, ws);
+    }
     a.unmasked = thr ? 0u : 1u;
     a.tiles = d->N / kVTile;
     if (M <= 2) {
@@ -2235,7 +1869,7 @@ extern "C" size_t sgemv_workspace_bytes(const sgemv_desc* d, int32_t M) {
     if (check_desc(d) != SGEMV_OK || M < 1 || M > SGEMV_MAX_BATCH) return 0;
     const int tiles = d->N / kVTile;
     size_t part = 0;  // enough for every call with up to M rows
-    for (int mt = 1; mt <= pow2_ceil(M); mt *= 2) {
+    for (int mt = 1; mt <= (M < 2 ? M : 2); ++mt) {   // the list-driven kernel's rows
         const size_t b = ws_partial_bytes(d, mt);
         part = b > part ? b : part;
     }
