@@ -328,3 +328,48 @@ def test_run_batched_every_column(M):
         else:
             y_ref, B, _ = oracle.gemv_masked(q[rows], s[rows], z[rows], X, ts)
         G.check_y(y.cpu().numpy()[:, rows], y_ref, B, f"every column M={M} masked={thr is not None}")
+
+
+@pytest.mark.gpu
+def test_run_batched_given_list_edges():
+    """3+ rows over a given list (the many-row fused kernel in list mode):
+    an empty list, a hand-made list touching the first and last groups with
+    junk beyond its count, a ragged K, and a count above K (clamped)."""
+    from activation_sparse_bit_amd import sgemv
+    K, N, M = 1152, 1024, 5
+    q, s, z = synth.random_int4_problem(77, N, K)
+    pm = sgemv.PackedMatrix(q, s, z, device=G.torch_dev())
+    X = np.stack([synth.plain_activation(60 + m, K) for m in range(M)])
+    ts = [0.2 * m for m in range(M)]
+    xd = G.to_dev(X)
+    dev = G.torch_dev()
+    lists = [np.zeros(0, dtype=np.int32),
+             np.array([0, 1, 127, 128, 300, 640, 641, 1023, 1024, 1151], dtype=np.int32),
+             np.arange(0, K, 3, dtype=np.int32)]
+    for L in lists:
+        buf = np.full(K, 5000, dtype=np.int32)          # junk beyond the count
+        buf[:len(L)] = L
+        idx = torch.from_numpy(buf).to(dev)
+        cnt = torch.tensor([len(L)], dtype=torch.int32, device=dev)
+        for thr in (ts, None):
+            y = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+            sgemv.sgemv_run_batched(pm.desc, pm.blob, xd, thr, idx, cnt, y, pm.workspace)
+            torch.cuda.synchronize()
+            yy = y.cpu().numpy()
+            if len(L) == 0:
+                assert np.all(yy == 0) and not np.any(np.signbit(yy))
+                continue
+            if thr is None:
+                y_ref, B = oracle.gemv_listed(q, s, z, X, L)
+            else:
+                Xm = np.where(oracle.active_mask(X, ts), X, np.float16(0))
+                y_ref, B = oracle.gemv_listed(q, s, z, Xm, L)
+            G.check_y(yy, y_ref, B, f"given list len={len(L)} masked={thr is not None}")
+    # a count above K is clamped to K: every column
+    idx = torch.arange(K, dtype=torch.int32, device=dev)
+    cnt = torch.tensor([K + 100], dtype=torch.int32, device=dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    sgemv.sgemv_run_batched(pm.desc, pm.blob, xd, None, idx, cnt, y, pm.workspace)
+    torch.cuda.synchronize()
+    y_ref, B = oracle.gemv_dense(q, s, z, X)
+    G.check_y(y.cpu().numpy(), y_ref, B, "given list count > K")
