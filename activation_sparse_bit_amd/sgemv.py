@@ -206,7 +206,8 @@ def sgemv_run_batched(desc: Desc, packed, x, thresholds, idx, count, y, workspac
 def sgemv_run_fused(desc: Desc, packed, x, thresholds, y, workspace, idx=None, count=None,
                     stream=None):
     """Threshold + compact + GEMV in one launch; x is [K] or [M][ldx] with
-    M <= 2, y matches; idx/count (optional) receive the active list."""
+    M <= 16, y matches; idx/count (optional) receive the active list (the
+    union over the rows)."""
     M = 1 if x.dim() == 1 else x.shape[0]
     ldx = desc.K if x.dim() == 1 else x.stride(0)
     ldy = desc.N if y.dim() == 1 else y.stride(0)
