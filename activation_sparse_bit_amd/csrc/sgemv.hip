@@ -815,26 +815,24 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
 
 constexpr int kFsCols = kGroup;                // columns per wavefront: one quantization group
 constexpr int kFsMaxPairs = kFsCols / 16;       // column pairs per lane with every column active
-// wavefronts per workgroup (one row, two rows); a workgroup owns W groups
-template <int MT>
-struct FsCfg {
-    static constexpr int W = MT == 1 ? 8 : 8;
-    static constexpr int kSeg = W * kFsCols;    // columns per workgroup
-};
-
-template <int MT>
+constexpr int kFsW = 8;                          // wavefronts per workgroup (groups per segment)
+constexpr int kFsWSmall = 4;                     // ... for one row on small matrices
+// A workgroup of W wavefronts owns W groups (W * 128 columns) of a half
+// tile.  W = 8 in general; small matrices take W = 4 (one row), twice the
+// workgroups over the same columns, so that more CUs stream them.
+template <int MT, int W>
 struct FsShared {
-    uint32_t zc[FsCfg<MT>::W][kVTile / 2];                  // per wavefront: (1024 + z, 1024 + 16 z) of output pairs
-    __align__(16) float sc[FsCfg<MT>::W][kVTile];           // ... scale of output sp_out(l, d) at 4 l + d (1/16 folded in for odd)
-    __align__(16) int k[FsCfg<MT>::W][kFsCols];             // ... its active columns
-    __align__(16) uint16_t xs[FsCfg<MT>::W][MT][kFsCols];   // ... and their masked activations
+    uint32_t zc[W][kVTile / 2];                  // per wavefront: (1024 + z, 1024 + 16 z) of output pairs
+    __align__(16) float sc[W][kVTile];           // ... scale of output sp_out(l, d) at 4 l + d (1/16 folded in for odd)
+    __align__(16) int k[W][kFsCols];             // ... its active columns
+    __align__(16) uint16_t xs[W][MT][kFsCols];   // ... and their masked activations
 };
 
-template <int MT>
+template <int MT, int W>
 union FsLds {
     struct {
-        FsShared<MT> f;
-        SpShared<MT, FsCfg<MT>::W> sh;
+        FsShared<MT, W> f;
+        SpShared<MT, W> sh;
     } g;
     GatherShared gl;
 };
@@ -865,8 +863,8 @@ __device__ __forceinline__ void fs_pair8(uint32_t Ad, uint32_t Bd, const uint32_
 // (positions past nact repeat the first column with x = 0).  Issues all
 // 16-byte weight loads, then accumulates pair by pair as they arrive, and
 // returns in v4[m][d] the scaled sum of output sp_out(lane, d).
-template <int MT, int NP>
-__device__ __forceinline__ void fs_block(FsShared<MT>& fs, int wave, int lane, int slot, int blk, int nact,
+template <int MT, int NP, int W>
+__device__ __forceinline__ void fs_block(FsShared<MT, W>& fs, int wave, int lane, int slot, int blk, int nact,
                                          int K, const uint8_t* __restrict__ wcol, const u32x4& mdv,
                                          uint32_t z4, float (&v4)[MT][4]) {
     const int kfirst = fs.k[wave][0];
@@ -967,18 +965,18 @@ __device__ __forceinline__ void fs_block(FsShared<MT>& fs, int wave, int lane, i
     }
 }
 
-template <int MT, bool Z4>
-__device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT>& lds) {
+template <int MT, bool Z4, int W>
+__device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
     int bid = blockIdx.x;
     if (a.idx_out) {  // block 0 writes the list
         if (bid == 0) {
-            constexpr int WL = FsCfg<MT>::W >= 16 ? 16 : FsCfg<MT>::W >= 8 ? 8 : 4;
+            constexpr int WL = W >= 16 ? 16 : W >= 8 ? 8 : 4;
             gather_body<WL>(a.x, a.M, a.K, a.ldx, a.tc, a.idx_out, a.count_out, lds.gl);
             return;
         }
         --bid;
     }
-    FsShared<MT>& fs = lds.g.f;
+    FsShared<MT, W>& fs = lds.g.f;
 
     const int T = a.tiles;
     const int vt = bid % T;
@@ -989,7 +987,7 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT>& lds) {
     const int slot = lane >> 3, blk = lane & 7;
     const int K = a.K;
     const int Gk = K / kGroup;
-    const int kw = seg * FsCfg<MT>::kSeg + wave * kFsCols;  // this wavefront's first column
+    const int kw = seg * (W * kFsCols) + wave * kFsCols;  // this wavefront's first column
     const bool has = kw < K;                       // K is a multiple of 128: all of the group or none
     const int g = (has ? kw : 0) / kGroup;
 
@@ -1008,6 +1006,11 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT>& lds) {
             const int mr = m < a.M ? m : a.M - 1;
             xr[h][m] = a.x[(size_t)mr * a.ldx + (has ? kw : 0) + 64 * h + lane];
         }
+    // the group's scale/zero row (16 bytes per lane), converted after the
+    // weight loads are issued.  Loaded on every path, after the activations:
+    // loads complete in order, so the activations are then waited for
+    // without it, and the weight loads are not held back by it.
+    const u32x4 mdv = md_raw4(mdh, g, 4 * lane);
 
     // 2. threshold, rank, compact into this wavefront's LDS rows (no branch
     //    before the ballots: x is waited for on every path)
@@ -1034,10 +1037,6 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT>& lds) {
         nact += __popcll(bal);
     }
     const int np = (nact + 15) / 16;
-    // the group's scale/zero row (16 bytes per lane), only with work to do;
-    // converted after the weight loads are issued
-    u32x4 mdv = {0u, 0u, 0u, 0u};
-    if (np > 0) mdv = md_raw4(mdh, g, 4 * lane);
 #pragma unroll
     for (int h = 0; h < H; ++h) {
         if (act[h]) {
@@ -1052,33 +1051,33 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT>& lds) {
     //      pair waits only for its own loads)
     float v4[MT][4] = {};
     switch (np) {
-        case 1: fs_block<MT, 1>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
-        case 2: fs_block<MT, 2>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
-        case 3: fs_block<MT, 3>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
-        case 4: fs_block<MT, 4>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
-        case 5: fs_block<MT, 5>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
-        case 6: fs_block<MT, 6>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
-        case 7: fs_block<MT, 7>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
-        case 8: fs_block<MT, 8>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 1: fs_block<MT, 1, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 2: fs_block<MT, 2, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 3: fs_block<MT, 3, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 4: fs_block<MT, 4, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 5: fs_block<MT, 5, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 6: fs_block<MT, 6, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 7: fs_block<MT, 7, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 8: fs_block<MT, 8, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
         default: break;
     }
-    sp_finish<MT, FsCfg<MT>::W>(a, vt, seg, S, wave, lane, v4, lds.g.sh);
+    sp_finish<MT, W>(a, vt, seg, S, wave, lane, v4, lds.g.sh);
 }
 
 // Two builds of the same kernel: two wavefronts per SIMD (the whole register
 // budget, for grids of at most one workgroup per CU), and four (two
 // workgroups per CU, so that one's loads overlap the other's latency in
 // grids that take several rounds).
-template <int MT, bool Z4>
-__global__ __launch_bounds__(FsCfg<MT>::W * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fs(RunArgs a) {
-    __shared__ FsLds<MT> lds;
-    fs_body<MT, Z4>(a, lds);
+template <int MT, bool Z4, int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fs(RunArgs a) {
+    __shared__ FsLds<MT, W> lds;
+    fs_body<MT, Z4, W>(a, lds);
 }
 
 template <int MT, bool Z4>
-__global__ __launch_bounds__(FsCfg<MT>::W * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_fs4(RunArgs a) {
-    __shared__ FsLds<MT> lds;
-    fs_body<MT, Z4>(a, lds);
+__global__ __launch_bounds__(kFsW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_fs4(RunArgs a) {
+    __shared__ FsLds<MT, kFsW> lds;
+    fs_body<MT, Z4, kFsW>(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1631,6 +1630,12 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // Fused one/two-row kernel: grids of at most this many workgroups run in one
 // round (one per CU) with the two-wavefronts-per-SIMD build.
 constexpr int kFsOneRound = 256;
+// One row: below this many 8-wavefront workgroups, 4-wavefront workgroups
+// (twice as many, at most two per CU: still one round).  At decode sizes a
+// workgroup's stream is bound by how many loads one CU keeps in flight, so a
+// small matrix is read faster by more CUs; near one full round the extra
+// partial sums cost more than that gains.
+constexpr int kFsSmallGrid = 160;
 
 // The list-driven kernel, one or two rows (3 and more rows over a given list
 // run on the fused many-row kernel).
@@ -1730,11 +1735,12 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
 // The fused kernels; with all_cols every column is listed (the dense GEMV,
 // rows masked by their thresholds unless thr is NULL).
 template <bool Z4>
-void launch_fused(int M, bool one_round, dim3 grid, const RunArgs& a, hipStream_t s) {
-    if (M == 1 && one_round) hipLaunchKernelGGL((k_fs<1, Z4>), grid, dim3(FsCfg<1>::W * 64), 0, s, a);
-    else if (M == 1) hipLaunchKernelGGL((k_fs4<1, Z4>), grid, dim3(FsCfg<1>::W * 64), 0, s, a);
-    else if (M == 2 && one_round) hipLaunchKernelGGL((k_fs<2, Z4>), grid, dim3(FsCfg<2>::W * 64), 0, s, a);
-    else if (M == 2) hipLaunchKernelGGL((k_fs4<2, Z4>), grid, dim3(FsCfg<2>::W * 64), 0, s, a);
+void launch_fused(int M, int W, bool one_round, dim3 grid, const RunArgs& a, hipStream_t s) {
+    if (M == 1 && W == kFsWSmall) hipLaunchKernelGGL((k_fs<1, Z4, kFsWSmall>), grid, dim3(kFsWSmall * 64), 0, s, a);
+    else if (M == 1 && one_round) hipLaunchKernelGGL((k_fs<1, Z4, kFsW>), grid, dim3(kFsW * 64), 0, s, a);
+    else if (M == 1) hipLaunchKernelGGL((k_fs4<1, Z4>), grid, dim3(kFsW * 64), 0, s, a);
+    else if (M == 2 && one_round) hipLaunchKernelGGL((k_fs<2, Z4, kFsW>), grid, dim3(kFsW * 64), 0, s, a);
+    else if (M == 2) hipLaunchKernelGGL((k_fs4<2, Z4>), grid, dim3(kFsW * 64), 0, s, a);
     else hipLaunchKernelGGL(k_fm<Z4>, grid, dim3(fm::kWaves * 64), 0, s, a);
 }
 
@@ -1767,10 +1773,12 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     }
     a.unmasked = thr ? 0u : 1u;
     a.tiles = d->N / kVTile;
+    int W = kFsW;
     if (M <= 2) {
         a.slices = slices_for(d, M);   // stride of the partials region
-        const int seg_cols = M == 1 ? FsCfg<1>::kSeg : FsCfg<2>::kSeg;
-        a.segs = (d->K + seg_cols - 1) / seg_cols;
+        const int segs8 = (d->K + kFsW * kFsCols - 1) / (kFsW * kFsCols);
+        if (M == 1 && a.tiles * segs8 < kFsSmallGrid) W = kFsWSmall;
+        a.segs = (d->K + W * kFsCols - 1) / (W * kFsCols);
     } else {
         a.segs = (d->K + fm::kSeg - 1) / fm::kSeg;
         a.slices = a.segs;
@@ -1810,8 +1818,8 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     const dim3 grid((unsigned)(a.tiles * a.segs + a.gblocks));  // + the list's workgroups
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool one_round = a.tiles * a.segs <= kFsOneRound;
-    if (a.md_z4) launch_fused<true>(M, one_round, grid, a, s);
-    else launch_fused<false>(M, one_round, grid, a, s);
+    if (a.md_z4) launch_fused<true>(M, W, one_round, grid, a, s);
+    else launch_fused<false>(M, W, one_round, grid, a, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         g_last_hip_error = (int)e;
