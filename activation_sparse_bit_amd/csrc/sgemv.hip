@@ -1231,7 +1231,19 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
     const MdHalf mdh = md_half<Z4>(a, tt, hh);
 
-    // 1. activations: lane (row xm = lane / 4, quarter xq = lane % 4) loads
+    // 1. the group's scale/zero row (converted where it is used) and, over a
+    //    given list, its count and this group's range of it (g + 1 <= K / 128:
+    //    the table has K / 128 + 1 entries); without a list the same loads read
+    //    the activations (at least 2K >= 4 (K / 128 + 1) bytes) and are unused,
+    //    so that no path waits for them early.  Issued before the activations:
+    //    loads complete in order, and all of these are needed before the
+    //    weight loads.
+    const u32x4 mdv = md_raw4(mdh, g, 4 * lane);
+    const int32_t* lcp = a.lidx ? a.lcount : reinterpret_cast<const int32_t*>(a.x);
+    const int32_t* gsp = a.lidx ? a.gstart : reinterpret_cast<const int32_t*>(a.x);
+    const int lc = *lcp, ls0 = gsp[g], ls1 = gsp[g + 1];
+    __builtin_amdgcn_sched_barrier(0);   // keeps these loads ahead of the activations'
+    // 2. activations: lane (row xm = lane / 4, quarter xq = lane % 4) loads
     //    32 columns; rows past M read row M - 1 and are masked out
     const int xm = lane >> 2, xq = lane & 3;
     const int xmr = xm < a.M ? xm : a.M - 1;
@@ -1239,7 +1251,6 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         xv[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)xmr * a.ldx + (has ? kw : 0) + 32 * xq + 8 * i);
-    const u32x4 mdv = md_raw4(mdh, g, 4 * lane);   // converted where it is used
 
     const uint32_t code = code_of(a.tc, xmr);
     const bool row_ok = has && xm < a.M;
@@ -1269,18 +1280,23 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
         un = r32[0] | r32[1];
     }
     if (a.all_cols) un = has ? ~0u : 0u;
+    // the group's range of a given list (computed on every path, so that its
+    // loads stay beside the activations' instead of moving into the branch)
+    int lcnt = __builtin_amdgcn_readfirstlane(lc);
+    lcnt = lcnt < 0 ? 0 : (lcnt > K ? K : lcnt);
+    int lp0 = has ? __builtin_amdgcn_readfirstlane(ls0) : 0, lp1 = has ? __builtin_amdgcn_readfirstlane(ls1) : 0;
+    lp0 = lp0 < 0 ? 0 : (lp0 > lcnt ? lcnt : lp0);
+    lp1 = lp1 < lp0 ? lp0 : (lp1 > lcnt ? lcnt : lp1);
+    lp1 = lp1 - lp0 > fm::kCols ? lp0 + fm::kCols : lp1;
     if (a.lidx) {  // a given list: the group's entries are the union (the rows stay masked by t)
         if (lane < 4) fw.lm[lane] = 0u;
         __builtin_amdgcn_wave_barrier();
-        int c = __builtin_amdgcn_readfirstlane(*a.lcount);
-        c = c < 0 ? 0 : (c > K ? K : c);
-        int s0 = has ? a.gstart[g] : 0, s1 = has ? a.gstart[g + 1] : 0;
-        s0 = s0 < 0 ? 0 : (s0 > c ? c : s0);
-        s1 = s1 < s0 ? s0 : (s1 > c ? c : s1);
-        s1 = s1 - s0 > fm::kCols ? s0 + fm::kCols : s1;
-        for (int e = lane; e < s1 - s0; e += 64) {
-            const int cc = a.lidx[s0 + e] - kw;
-            if ((unsigned)cc < (unsigned)fm::kCols) atomicOr(&fw.lm[cc >> 5], 1u << (cc & 31));
+        const int n = lp1 - lp0;   // at most 128 entries: two per lane, both loads in flight
+        if (n > 0) {
+            const int e0 = lane < n ? lane : n - 1, e1 = lane + 64 < n ? lane + 64 : n - 1;
+            const int c0 = a.lidx[lp0 + e0] - kw, c1 = a.lidx[lp0 + e1] - kw;
+            if (lane < n && (unsigned)c0 < (unsigned)fm::kCols) atomicOr(&fw.lm[c0 >> 5], 1u << (c0 & 31));
+            if (lane + 64 < n && (unsigned)c1 < (unsigned)fm::kCols) atomicOr(&fw.lm[c1 >> 5], 1u << (c1 & 31));
         }
         __builtin_amdgcn_wave_barrier();
         un = fw.lm[lane & 3];  // word q at lane q, as the union above
