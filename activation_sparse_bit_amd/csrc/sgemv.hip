@@ -12,8 +12,6 @@
 //   k_gather   one 1024-thread workgroup: per-lane 8-element masks from
 //              16-byte loads, wavefront ballots and mbcnt for in-wave ranks,
 //              an LDS scan across the 16 wavefronts, ordered index writes.
-//   k_gstart   where each quantization group's entries start in a given
-//              list (for the many-row kernel over that list).
 //   k_sp       one or two rows over a given list: every wavefront takes 32
 //              list positions of one half tile (256 outputs) and loads them
 //              at once with 16-byte loads that cover 8 listed columns per
@@ -82,7 +80,6 @@ struct RunArgs {
     uint32_t* gsync;         // ... [0]: arrival counter, [16 + j]: length of list j
     const int32_t* lidx;     // many-row fused kernel over a given list (NULL: the list is computed)
     const int32_t* lcount;   // ... its length
-    const int32_t* gstart;   // ... position of each group's first entry ([K/128 + 1], k_gstart)
 };
 
 __device__ __forceinline__ uint32_t code_of(const Codes& c, int m) {
@@ -226,34 +223,6 @@ __global__ __launch_bounds__(1024) void k_gather(const uint16_t* __restrict__ x,
                                                  int32_t* __restrict__ count) {
     __shared__ GatherShared gs;
     gather_body<16>(x, M, K, ldx, tc, idx, count, gs);
-}
-
-// Start of each quantization group's entries in an ascending list:
-// start[g] = the first position whose column is >= 128 g, start[K/128] =
-// count.  Thread p compares entries p - 1 and p and writes the starts of the
-// groups in between, so every entry is written for an ascending list (one
-// that is not gives wrong starts, never a stray access; the readers clamp).
-__global__ __launch_bounds__(256) void k_gstart(const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
-                                                int K, int32_t* __restrict__ start) {
-    const int Gk = K / kGroup;
-    int c = *count;
-    c = c < 0 ? 0 : (c > K ? K : c);
-    const int p = blockIdx.x * 256 + threadIdx.x;
-    if (c == 0) {
-        for (int s = p; s <= Gk; s += gridDim.x * 256) start[s] = 0;
-        return;
-    }
-    if (p >= c) return;
-    auto grp = [&](int q) {
-        int k = idx[q];
-        k = k < 0 ? 0 : (k >= K ? K - 1 : k);
-        return k / kGroup;
-    };
-    const int g = grp(p);
-    const int gp = p > 0 ? grp(p - 1) : -1;
-    for (int s = gp + 1; s <= g; ++s) start[s] = p;
-    if (p == c - 1)
-        for (int s = g + 1; s <= Gk; ++s) start[s] = c;
 }
 
 // ---------------------------------------------------------------------------
@@ -687,7 +656,6 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
     const int lane = threadIdx.x & 63;
     const int slot = lane >> 3, blk = lane & 7;
     const int K = a.K;
-    const int Gk = K / kGroup;
     const int P0 = slice * sp::kPos;
     const int j0 = P0 + wave * sp::kCh;   // this wavefront's chunk
 
@@ -793,19 +761,20 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
 // fused threshold + compact + sparse GEMV (one or two rows)
 // ---------------------------------------------------------------------------
 //
-// Workgroup (half tile vt, segment seg) owns columns seg * 512 ..
-// seg * 512 + 511, and its wavefront w the 64 columns seg * 512 + 64 w ..,
-// which lie in one quantization group.  Every wavefront works on its own
-// until the final sums, with no workgroup barrier:
-//   1. it loads its 64 activations (one per lane and row) and its group's
+// Workgroup (half tile vt, segment seg) of W wavefronts owns the W groups
+// seg * W .. seg * W + W - 1, and its wavefront w the 128 columns of group
+// seg * W + w.  Every wavefront works on its own until the final sums, with
+// no workgroup barrier:
+//   1. it loads its 128 activations (two per lane and row), then its group's
 //      scale/zero row for the half tile (16 bytes per lane);
-//   2. thresholds them, ranks the active lanes with a ballot and mbcnt, and
+//   2. thresholds them, ranks the active lanes with ballots and mbcnt, and
 //      writes the active columns and their masked activations to its own
-//      LDS rows, beside the converted (1024 + z | s) pairs;
+//      LDS rows;
 //   3. splits its n active columns over the 8 slots, ceil(n / 16) column
 //      pairs per lane, and issues all their 16-byte weight loads at once;
-//   4. dequantizes and accumulates per lane (one group: the scale is applied
-//      once per output), and sums the slots with lane swaps.
+//   4. converts the scale/zero row, dequantizes and accumulates per lane (one
+//      group: the scale is applied once per output), and sums the slots with
+//      lane swaps.
 // The workgroup then sums its wavefronts, and the segments of a half tile
 // are added as slices (as in the list-driven kernel).
 //
@@ -814,7 +783,6 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
 // activations.
 
 constexpr int kFsCols = kGroup;                // columns per wavefront: one quantization group
-constexpr int kFsMaxPairs = kFsCols / 16;       // column pairs per lane with every column active
 constexpr int kFsW = 8;                          // wavefronts per workgroup (groups per segment)
 constexpr int kFsWSmall = 4;                     // ... for one row on small matrices
 // A workgroup of W wavefronts owns W groups (W * 128 columns) of a half
@@ -986,7 +954,6 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
     const int lane = threadIdx.x & 63;
     const int slot = lane >> 3, blk = lane & 7;
     const int K = a.K;
-    const int Gk = K / kGroup;
     const int kw = seg * (W * kFsCols) + wave * kFsCols;  // this wavefront's first column
     const bool has = kw < K;                       // K is a multiple of 128: all of the group or none
     const int g = (has ? kw : 0) / kGroup;
@@ -1119,6 +1086,10 @@ constexpr int kSeg = kWaves * kCols;     // columns per workgroup
 constexpr int kRows = 16;                // batch rows (the MFMA's N), padded with zeros
 constexpr int kCh = 32;                  // listed columns per MFMA step (its K)
 constexpr int kMaxCh = kCols / kCh;
+// Over a given list: entries read per lane per round (all in flight).  The
+// window searched for a group holds at most ceil(count / 64) + 128 entries,
+// so one round of 6 covers every count up to 16384.
+constexpr int kListLoads = 6;
 constexpr int kOutFloats = kRows * kVTile;   // one workgroup's sums
 // LDS row strides, padded so that the 16-byte tile writes, the transposing
 // reads and the row-wise accesses spread over the banks
@@ -1221,7 +1192,6 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int K = a.K;
-    const int Gk = K / kGroup;
     const int kw = seg * fm::kSeg + wave * fm::kCols;
     const bool has = kw < K;                       // K is a multiple of 128: the whole group or none
     const int g = (has ? kw : 0) / kGroup;
@@ -1232,16 +1202,12 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     const MdHalf mdh = md_half<Z4>(a, tt, hh);
 
     // 1. the group's scale/zero row (converted where it is used) and, over a
-    //    given list, its count and this group's range of it (g + 1 <= K / 128:
-    //    the table has K / 128 + 1 entries); without a list the same loads read
-    //    the activations (at least 2K >= 4 (K / 128 + 1) bytes) and are unused,
-    //    so that no path waits for them early.  Issued before the activations:
-    //    loads complete in order, and all of these are needed before the
-    //    weight loads.
+    //    given list, its length (without a list the same load reads the
+    //    activations and is unused, so that no path waits for it early).
+    //    Issued before the activations: loads complete in order, and both are
+    //    needed before the weight loads.
     const u32x4 mdv = md_raw4(mdh, g, 4 * lane);
-    const int32_t* lcp = a.lidx ? a.lcount : reinterpret_cast<const int32_t*>(a.x);
-    const int32_t* gsp = a.lidx ? a.gstart : reinterpret_cast<const int32_t*>(a.x);
-    const int lc = *lcp, ls0 = gsp[g], ls1 = gsp[g + 1];
+    const int lc = *(a.lidx ? a.lcount : reinterpret_cast<const int32_t*>(a.x));
     __builtin_amdgcn_sched_barrier(0);   // keeps these loads ahead of the activations'
     // 2. activations: lane (row xm = lane / 4, quarter xq = lane % 4) loads
     //    32 columns; rows past M read row M - 1 and are masked out
@@ -1280,23 +1246,35 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
         un = r32[0] | r32[1];
     }
     if (a.all_cols) un = has ? ~0u : 0u;
-    // the group's range of a given list (computed on every path, so that its
-    // loads stay beside the activations' instead of moving into the branch)
-    int lcnt = __builtin_amdgcn_readfirstlane(lc);
-    lcnt = lcnt < 0 ? 0 : (lcnt > K ? K : lcnt);
-    int lp0 = has ? __builtin_amdgcn_readfirstlane(ls0) : 0, lp1 = has ? __builtin_amdgcn_readfirstlane(ls1) : 0;
-    lp0 = lp0 < 0 ? 0 : (lp0 > lcnt ? lcnt : lp0);
-    lp1 = lp1 < lp0 ? lp0 : (lp1 > lcnt ? lcnt : lp1);
-    lp1 = lp1 - lp0 > fm::kCols ? lp0 + fm::kCols : lp1;
     if (a.lidx) {  // a given list: the group's entries are the union (the rows stay masked by t)
         if (lane < 4) fw.lm[lane] = 0u;
         __builtin_amdgcn_wave_barrier();
-        const int n = lp1 - lp0;   // at most 128 entries: two per lane, both loads in flight
-        if (n > 0) {
-            const int e0 = lane < n ? lane : n - 1, e1 = lane + 64 < n ? lane + 64 : n - 1;
-            const int c0 = a.lidx[lp0 + e0] - kw, c1 = a.lidx[lp0 + e1] - kw;
-            if (lane < n && (unsigned)c0 < (unsigned)fm::kCols) atomicOr(&fw.lm[c0 >> 5], 1u << (c0 & 31));
-            if (lane + 64 < n && (unsigned)c1 < (unsigned)fm::kCols) atomicOr(&fw.lm[c1 >> 5], 1u << (c1 & 31));
+        int c = __builtin_amdgcn_readfirstlane(lc);
+        c = c < 0 ? 0 : (c > K ? K : c);
+        if (has && c > 0) {
+            // 64 evenly spaced samples of the ascending list: those below the
+            // group's first column are a prefix of the lanes, nlo of them
+            const int step = (c + 63) / 64;
+            const int sv = a.lidx[lane * step < c ? lane * step : c - 1];
+            const int nlo = __popcll(__ballot(sv < kw));
+            // the group's entries (at most 128) lie after sample nlo - 1 and
+            // start at or before sample nlo: positions [ws, we)
+            const int ws = nlo > 0 ? (nlo - 1) * step : 0;
+            const int we = nlo * step + fm::kCols < c ? nlo * step + fm::kCols : c;
+            for (int b = ws; b < we; b += 64 * fm::kListLoads) {
+                int v[fm::kListLoads];
+#pragma unroll
+                for (int i = 0; i < fm::kListLoads; ++i) {   // all in flight, then the bits
+                    const int pos = b + 64 * i + lane;
+                    v[i] = a.lidx[pos < we ? pos : we - 1];
+                }
+#pragma unroll
+                for (int i = 0; i < fm::kListLoads; ++i) {
+                    const int cc = v[i] - kw;
+                    if (b + 64 * i + lane < we && (unsigned)cc < (unsigned)fm::kCols)
+                        atomicOr(&fw.lm[cc >> 5], 1u << (cc & 31));
+                }
+            }
         }
         __builtin_amdgcn_wave_barrier();
         un = fw.lm[lane & 3];  // word q at lane q, as the union above
@@ -1613,13 +1591,7 @@ size_t ws_counters_bytes(int tiles) { return (size_t)tiles * kCounterStride * 4;
 
 // The many-row fused call's list workgroups: a 256-byte line (their arrival
 // counter and list lengths), then a K-entry scratch list.
-size_t ws_gather_bytes(const sgemv_desc* d) {
-    return 256 + ((size_t)d->K * 4 + 255) / 256 * 256 + ((size_t)(d->K / kGroup + 1) * 4 + 255) / 256 * 256;
-}
-int32_t* ws_gstart(const sgemv_desc* d, void* ws) {   // the group starts of a given list
-    return reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + ws_counters_bytes(d->N / kVTile) + 256 +
-                                      ((size_t)d->K * 4 + 255) / 256 * 256);
-}
+size_t ws_gather_bytes(const sgemv_desc* d) { return 256 + ((size_t)d->K * 4 + 255) / 256 * 256; }
 
 // Workspace: counters, the list workgroups' region, then the partial sums
 // (whose size depends on the largest batch).
@@ -1687,23 +1659,8 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
     if (count && !aligned(count, 4)) return SGEMV_EALIGN;
     if (!idx)   // every column: the fused kernels with the whole list, which stream faster
         return run_fused(d, packed, x, M, ldx, thr, nullptr, nullptr, y, ldy, flags, ws, stream, true);
-    if (M > 2) {  // 3..16 rows over a given list: its group starts, then the many-row fused kernel
-        if (thr) {  // every argument is checked before the first launch
-            Codes c;
-            st = fill_codes(thr, M, c);
-            if (st) return st;
-        }
-        if (!ws) return SGEMV_EINVAL;
-        if (!aligned(ws, 256)) return SGEMV_EALIGN;
-        hipLaunchKernelGGL(k_gstart, dim3((unsigned)((d->K + 255) / 256)), dim3(256), 0,
-                           static_cast<hipStream_t>(stream), idx, count, (int)d->K, ws_gstart(d, ws));
-        const hipError_t e0 = hipGetLastError();
-        if (e0 != hipSuccess) {
-            g_last_hip_error = (int)e0;
-            return SGEMV_EHIP;
-        }
+    if (M > 2)  // 3..16 rows over a given list: the many-row fused kernel reads the list itself
         return run_fused(d, packed, x, M, ldx, thr, nullptr, nullptr, y, ldy, flags, ws, stream, false, idx, count);
-    }
 
     const int mt = pow2_ceil(M);
     RunArgs a;
@@ -1781,11 +1738,9 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
         if (st) return st;
     }
     a.all_cols = all_cols ? 1u : 0u;
-    if (lidx) {   // list mode (many rows): the group starts, written by k_gstart before
-        if (!ws) return SGEMV_EINVAL;
+    if (lidx) {   // list mode (many rows)
         a.lidx = lidx;
         a.lcount = lcount;
-        a.gstart = ws_gstart(d, ws);
     }
     a.unmasked = thr ? 0u : 1u;
     a.tiles = d->N / kVTile;
@@ -1891,7 +1846,6 @@ extern "C" int sgemv_run_batched(const sgemv_desc* d, const void* packed, const 
 
 extern "C" size_t sgemv_workspace_bytes(const sgemv_desc* d, int32_t M) {
     if (check_desc(d) != SGEMV_OK || M < 1 || M > SGEMV_MAX_BATCH) return 0;
-    const int tiles = d->N / kVTile;
     size_t part = 0;  // enough for every call with up to M rows
     for (int mt = 1; mt <= (M < 2 ? M : 2); ++mt) {   // the list-driven kernel's rows
         const size_t b = ws_partial_bytes(d, mt);
