@@ -373,3 +373,28 @@ def test_run_batched_given_list_edges():
     torch.cuda.synchronize()
     y_ref, B = oracle.gemv_dense(q, s, z, X)
     G.check_y(y.cpu().numpy(), y_ref, B, "given list count > K")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("K,keep", [(28672, 0.95), (65536, 0.6), (65536, 0.002)])
+def test_run_batched_given_list_long(K, keep):
+    """3+ rows over a long given list: the window searched for each group
+    spans several rounds of loads when the count is above 16384, and a
+    near-empty list leaves most groups with no entry."""
+    from activation_sparse_bit_amd import sgemv
+    N, M = 512, 4
+    q, s, z = synth.random_int4_problem(int(K * keep) + 5, N, K)
+    pm = sgemv.PackedMatrix(q, s, z, device=G.torch_dev())
+    X = np.stack([synth.plain_activation(90 + m, K) for m in range(M)])
+    rng = np.random.default_rng(K)
+    L = np.flatnonzero(rng.random(K) < keep).astype(np.int32)
+    dev = G.torch_dev()
+    buf = np.full(K, -3, dtype=np.int32)
+    buf[:len(L)] = L
+    idx = torch.from_numpy(buf).to(dev)
+    cnt = torch.tensor([len(L)], dtype=torch.int32, device=dev)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    sgemv.sgemv_run_batched(pm.desc, pm.blob, G.to_dev(X), None, idx, cnt, y, pm.workspace)
+    torch.cuda.synchronize()
+    y_ref, B = oracle.gemv_listed(q, s, z, X, L)
+    G.check_y(y.cpu().numpy(), y_ref, B, f"long given list K={K} count={len(L)}")
