@@ -826,37 +826,14 @@ __device__ __forceinline__ void fs_pair8(uint32_t Ad, uint32_t Bd, const uint32_
     }
 }
 
-// A wavefront's nact active columns (nact <= 64, in its LDS rows) as NP
-// column pairs per lane: slot c takes positions 2 NP c .. 2 NP c + 2 NP - 1
-// (positions past nact repeat the first column with x = 0).  Issues all
-// 16-byte weight loads, then accumulates pair by pair as they arrive, and
+// The weights' arithmetic of a wavefront's NP column pairs per lane (their
+// loads issued by the caller, x pairs in xp): converts the group's scale/zero
+// row, dequantizes and accumulates pair by pair as the loads arrive, and
 // returns in v4[m][d] the scaled sum of output sp_out(lane, d).
 template <int MT, int NP, int W>
-__device__ __forceinline__ void fs_block(FsShared<MT, W>& fs, int wave, int lane, int slot, int blk, int nact,
-                                         int K, const uint8_t* __restrict__ wcol, const u32x4& mdv,
-                                         uint32_t z4, float (&v4)[MT][4]) {
-    const int kfirst = fs.k[wave][0];
-    int kk[2 * NP];
-    uint32_t xp[NP][MT];
-    u32x4 w[2 * NP];
-#pragma unroll
-    for (int pr = 0; pr < NP; ++pr) {
-        const int p = 2 * NP * slot + 2 * pr;          // even, below kFsCols: 8-byte aligned pairs
-        const int2 k2 = *reinterpret_cast<const int2*>(&fs.k[wave][p]);
-        const bool ok0 = p < nact, ok1 = p + 1 < nact;
-        const int k0 = ok0 ? k2.x : kfirst, k1 = ok1 ? k2.y : kfirst;
-        kk[2 * pr] = (unsigned)k0 < (unsigned)K ? k0 : K - 1;
-        kk[2 * pr + 1] = (unsigned)k1 < (unsigned)K ? k1 : K - 1;
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const uint32_t x2 = *reinterpret_cast<const uint32_t*>(&fs.xs[wave][m][p]);
-            xp[pr][m] = (ok0 ? (x2 & 0xFFFFu) : 0u) | (ok1 ? (x2 & 0xFFFF0000u) : 0u);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < 2 * NP; ++j)
-        w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wcol + (size_t)kk[j] * (2 * kHalfRun)) + blk);
-
+__device__ __forceinline__ void fs_compute(FsShared<MT, W>& fs, int wave, int lane, int blk, const u32x4 (&w)[2 * NP],
+                                           const uint32_t (&xp)[NP][MT], const u32x4& mdv, uint32_t z4,
+                                           float (&v4)[MT][4]) {
     {
         // the group row: lane l holds outputs 4l .. 4l + 3; zero codes as two
         // (even, odd) pairs, scales at the lane and sum that will own them
@@ -933,6 +910,83 @@ __device__ __forceinline__ void fs_block(FsShared<MT, W>& fs, int wave, int lane
     }
 }
 
+// A wavefront's nact active columns (nact <= 128, in its LDS rows) as NP
+// column pairs per lane: slot c takes positions 2 NP c .. 2 NP c + 2 NP - 1
+// (positions past nact repeat the first column with x = 0).  Issues the
+// group's scale/zero row and all 16-byte weight loads, then accumulates pair
+// by pair as they arrive, and returns in v4[m][d] the scaled sum of output
+// sp_out(lane, d).
+template <int MT, int NP, int W>
+__device__ __forceinline__ void fs_block(FsShared<MT, W>& fs, int wave, int lane, int slot, int blk, int nact,
+                                         int K, const uint8_t* __restrict__ wcol, const MdHalf& mdh, int g,
+                                         float (&v4)[MT][4]) {
+    const int kfirst = fs.k[wave][0];
+    int kk[2 * NP];
+    uint32_t xp[NP][MT];
+    u32x4 w[2 * NP];
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+        const int p = 2 * NP * slot + 2 * pr;          // even, below kFsCols: 8-byte aligned pairs
+        const int2 k2 = *reinterpret_cast<const int2*>(&fs.k[wave][p]);
+        const bool ok0 = p < nact, ok1 = p + 1 < nact;
+        const int k0 = ok0 ? k2.x : kfirst, k1 = ok1 ? k2.y : kfirst;
+        kk[2 * pr] = (unsigned)k0 < (unsigned)K ? k0 : K - 1;
+        kk[2 * pr + 1] = (unsigned)k1 < (unsigned)K ? k1 : K - 1;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint32_t x2 = *reinterpret_cast<const uint32_t*>(&fs.xs[wave][m][p]);
+            xp[pr][m] = (ok0 ? (x2 & 0xFFFFu) : 0u) | (ok1 ? (x2 & 0xFFFF0000u) : 0u);
+        }
+    }
+    // the scale/zero row just before the weights (loads complete in order,
+    // and it is converted first); loading it here keeps it out of the
+    // registers of the compaction
+    const u32x4 mdv = md_raw4(mdh, g, 4 * lane);
+#pragma unroll
+    for (int j = 0; j < 2 * NP; ++j)
+        w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wcol + (size_t)kk[j] * (2 * kHalfRun)) + blk);
+
+    fs_compute<MT, NP, W>(fs, wave, lane, blk, w, xp, mdv, mdh.z4, v4);
+}
+
+// Every column of the wavefront's group (the dense GEMV): no thresholding
+// pass and no compaction, so the activation pairs, the scale/zero row and all
+// 16 weight loads per lane go out at once, in that order (loads complete in
+// order).  Rows are masked by their thresholds unless the call is unmasked.
+template <int MT, int W>
+__device__ __forceinline__ void fs_dense(const RunArgs& a, FsShared<MT, W>& fs, int wave, int lane, int slot, int blk,
+                                         int kw, const uint8_t* __restrict__ wcol, const MdHalf& mdh, int g,
+                                         float (&v4)[MT][4]) {
+    constexpr int NP = kFsCols / 16;        // 8 column pairs per lane
+    const int k0 = kw + 2 * NP * slot;      // the lane's 16 consecutive columns
+    uint32_t xp[NP][MT];
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int mr = m < a.M ? m : a.M - 1;
+            xp[pr][m] = *reinterpret_cast<const uint32_t*>(a.x + (size_t)mr * a.ldx + k0 + 2 * pr);
+        }
+    const u32x4 mdv = md_raw4(mdh, g, 4 * lane);
+    u32x4 w[2 * NP];
+#pragma unroll
+    for (int j = 0; j < 2 * NP; ++j)
+        w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wcol + (size_t)(k0 + j) * (2 * kHalfRun)) + blk);
+    if (!a.unmasked) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint32_t code = code_of(a.tc, m < a.M ? m : a.M - 1);
+#pragma unroll
+            for (int pr = 0; pr < NP; ++pr) {
+                const uint32_t v = xp[pr][m];
+                xp[pr][m] = (is_active(v & 0xFFFFu, code) ? (v & 0xFFFFu) : 0u) |
+                            (is_active(v >> 16, code) ? (v & 0xFFFF0000u) : 0u);
+            }
+        }
+    }
+    fs_compute<MT, NP, W>(fs, wave, lane, blk, w, xp, mdv, mdh.z4, v4);
+}
+
 template <int MT, bool Z4, int W>
 __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
     int bid = blockIdx.x;
@@ -962,6 +1016,13 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
     const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
     const MdHalf mdh = md_half<Z4>(a, tt, hh);
 
+    if (a.all_cols) {  // every column listed: the dense path
+        float v4[MT][4] = {};
+        if (has) fs_dense<MT, W>(a, fs, wave, lane, slot, blk, kw, wcol, mdh, g, v4);
+        sp_finish<MT, W>(a, vt, seg, S, wave, lane, v4, lds.g.sh);
+        return;
+    }
+
     // 1. activations (two per lane and row; a wavefront past K reads its
     //    first columns and ignores them, so the loads are unconditional)
     constexpr int H = kFsCols / 64;
@@ -973,11 +1034,6 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
             const int mr = m < a.M ? m : a.M - 1;
             xr[h][m] = a.x[(size_t)mr * a.ldx + (has ? kw : 0) + 64 * h + lane];
         }
-    // the group's scale/zero row (16 bytes per lane), converted after the
-    // weight loads are issued.  Loaded on every path, after the activations:
-    // loads complete in order, so the activations are then waited for
-    // without it, and the weight loads are not held back by it.
-    const u32x4 mdv = md_raw4(mdh, g, 4 * lane);
 
     // 2. threshold, rank, compact into this wavefront's LDS rows (no branch
     //    before the ballots: x is waited for on every path)
@@ -1018,14 +1074,14 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
     //      pair waits only for its own loads)
     float v4[MT][4] = {};
     switch (np) {
-        case 1: fs_block<MT, 1, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
-        case 2: fs_block<MT, 2, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
-        case 3: fs_block<MT, 3, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
-        case 4: fs_block<MT, 4, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
-        case 5: fs_block<MT, 5, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
-        case 6: fs_block<MT, 6, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
-        case 7: fs_block<MT, 7, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
-        case 8: fs_block<MT, 8, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdv, mdh.z4, v4); break;
+        case 1: fs_block<MT, 1, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdh, g, v4); break;
+        case 2: fs_block<MT, 2, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdh, g, v4); break;
+        case 3: fs_block<MT, 3, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdh, g, v4); break;
+        case 4: fs_block<MT, 4, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdh, g, v4); break;
+        case 5: fs_block<MT, 5, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdh, g, v4); break;
+        case 6: fs_block<MT, 6, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdh, g, v4); break;
+        case 7: fs_block<MT, 7, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdh, g, v4); break;
+        case 8: fs_block<MT, 8, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdh, g, v4); break;
         default: break;
     }
     sp_finish<MT, W>(a, vt, seg, S, wave, lane, v4, lds.g.sh);
