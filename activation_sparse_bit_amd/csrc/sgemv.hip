@@ -17,9 +17,10 @@
 //              at once with 16-byte loads that cover 8 listed columns per
 //              instruction.
 //   k_fs, k_fs4  one or two rows, fused: threshold, compaction and GEMV in
-//              one launch, one quantization group per wavefront (k_fs4: the
-//              128-register build for grids of several rounds); with every
-//              column listed, also the dense GEMV.
+//              one launch, one quantization group per wavefront, 8 or (one
+//              row, small or short-K matrices) 4 wavefronts per workgroup
+//              (k_fs4: the 8-wavefront build for grids of several rounds);
+//              with every column listed, also the dense GEMV (no compaction).
 //   k_fm       3 to 16 rows, fused (or over a given list): the union of the
 //              rows' active columns, exact fp16 dequantization in registers
 //              and v_mfma_f32_16x16x32_f16 on the matrix cores.
