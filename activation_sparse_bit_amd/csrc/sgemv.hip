@@ -12,10 +12,6 @@
 //   k_gather   one 1024-thread workgroup: per-lane 8-element masks from
 //              16-byte loads, wavefront ballots and mbcnt for in-wave ranks,
 //              an LDS scan across the 16 wavefronts, ordered index writes.
-//   k_sp       one or two rows over a given list: every wavefront takes 32
-//              list positions of one half tile (256 outputs) and loads them
-//              at once with 16-byte loads that cover 8 listed columns per
-//              instruction.
 //   k_fs, k_fs4  one or two rows, fused: threshold, compaction and GEMV in
 //              one launch, one quantization group per wavefront, 8 or (one
 //              row, small or short-K matrices) 4 wavefronts per workgroup
@@ -60,11 +56,9 @@ struct RunArgs {
     const uint8_t* md;       // metadata region (layout version 1 or 2)
     uint32_t md_z4;          // version 2: fp16 scales, then 4-bit zero-points
     const uint16_t* x;       // fp16 bits [M][ldx]
-    const int32_t* idx;      // listed columns (unused when dense)
-    const int32_t* count;    // number of listed columns (device)
     void* y;
     uint32_t* counters;      // one arrival counter per half tile, kCounterStride words apart
-    float* partials;         // [tile][slice][Mt][512] slice sums
+    float* partials;         // [half tile][segment][M][256] segment sums
     uint32_t partial_bytes;  // size of the partials region
     int32_t K, ldx, ldy, M;
     int32_t tiles, slices;
@@ -79,7 +73,7 @@ struct RunArgs {
     int32_t grange;          // ... columns per such workgroup (a multiple of 128)
     int32_t* gscratch;       // ... their lists, at the first column of each range ([K])
     uint32_t* gsync;         // ... [0]: arrival counter, [16 + j]: length of list j
-    const int32_t* lidx;     // many-row fused kernel over a given list (NULL: the list is computed)
+    const int32_t* lidx;     // fused kernels over a given list (NULL: the list is computed)
     const int32_t* lcount;   // ... its length
 };
 
@@ -232,9 +226,9 @@ __global__ __launch_bounds__(1024) void k_gather(const uint16_t* __restrict__ x,
 //
 // Every kernel works on half tiles: a workgroup owns 256 outputs, one half
 // of a 512-output layout tile, whose part of every column run is 128
-// contiguous bytes (one cache line).  The list-driven kernel (one or two
-// rows over a given list), the fused one- and two-row kernels and the fused
-// many-row kernel each describe their work split below.
+// contiguous bytes (one cache line).  The one- and two-row kernel and the
+// many-row kernel each describe their work split below; both also run over
+// a list the caller gives, which they search for each group's entries.
 //
 // Arithmetic.  For two listed columns a, b the two 4-bit codes of one output
 // are placed in the low mantissa bits of 0x6400 (= 1024.0 in fp16), which
@@ -277,9 +271,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // the layout: version 1 holds one (s, z) pair of fp16 bit patterns per output
 // and group (kTileN * 4 bytes per tile and group); version 2 holds the fp16
 // scales, then the integer zero-points as 4-bit codes, two per byte
-// (kTileN * 5 / 2 bytes).  md_words4 returns the version-1 words
-// (s bits | z bits << 16) of outputs o .. o + 3 (o a multiple of 4) either
-// way, so the kernels after it are the same for both.
+// (kTileN * 5 / 2 bytes).  md_raw4 loads the 16 bytes per lane of outputs
+// o .. o + 3 (o a multiple of 4) and md_cook4 turns them into the version-1
+// words (s bits | z bits << 16) either way, so the kernels after it are the
+// same for both.
 struct MdHalf {
     const uint8_t* tile;   // the tile's metadata (group 0)
     uint32_t h;            // which half of the tile
@@ -320,7 +315,6 @@ __device__ __forceinline__ u32x4 md_cook4(const u32x4& r, uint32_t z4) {
                    (r.y & 0xFFFFu) | (zb << 16), (r.y >> 16) | (zb & 0xFFFF0000u)};
 }
 
-__device__ __forceinline__ u32x4 md_words4(const MdHalf& m, int g, int o) { return md_cook4(md_raw4(m, g, o), m.z4); }
 
 // Wavefronts per workgroup: two per SIMD for few rows; four in all for
 // many rows, whose accumulators fill the register file.
@@ -331,7 +325,7 @@ __device__ __forceinline__ uint32_t and_or(uint32_t r, uint32_t mask, uint32_t v
 }
 
 // ---------------------------------------------------------------------------
-// sparse / dense GEMV for one or two rows
+// pieces shared by the one- and two-row kernels
 // ---------------------------------------------------------------------------
 //
 // Memory first.  Listed columns are scattered 128-byte runs (one per half
@@ -341,36 +335,15 @@ __device__ __forceinline__ uint32_t and_or(uint32_t r, uint32_t mask, uint32_t v
 // HBM limit.  So each lane reads 16 bytes of one column: lane
 // (c = lane / 8, o = lane % 8) reads bytes 16 o .. 16 o + 15 of the half
 // tile's run of its columns, which hold its 32 outputs 32 o .. 32 o + 31,
-// and one load instruction covers 8 listed columns.
-//
-// Work split.  A decode-time product is small next to the GPU (at 50 %
-// sparsity a 14336 -> 4096 matrix is about one 32-position chunk per
-// wavefront of the whole chip), so every wavefront takes exactly one chunk
-// of 32 list positions of one half tile and issues all its loads at once:
-// slot c owns positions 4c .. 4c + 3 (two column pairs for v_dot2).  A
-// workgroup of 8 wavefronts covers 256 consecutive positions; a half tile
-// has as many workgroups (slices) as its list needs, the rest of the grid,
-// sized for a full list, exits at once.
-//
-// Metadata.  The workgroup stages the scale/zero rows of the groups its
-// positions touch in LDS as (1024 + z | s) fp16 pairs (1024 + 16 z for odd
-// outputs).  Those loads are issued before the weight loads, so waiting for
-// them never waits for weights.  A lane handles its 4 positions group by
-// group (a ballot-driven loop, normally one pass), reading that group's
-// pairs for 8 of its outputs at a time.
+// and one load instruction covers 8 listed columns (slot c takes column
+// pairs, for v_dot2).
 //
 // Sums.  The 8 slots of an output are combined by a fixed reduce-scatter
-// butterfly across lanes (each lane ends with 4 outputs), wavefronts by a
-// fixed-order LDS tree, slices as in the kernel above: bitwise reproducible.
+// butterfly across lanes (each lane ends with 4 outputs), wavefronts by one
+// LDS pass, the segments of a half tile by the last workgroup to arrive, in
+// segment order: bitwise reproducible.
 
-namespace sp {
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kCh = 32;                  // list positions per wavefront and chunk
-constexpr int kPos = kWaves * kCh;       // list positions per workgroup (list-driven kernel)
-constexpr int kGCap = 24;                // scale/zero rows staged in LDS (list-driven kernel)
-constexpr int kOut = 32;                 // outputs per lane while computing
-}  // namespace sp
+constexpr int kLaneOut = 32;   // outputs per lane while computing
 
 __device__ __forceinline__ float u2f(uint32_t v) { return __uint_as_float(v); }
 __device__ __forceinline__ uint32_t f2u(float v) { return __float_as_uint(v); }
@@ -404,151 +377,6 @@ __device__ __forceinline__ float sp_reduce8(const float (&v)[8], int lane) {
     const float send = b3 ? t2[0] : t2[1];
     const float keep = b3 ? t2[1] : t2[0];
     return keep + u2f(__builtin_amdgcn_update_dpp(0u, f2u(send), 0x128 /* row_ror:8 */, 0xF, 0xF, false));
-}
-
-// (1024 + z | s) pair of an output from its stored (s | z) word; odd outputs
-// (high nibbles) use 1024 + 16 z.
-__device__ __forceinline__ uint32_t sp_zc(uint32_t sz_word, int odd) {
-    const half2_t sz = as_h2(sz_word);
-    const _Float16 zc = odd ? (_Float16)(sz.y * (_Float16)16.0f + (_Float16)1024.0f)
-                            : (_Float16)(sz.y + (_Float16)1024.0f);
-    return __builtin_bit_cast(uint32_t, (half2_t){zc, sz.x});
-}
-
-// Pairs (1024 + z | s) of 8 outputs 8d .. 8d + 7 of the lane's block for
-// group g: from the rows gF .. gF + gcap - 1 staged in LDS, else from HBM.
-__device__ __forceinline__ void sp_md8(const uint32_t (*s_md)[kVTile], int gcap, const MdHalf& mdh, int gF,
-                                       int staged, int g, int blk, int d, uint32_t (&md)[8]) {
-    if (staged) {
-        int gi = g - gF;  // a list that is not ascending gives wrong results, never a stray access
-        gi = gi < 0 ? 0 : (gi >= gcap ? gcap - 1 : gi);
-        const u32x4* src = reinterpret_cast<const u32x4*>(&s_md[gi][blk * sp::kOut + 8 * d]);
-        const u32x4 u = src[0], v = src[1];
-        md[0] = u.x; md[1] = u.y; md[2] = u.z; md[3] = u.w;
-        md[4] = v.x; md[5] = v.y; md[6] = v.z; md[7] = v.w;
-    } else {
-        const u32x4 u = md_words4(mdh, g, blk * sp::kOut + 8 * d), v = md_words4(mdh, g, blk * sp::kOut + 8 * d + 4);
-        const uint32_t raw[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int r = 0; r < 8; ++r) md[r] = sp_zc(raw[r], r & 1);
-    }
-}
-
-// Stage the scale/zero rows gF .. gF + ng - 1 of a half tile in LDS as
-// (1024 + z | s) pairs: thread e converts 4 words of row e / 64.  The
-// 16-byte loads of the first two rounds are issued by sp_md_issue before the
-// other loads of the kernel; sp_md_store writes them (and any further rows).
-struct SpMdRaw {
-    u32x4 v[2];
-};
-__device__ __forceinline__ void sp_md_issue(const MdHalf& mdh, int gF, int ng, SpMdRaw& r) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int e = threadIdx.x + i * sp::kThreads;
-        if (e < ng * (kVTile / 4)) r.v[i] = md_raw4(mdh, gF + e / (kVTile / 4), 4 * (e % (kVTile / 4)));
-    }
-}
-__device__ __forceinline__ void sp_md_put(uint32_t (*s_md)[kVTile], int e, u32x4 raw) {
-    *reinterpret_cast<u32x4*>(&s_md[e / (kVTile / 4)][4 * (e % (kVTile / 4))]) =
-        (u32x4){sp_zc(raw.x, 0), sp_zc(raw.y, 1), sp_zc(raw.z, 0), sp_zc(raw.w, 1)};
-}
-__device__ __forceinline__ void sp_md_store(uint32_t (*s_md)[kVTile], const MdHalf& mdh, int gF, int ng,
-                                            const SpMdRaw& r) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int e = threadIdx.x + i * sp::kThreads;
-        if (e < ng * (kVTile / 4)) sp_md_put(s_md, e, md_cook4(r.v[i], mdh.z4));
-    }
-    for (int e = threadIdx.x + 2 * sp::kThreads; e < ng * (kVTile / 4); e += sp::kThreads)
-        sp_md_put(s_md, e, md_words4(mdh, gF + e / (kVTile / 4), 4 * (e % (kVTile / 4))));
-}
-
-// One chunk of a wavefront: lane (slot, blk) holds listed columns kk[0..3]
-// (bit q of valid set where position q is in the list), their 16 weight
-// bytes w[q] (outputs 32 blk .. 32 blk + 31 of the half tile) and the
-// activations xw[m][q] (fp16 bits, 0 where masked).  Adds to v4[m][d] the
-// chunk's sum of output sp_out(lane, d).
-template <int MT>
-__device__ __forceinline__ void sp_chunk(const u32x4 (&w)[4], const uint32_t (&xw)[MT][4], const int (&kk)[4],
-                                         uint32_t valid, const uint32_t (*s_md)[kVTile], int gcap,
-                                         const MdHalf& mdh, int gF, int staged, int blk, int lane,
-                                         float (&v4)[MT][4]) {
-    const uint32_t vmagic = 0x64006400u | __builtin_amdgcn_mbcnt_lo(0u, 0u);  // per-lane (VGPR) copy
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        float y8[MT][8];
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int r = 0; r < 8; ++r) y8[m][r] = 0.f;
-        uint32_t todo = valid;
-        while (__ballot(todo != 0) != 0ull) {
-            int g = gF;
-            if (todo) {
-                const int q0 = __builtin_ctz(todo);
-                g = kk[0] >> 7;
-#pragma unroll
-                for (int q = 1; q < 4; ++q) g = (q == q0) ? (kk[q] >> 7) : g;
-            }
-            uint32_t msk = 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) msk |= (((todo >> q) & 1u) && ((kk[q] >> 7) == g)) ? (1u << q) : 0u;
-            todo &= ~msk;
-            uint32_t md[8];
-            sp_md8(s_md, gcap, mdh, gF, staged, g, blk, d, md);
-            float acc[MT][8];
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int r = 0; r < 8; ++r) acc[m][r] = 0.f;
-#pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
-                uint32_t xp[MT];
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    const uint32_t lo = ((msk >> (2 * pr)) & 1u) ? xw[m][2 * pr] : 0u;
-                    const uint32_t hi = ((msk >> (2 * pr + 1)) & 1u) ? xw[m][2 * pr + 1] : 0u;
-                    xp[m] = lo | (hi << 16);
-                }
-                const u32x4 A = w[2 * pr], B = w[2 * pr + 1];
-                const uint32_t Ad = d == 0 ? A.x : d == 1 ? A.y : d == 2 ? A.z : A.w;
-                const uint32_t Bd = d == 0 ? B.x : d == 1 ? B.y : d == 2 ? B.z : B.w;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // byte i of the two columns into the low bytes of the two halves
-                    const uint32_t sel = (0x0Cu << 24) | ((uint32_t)i << 16) | (0x0Cu << 8) | (4u + i);
-                    const uint32_t R = __builtin_amdgcn_perm(Ad, Bd, sel);
-                    const _Float16 zl = as_h2(md[2 * i]).x, zh = as_h2(md[2 * i + 1]).x;
-                    const half2_t lo = as_h2(and_or(R, 0x000F000Fu, vmagic)) - (half2_t){zl, zl};  // q - z
-                    const half2_t hi = as_h2(and_or(R, 0x00F000F0u, vmagic)) - (half2_t){zh, zh};  // 16 (q - z)
-#pragma unroll
-                    for (int m = 0; m < MT; ++m) {
-                        acc[m][2 * i] = __builtin_amdgcn_fdot2(lo, as_h2(xp[m]), acc[m][2 * i], false);
-                        acc[m][2 * i + 1] = __builtin_amdgcn_fdot2(hi, as_h2(xp[m]), acc[m][2 * i + 1], false);
-                    }
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const float sc = (float)as_h2(md[r]).y;
-#pragma unroll
-                for (int m = 0; m < MT; ++m) y8[m][r] = __builtin_fmaf(sc, acc[m][r], y8[m][r]);
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-#pragma unroll
-            for (int r = 1; r < 8; r += 2) y8[m][r] *= 0.0625f;  // the 16 of the high nibbles
-            v4[m][d] += sp_reduce8(y8[m], lane);
-        }
-    }
-}
-
-// Issue the weight loads of a lane's 4 columns.
-__device__ __forceinline__ void sp_load_w(const uint8_t* wcol, const int (&kk)[4], int blk, u32x4 (&w)[4]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        w[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wcol + (size_t)kk[q] * (2 * kHalfRun)) + blk);
 }
 
 template <int MT, int NW>
@@ -643,119 +471,41 @@ __device__ __forceinline__ void sp_finish(const RunArgs& a, int vt, int slice, i
     if (t == 0) __hip_atomic_store(&a.counters[vt * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// List-driven kernel: the list positions of the workgroup are
-// slice * 256 .. slice * 256 + 255 (one chunk per wavefront).
-template <int MT, bool DENSE, bool MASK, bool Z4>
-__global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_sp(RunArgs a) {
-    __shared__ uint32_t s_md[sp::kGCap][kVTile];
-    __shared__ SpShared<MT, sp::kWaves> sh;
+// ---------------------------------------------------------------------------
+// a quantization group's entries in a given ascending list
+// ---------------------------------------------------------------------------
+//
+// Entries read per lane per round (all in flight).  The window searched for a
+// group holds at most ceil(count / 64) + 128 entries, so one round of 6
+// covers every count up to 16384.
+constexpr int kListLoads = 6;
 
-    const int T = a.tiles;
-    const int vt = blockIdx.x % T;
-    const int slice = blockIdx.x / T;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int slot = lane >> 3, blk = lane & 7;
-    const int K = a.K;
-    const int P0 = slice * sp::kPos;
-    const int j0 = P0 + wave * sp::kCh;   // this wavefront's chunk
-
-    // the count, the workgroup's first and (if the list is long enough) last
-    // entry, and the lane's 4 entries are read together
-    int count, f = 0, l = 0;
-    int4 k4 = make_int4(0, 0, 0, 0);
-    if (DENSE) {
-        count = K;
-    } else {
-        count = __builtin_amdgcn_readfirstlane(*a.count);
-        const int pl = P0 + sp::kPos - 1 < K ? P0 + sp::kPos - 1 : K - 1;
-        f = a.idx[P0 < K ? P0 : K - 1];
-        l = a.idx[pl];
-        int jl = j0 + 4 * slot;
-        jl = jl + 3 < K ? jl : K - 4;  // K is a multiple of 128: stays in the K-entry list, 16-byte aligned
-        k4 = *reinterpret_cast<const int4*>(a.idx + jl);
-    }
-    count = count < 0 ? 0 : (count > K ? K : count);
-    const int S = (count + sp::kPos - 1) / sp::kPos;   // slices in use
-    if (count == 0) {  // nothing listed: y = +0
-        if (slice == 0) {
-            const float z[MT][4] = {};
-            sp_finish<MT, sp::kWaves>(a, vt, 0, 1, wave, lane, z, sh);
+// Sets bit k - kw of the four LDS words lm (zeroed by the caller) for every
+// entry k of lidx[0 .. c) in [kw, kw + 128), with c > 0.  The wavefront reads
+// 64 evenly spaced entries; those below kw are a prefix of the lanes (the list
+// is ascending), nlo of them, so the group's entries (at most 128) lie after
+// sample nlo - 1 and start at or before sample nlo: one window of positions.
+// An unsorted list gives wrong bits, never an access outside lidx[0 .. c).
+__device__ __forceinline__ void list_group_bits(const int32_t* __restrict__ lidx, int c, int kw, int lane,
+                                                uint32_t* lm) {
+    const int step = (c + 63) / 64;
+    const int sv = lidx[lane * step < c ? lane * step : c - 1];
+    const int nlo = __popcll(__ballot(sv < kw));
+    const int ws = nlo > 0 ? (nlo - 1) * step : 0;
+    const int we = nlo * step + kGroup < c ? nlo * step + kGroup : c;
+    for (int b = ws; b < we; b += 64 * kListLoads) {
+        int v[kListLoads];
+#pragma unroll
+        for (int i = 0; i < kListLoads; ++i) {
+            const int pos = b + 64 * i + lane;
+            v[i] = lidx[pos < we ? pos : we - 1];
         }
-        return;
-    }
-    if (slice >= S) return;
-    const int P1 = P0 + sp::kPos < count ? P0 + sp::kPos : count;
-
-    const int tt = vt >> 1, hh = vt & 1;
-    const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
-    const MdHalf mdh = md_half<Z4>(a, tt, hh);
-
-    // groups of the workgroup's first and last position
-    int gF, gL;
-    if (DENSE) {
-        gF = P0 >> 7;
-        gL = (P1 - 1) >> 7;
-    } else {
-        if (P1 != P0 + sp::kPos) l = a.idx[P1 - 1];  // the last slice of the list
-        f = (unsigned)f < (unsigned)K ? f : K - 1;
-        l = (unsigned)l < (unsigned)K ? l : K - 1;
-        gF = __builtin_amdgcn_readfirstlane(f >> 7);
-        gL = __builtin_amdgcn_readfirstlane(l >> 7);
-    }
-    const int ng = gL - gF + 1;
-    const int staged = (ng >= 1 && ng <= sp::kGCap) ? 1 : 0;
-
-    // this lane's 4 positions
-    const int nv = j0 < P1 ? (P1 - j0 < sp::kCh ? P1 - j0 : sp::kCh) : 0;
-    int kk[4];
-    uint32_t valid = 0;
-    {
-        const int jl = j0 + 4 * slot;
-        const int kv[4] = {DENSE ? jl : k4.x, DENSE ? jl + 1 : k4.y, DENSE ? jl + 2 : k4.z, DENSE ? jl + 3 : k4.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const bool ok = 4 * slot + q < nv;
-            int k = kv[q];
-            k = (unsigned)k < (unsigned)K ? k : K - 1;
-            kk[q] = ok ? k : -1;
-            valid |= (ok ? 1u : 0u) << q;
+        for (int i = 0; i < kListLoads; ++i) {
+            const int cc = v[i] - kw;
+            if (b + 64 * i + lane < we && (unsigned)cc < (unsigned)kGroup) atomicOr(&lm[cc >> 5], 1u << (cc & 31));
         }
-        // padding positions repeat a valid column of the lane, else the workgroup's first
-        int kfill = f;
-#pragma unroll
-        for (int q = 3; q >= 0; --q) kfill = kk[q] >= 0 ? kk[q] : kfill;
-        if (DENSE && kfill < 0) kfill = P0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) kk[q] = kk[q] >= 0 ? kk[q] : kfill;
     }
-
-    // 1. scale/zero rows (issued first), 2. activations and weights
-    SpMdRaw mdr;
-    if (staged) sp_md_issue(mdh, gF, ng, mdr);
-    uint32_t xw[MT][4];
-    u32x4 w[4];
-    if (nv > 0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const int mr = m < a.M ? m : a.M - 1;  // rows past M are never stored
-                uint32_t v = a.x[(size_t)mr * a.ldx + kk[q]];
-                if (MASK && !is_active(v, code_of(a.tc, mr))) v = 0;
-                xw[m][q] = ((valid >> q) & 1u) ? v : 0u;
-            }
-        }
-        sp_load_w(wcol, kk, blk, w);
-    }
-    // 3. stage the metadata
-    if (staged) sp_md_store(s_md, mdh, gF, ng, mdr);
-    __syncthreads();
-
-    // 4. the chunk, 5. the sums
-    float v4[MT][4] = {};
-    if (nv > 0) sp_chunk<MT>(w, xw, kk, valid, s_md, sp::kGCap, mdh, gF, staged, blk, lane, v4);
-    sp_finish<MT, sp::kWaves>(a, vt, slice, S, wave, lane, v4, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -777,7 +527,7 @@ __global__ __launch_bounds__(sp::kThreads) __attribute__((amdgpu_waves_per_eu(4)
 //      group: the scale is applied once per output), and sums the slots with
 //      lane swaps.
 // The workgroup then sums its wavefronts, and the segments of a half tile
-// are added as slices (as in the list-driven kernel).
+// are added by the last workgroup to arrive (sp_finish).
 //
 // When the global list is asked for, one more workgroup (block 0) writes it
 // with the gathering routine while the others compute; it reads only the
@@ -795,6 +545,7 @@ struct FsShared {
     __align__(16) float sc[W][kVTile];           // ... scale of output sp_out(l, d) at 4 l + d (1/16 folded in for odd)
     __align__(16) int k[W][kFsCols];             // ... its active columns
     __align__(16) uint16_t xs[W][MT][kFsCols];   // ... and their masked activations
+    uint32_t lm[W][4];                           // ... over a given list: its listed columns
 };
 
 template <int MT, int W>
@@ -860,7 +611,7 @@ __device__ __forceinline__ void fs_compute(FsShared<MT, W>& fs, int wave, int la
     // zero codes of the lane's 32 outputs, scales of its 4 final outputs
     uint32_t zc[16];
     {
-        const u32x4* src = reinterpret_cast<const u32x4*>(&fs.zc[wave][blk * (sp::kOut / 2)]);
+        const u32x4* src = reinterpret_cast<const u32x4*>(&fs.zc[wave][blk * (kLaneOut / 2)]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const u32x4 u = src[i];
@@ -988,7 +739,7 @@ __device__ __forceinline__ void fs_dense(const RunArgs& a, FsShared<MT, W>& fs, 
     fs_compute<MT, NP, W>(fs, wave, lane, blk, w, xp, mdv, mdh.z4, v4);
 }
 
-template <int MT, bool Z4, int W>
+template <int MT, bool Z4, int W, bool LIST>
 __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
     int bid = blockIdx.x;
     if (a.idx_out) {  // block 0 writes the list
@@ -1036,7 +787,22 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
             xr[h][m] = a.x[(size_t)mr * a.ldx + (has ? kw : 0) + 64 * h + lane];
         }
 
-    // 2. threshold, rank, compact into this wavefront's LDS rows (no branch
+    // 2. over a given list (a separate build), the group's listed columns
+    //    (bit h of lb: column lane + 64 h); without one, every column may be
+    //    active
+    uint32_t lb = 3u;
+    if constexpr (LIST) {
+        const int lc = *a.lcount;   // issued after the activations, waited for with them
+        if (lane < 4) fs.lm[wave][lane] = 0u;
+        __builtin_amdgcn_wave_barrier();
+        int c = __builtin_amdgcn_readfirstlane(lc);
+        c = c < 0 ? 0 : (c > K ? K : c);
+        if (has && c > 0) list_group_bits(a.lidx, c, kw, lane, fs.lm[wave]);
+        __builtin_amdgcn_wave_barrier();
+        lb = ((fs.lm[wave][lane >> 5] >> (lane & 31)) & 1u) | (((fs.lm[wave][2 + (lane >> 5)] >> (lane & 31)) & 1u) << 1);
+    }
+
+    // 3. threshold, rank, compact into this wavefront's LDS rows (no branch
     //    before the ballots: x is waited for on every path)
     bool act[H];
     uint32_t xm[H][MT];
@@ -1046,11 +812,10 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const int mr = m < a.M ? m : a.M - 1;
-            const bool am = (a.unmasked || is_active(xr[h][m], code_of(a.tc, mr))) & has;
+            const bool am = (a.unmasked || is_active(xr[h][m], code_of(a.tc, mr))) & has & ((lb >> h) & 1u);
             act[h] = act[h] | am;
             xm[h][m] = am ? xr[h][m] : 0u;
         }
-        if (a.all_cols) act[h] = has;
     }
     int nact = 0;
     uint32_t rank[H];
@@ -1071,7 +836,7 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
     }
     __builtin_amdgcn_wave_barrier();  // LDS operations of a wavefront complete in order
 
-    // 3-5. np column pairs per lane (straight-line code per np, so that every
+    // 4. np column pairs per lane (straight-line code per np, so that every
     //      pair waits only for its own loads)
     float v4[MT][4] = {};
     switch (np) {
@@ -1092,16 +857,16 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
 // budget, for grids of at most one workgroup per CU), and four (two
 // workgroups per CU, so that one's loads overlap the other's latency in
 // grids that take several rounds).
-template <int MT, bool Z4, int W>
+template <int MT, bool Z4, int W, bool LIST>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fs(RunArgs a) {
     __shared__ FsLds<MT, W> lds;
-    fs_body<MT, Z4, W>(a, lds);
+    fs_body<MT, Z4, W, LIST>(a, lds);
 }
 
-template <int MT, bool Z4>
+template <int MT, bool Z4, bool LIST>
 __global__ __launch_bounds__(kFsW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_fs4(RunArgs a) {
     __shared__ FsLds<MT, kFsW> lds;
-    fs_body<MT, Z4, kFsW>(a, lds);
+    fs_body<MT, Z4, kFsW, LIST>(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1143,10 +908,6 @@ constexpr int kSeg = kWaves * kCols;     // columns per workgroup
 constexpr int kRows = 16;                // batch rows (the MFMA's N), padded with zeros
 constexpr int kCh = 32;                  // listed columns per MFMA step (its K)
 constexpr int kMaxCh = kCols / kCh;
-// Over a given list: entries read per lane per round (all in flight).  The
-// window searched for a group holds at most ceil(count / 64) + 128 entries,
-// so one round of 6 covers every count up to 16384.
-constexpr int kListLoads = 6;
 constexpr int kOutFloats = kRows * kVTile;   // one workgroup's sums
 // LDS row strides, padded so that the 16-byte tile writes, the transposing
 // reads and the row-wise accesses spread over the banks
@@ -1308,31 +1069,7 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
         __builtin_amdgcn_wave_barrier();
         int c = __builtin_amdgcn_readfirstlane(lc);
         c = c < 0 ? 0 : (c > K ? K : c);
-        if (has && c > 0) {
-            // 64 evenly spaced samples of the ascending list: those below the
-            // group's first column are a prefix of the lanes, nlo of them
-            const int step = (c + 63) / 64;
-            const int sv = a.lidx[lane * step < c ? lane * step : c - 1];
-            const int nlo = __popcll(__ballot(sv < kw));
-            // the group's entries (at most 128) lie after sample nlo - 1 and
-            // start at or before sample nlo: positions [ws, we)
-            const int ws = nlo > 0 ? (nlo - 1) * step : 0;
-            const int we = nlo * step + fm::kCols < c ? nlo * step + fm::kCols : c;
-            for (int b = ws; b < we; b += 64 * fm::kListLoads) {
-                int v[fm::kListLoads];
-#pragma unroll
-                for (int i = 0; i < fm::kListLoads; ++i) {   // all in flight, then the bits
-                    const int pos = b + 64 * i + lane;
-                    v[i] = a.lidx[pos < we ? pos : we - 1];
-                }
-#pragma unroll
-                for (int i = 0; i < fm::kListLoads; ++i) {
-                    const int cc = v[i] - kw;
-                    if (b + 64 * i + lane < we && (unsigned)cc < (unsigned)fm::kCols)
-                        atomicOr(&fw.lm[cc >> 5], 1u << (cc & 31));
-                }
-            }
-        }
+        if (has && c > 0) list_group_bits(a.lidx, c, kw, lane, fw.lm);
         __builtin_amdgcn_wave_barrier();
         un = fw.lm[lane & 3];  // word q at lane q, as the union above
     }
@@ -1584,18 +1321,6 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
 // host side
 // ---------------------------------------------------------------------------
 
-int pow2_ceil(int m) {
-    int p = 1;
-    while (p < m) p <<= 1;
-    return p;
-}
-
-// Slices per tile: enough workgroups to cover the chip, never more slices
-// than 16-position chunks in a full list.
-// Slices of the list-driven kernel (one or two rows): one workgroup per 256
-// list positions.
-int slices_for(const sgemv_desc* d, int) { return (d->K + sp::kPos - 1) / sp::kPos; }
-
 float half_value(uint32_t b) {
     const int e = (b >> 10) & 0x1F;
     const int m = b & 0x3FF;
@@ -1654,19 +1379,13 @@ size_t ws_gather_bytes(const sgemv_desc* d) { return 256 + ((size_t)d->K * 4 + 2
 // (whose size depends on the largest batch).
 size_t ws_head_bytes(const sgemv_desc* d) { return ws_counters_bytes(d->N / kVTile) + ws_gather_bytes(d); }
 
-size_t ws_partial_bytes(const sgemv_desc* d, int mt) {
-    const int tiles = d->N / kVTile;
-    const int s = slices_for(d, mt);
-    return s > 1 ? (size_t)tiles * s * mt * kVTile * sizeof(float) : 0;
-}
-
-// Partial sums of the fused call with M rows: one or two rows use the
-// list-driven layout (slices_for stride), 3 to 16 rows M x 256 sums per
-// 1024-column segment and half tile.
+// Partial sums of a call with M rows: M x 256 fp32 sums per half tile and
+// segment (one or two rows: at most one segment per 512 columns, the
+// smallest workgroup's; 3 to 16 rows: one per 1024 columns).
 size_t ws_fused_bytes(const sgemv_desc* d, int M) {
-    if (M <= 2) return ws_partial_bytes(d, M);
     const int tiles = d->N / kVTile;
-    const int segs = (d->K + fm::kSeg - 1) / fm::kSeg;
+    const int seg_cols = M <= 2 ? kFsWSmall * kFsCols : fm::kSeg;
+    const int segs = (d->K + seg_cols - 1) / seg_cols;
     return segs > 1 ? (size_t)tiles * segs * M * kVTile * sizeof(float) : 0;
 }
 
@@ -1688,20 +1407,6 @@ constexpr int kFsSmallGrid = 160;
 // partial sums grows too long (70B down, 56 segments: slower).
 constexpr int kFsSmallMaxSegs = 32;
 
-// The list-driven kernel, one or two rows (3 and more rows over a given list
-// run on the fused many-row kernel).
-template <int MT, bool DENSE, bool MASK, bool Z4>
-hipError_t launch_run(const RunArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)(a.tiles * a.slices));  // slices: see slices_for
-    hipLaunchKernelGGL((k_sp<MT, DENSE, MASK, Z4>), grid, dim3(sp::kWaves * 64), 0, s, a);
-    return hipGetLastError();
-}
-
-template <bool DENSE, bool MASK, bool Z4>
-hipError_t launch_mt(int mt, const RunArgs& a, hipStream_t s) {
-    return mt == 1 ? launch_run<1, DENSE, MASK, Z4>(a, s) : launch_run<2, DENSE, MASK, Z4>(a, s);
-}
-
 int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx, const float* thr,
               int32_t* idx, int32_t* count, void* y, int ldy, uint32_t flags, void* ws, void* stream,
               bool all_cols = false, const int32_t* lidx = nullptr, const int32_t* lcount = nullptr);
@@ -1722,62 +1427,27 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
     if (count && !aligned(count, 4)) return SGEMV_EALIGN;
     if (!idx)   // every column: the fused kernels with the whole list, which stream faster
         return run_fused(d, packed, x, M, ldx, thr, nullptr, nullptr, y, ldy, flags, ws, stream, true);
-    if (M > 2)  // 3..16 rows over a given list: the many-row fused kernel reads the list itself
-        return run_fused(d, packed, x, M, ldx, thr, nullptr, nullptr, y, ldy, flags, ws, stream, false, idx, count);
+    // over a given list the fused kernels read the list themselves
+    return run_fused(d, packed, x, M, ldx, thr, nullptr, nullptr, y, ldy, flags, ws, stream, false, idx, count);
 
-    const int mt = pow2_ceil(M);
-    RunArgs a;
-    std::memset(&a, 0, sizeof a);
-    if (thr) {
-        st = fill_codes(thr, M, a.tc);
-        if (st) return st;
-    }
-    a.tiles = d->N / kVTile;
-    a.slices = slices_for(d, mt);
-    const size_t pbytes = ws_partial_bytes(d, mt);
-    if (a.slices > 1) {
-        if (!ws) return SGEMV_EINVAL;
-        if (!aligned(ws, 256)) return SGEMV_EALIGN;
-    }
-    const uint8_t* blob = static_cast<const uint8_t*>(packed);
-    a.w = blob + d->w_off;
-    a.md = blob + d->m_off;
-    a.md_z4 = d->version == SGEMV_LAYOUT_Z4 ? 1u : 0u;
-    a.x = static_cast<const uint16_t*>(x);
-    a.idx = idx;
-    a.count = count;
-    a.y = y;
-    a.counters = static_cast<uint32_t*>(ws);
-    a.partials = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ws_head_bytes(d)) : nullptr;
-    a.partial_bytes = (uint32_t)pbytes;
-    a.K = d->K;
-    a.ldx = ldx;
-    a.ldy = ldy;
-    a.M = M;
-    a.out_f32 = (flags & SGEMV_OUT_F32) ? 1u : 0u;
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    const bool mask = (thr != nullptr);
-    if (a.md_z4) e = mask ? launch_mt<false, true, true>(mt, a, s) : launch_mt<false, false, true>(mt, a, s);
-    else e = mask ? launch_mt<false, true, false>(mt, a, s) : launch_mt<false, false, false>(mt, a, s);
-    if (e != hipSuccess) {
-        g_last_hip_error = (int)e;
-        return SGEMV_EHIP;
-    }
-    return SGEMV_OK;
 }
 
 // The fused kernels; with all_cols every column is listed (the dense GEMV,
 // rows masked by their thresholds unless thr is NULL).
+template <bool Z4, bool LIST>
+void launch_fs(int M, int W, bool one_round, dim3 grid, const RunArgs& a, hipStream_t s) {
+    if (M == 1 && W == kFsWSmall) hipLaunchKernelGGL((k_fs<1, Z4, kFsWSmall, LIST>), grid, dim3(kFsWSmall * 64), 0, s, a);
+    else if (M == 1 && one_round) hipLaunchKernelGGL((k_fs<1, Z4, kFsW, LIST>), grid, dim3(kFsW * 64), 0, s, a);
+    else if (M == 1) hipLaunchKernelGGL((k_fs4<1, Z4, LIST>), grid, dim3(kFsW * 64), 0, s, a);
+    else if (one_round) hipLaunchKernelGGL((k_fs<2, Z4, kFsW, LIST>), grid, dim3(kFsW * 64), 0, s, a);
+    else hipLaunchKernelGGL((k_fs4<2, Z4, LIST>), grid, dim3(kFsW * 64), 0, s, a);
+}
+
 template <bool Z4>
 void launch_fused(int M, int W, bool one_round, dim3 grid, const RunArgs& a, hipStream_t s) {
-    if (M == 1 && W == kFsWSmall) hipLaunchKernelGGL((k_fs<1, Z4, kFsWSmall>), grid, dim3(kFsWSmall * 64), 0, s, a);
-    else if (M == 1 && one_round) hipLaunchKernelGGL((k_fs<1, Z4, kFsW>), grid, dim3(kFsW * 64), 0, s, a);
-    else if (M == 1) hipLaunchKernelGGL((k_fs4<1, Z4>), grid, dim3(kFsW * 64), 0, s, a);
-    else if (M == 2 && one_round) hipLaunchKernelGGL((k_fs<2, Z4, kFsW>), grid, dim3(kFsW * 64), 0, s, a);
-    else if (M == 2) hipLaunchKernelGGL((k_fs4<2, Z4>), grid, dim3(kFsW * 64), 0, s, a);
-    else hipLaunchKernelGGL(k_fm<Z4>, grid, dim3(fm::kWaves * 64), 0, s, a);
+    if (M > 2) hipLaunchKernelGGL(k_fm<Z4>, grid, dim3(fm::kWaves * 64), 0, s, a);
+    else if (a.lidx) launch_fs<Z4, true>(M, W, one_round, grid, a, s);
+    else launch_fs<Z4, false>(M, W, one_round, grid, a, s);
 }
 
 int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx, const float* thr,
@@ -1809,7 +1479,6 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     a.tiles = d->N / kVTile;
     int W = kFsW;
     if (M <= 2) {
-        a.slices = slices_for(d, M);   // stride of the partials region
         const int segs8 = (d->K + kFsW * kFsCols - 1) / (kFsW * kFsCols);
         const int segs4 = (d->K + kFsWSmall * kFsCols - 1) / (kFsWSmall * kFsCols);
         if (M == 1 && (a.tiles * segs8 < kFsSmallGrid ||
@@ -1818,8 +1487,8 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
         a.segs = (d->K + W * kFsCols - 1) / (W * kFsCols);
     } else {
         a.segs = (d->K + fm::kSeg - 1) / fm::kSeg;
-        a.slices = a.segs;
     }
+    a.slices = a.segs;   // stride of the partial sums
     if (a.segs > 1) {
         if (!ws) return SGEMV_EINVAL;
         if (!aligned(ws, 256)) return SGEMV_EALIGN;
@@ -1913,10 +1582,6 @@ extern "C" int sgemv_run_batched(const sgemv_desc* d, const void* packed, const 
 extern "C" size_t sgemv_workspace_bytes(const sgemv_desc* d, int32_t M) {
     if (check_desc(d) != SGEMV_OK || M < 1 || M > SGEMV_MAX_BATCH) return 0;
     size_t part = 0;  // enough for every call with up to M rows
-    for (int mt = 1; mt <= (M < 2 ? M : 2); ++mt) {   // the list-driven kernel's rows
-        const size_t b = ws_partial_bytes(d, mt);
-        part = b > part ? b : part;
-    }
     for (int m = 1; m <= M; ++m) {
         const size_t b = ws_fused_bytes(d, m);
         part = b > part ? b : part;

@@ -429,7 +429,7 @@ def main():
                                "50% magnitude sparsity; step = threshold + compact (list written) + "
                                "sparse GEMV in one launch",
                    "K": K_DOWN, "N": N_DOWN, "sparsity": 0.5, "weight_copies_rotated": R},
-        "roofline": {"bound": "hbm", "kernel": "k_fs<1, false, 8> (fused threshold + compact + sparse GEMV; layout version 1)",
+        "roofline": {"bound": "hbm", "kernel": "k_fs<1, false, 8, false> (fused threshold + compact + sparse GEMV; layout version 1)",
                      "achieved": round(main_res["GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(main_res["frac_hbm_peak"], 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": main_res["bytes"],
