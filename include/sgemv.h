@@ -243,8 +243,8 @@ int sgemv_run_batched(const sgemv_desc* d, const void* packed,
  * thresholding from the weight reads (the page's Abstract asks for index
  * gathering with minimal overhead).  Each wavefront thresholds one
  * 128-column group of every row, compacts the columns active in any row in
- * LDS and reads only their weight bytes; the workgroups of 1024-column
- * segments are summed as in sgemv_run.
+ * LDS and reads only their weight bytes; the workgroups of the column
+ * segments (512 or 1024 columns) are summed as in sgemv_run.
  *   y[m][n] = sum over active k of w^[n][k] * xe[m][k]
  * with xe and the union of active columns as in sgemv_run_batched (with
  * thresholds), which it equals within the same error bound (the order of
@@ -252,7 +252,7 @@ int sgemv_run_batched(const sgemv_desc* d, const void* packed,
  *
  *   M          1..SGEMV_MAX_BATCH.  One or two rows run on the vector
  *              units; 3 to 16 rows run on the matrix cores
- *              (v_mfma_f32_16x16x16_f16 over exactly dequantized fp16
+ *              (v_mfma_f32_16x16x32_f16 over exactly dequantized fp16
  *              q - z, fp32 accumulation), each row masked by its own
  *              threshold over the union of the rows' active columns
  *   thresholds host float [M], each finite and >= 0 (required)
