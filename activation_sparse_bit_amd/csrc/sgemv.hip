@@ -1019,22 +1019,22 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
     const MdHalf mdh = md_half<Z4>(a, tt, hh);
 
-    // 1. the group's scale/zero row (converted where it is used) and, over a
-    //    given list, its length (without a list the same load reads the
-    //    activations and is unused, so that no path waits for it early).
-    //    Issued before the activations: loads complete in order, and both are
-    //    needed before the weight loads.
-    const u32x4 mdv = md_raw4(mdh, g, 4 * lane);
+    // 1. over a given list, its length (without a list the same load reads
+    //    the activations and is unused, so that no path waits for it early);
+    //    the activations: lane (row xm = lane / 4, quarter xq = lane % 4)
+    //    loads 32 columns, rows past M read row M - 1 and are masked out; then
+    //    the group's scale/zero row, which is converted after the weight loads
+    //    are issued (loads complete in order: the activations are waited for
+    //    without it, and it arrives before the weights)
     const int lc = *(a.lidx ? a.lcount : reinterpret_cast<const int32_t*>(a.x));
-    __builtin_amdgcn_sched_barrier(0);   // keeps these loads ahead of the activations'
-    // 2. activations: lane (row xm = lane / 4, quarter xq = lane % 4) loads
-    //    32 columns; rows past M read row M - 1 and are masked out
     const int xm = lane >> 2, xq = lane & 3;
     const int xmr = xm < a.M ? xm : a.M - 1;
     uint4 xv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         xv[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)xmr * a.ldx + (has ? kw : 0) + 32 * xq + 8 * i);
+    __builtin_amdgcn_sched_barrier(0);   // keeps the scale/zero load behind the activations'
+    const u32x4 mdv = md_raw4(mdh, g, 4 * lane);
 
     const uint32_t code = code_of(a.tc, xmr);
     const bool row_ok = has && xm < a.M;
@@ -1104,26 +1104,6 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[i] = (u32x4){mw[4 * i], mw[4 * i + 1], mw[4 * i + 2], mw[4 * i + 3]};
     }
-    // 2c. zero codes of the weight bytes 2 lane, 2 lane + 1 (outputs 4 lane ..
-    //     4 lane + 3) and their scales in storage order
-    {
-        const u32x4 mc = md_cook4(mdv, mdh.z4);
-        const uint32_t mw[4] = {mc.x, mc.y, mc.z, mc.w};
-        uint32_t zpair[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const half2_t se = as_h2(mw[2 * h]), so = as_h2(mw[2 * h + 1]);
-            const half2_t zp = (half2_t){(_Float16)(se.y + (_Float16)1024.0f),
-                                         (_Float16)(so.y * (_Float16)16.0f + (_Float16)1024.0f)};
-            zpair[h] = __builtin_bit_cast(uint32_t, zp);
-        }
-        *reinterpret_cast<uint2*>(&fw.zc[2 * lane]) = make_uint2(zpair[0], zpair[1]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const half2_t sz = as_h2(mw[r]);
-            fw.sc[fm_store_of(4 * lane + r)] = (r & 1) ? (float)sz.x * 0.0625f : (float)sz.x;
-        }
-    }
     __builtin_amdgcn_wave_barrier();  // LDS operations of a wavefront complete in order
 
     // 3. chunks of 32 listed columns
@@ -1148,6 +1128,27 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
                 wl[c][i] = __builtin_nontemporal_load(
                     reinterpret_cast<const u32x4*>(wcol + (size_t)k * (2 * kHalfRun)) + lo);
             }
+        // 3a. zero codes of the weight bytes 2 lane, 2 lane + 1 (outputs 4 lane ..
+        //     4 lane + 3) and their scales in storage order
+        {
+            const u32x4 mc = md_cook4(mdv, mdh.z4);
+            const uint32_t mw[4] = {mc.x, mc.y, mc.z, mc.w};
+            uint32_t zpair[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const half2_t se = as_h2(mw[2 * h]), so = as_h2(mw[2 * h + 1]);
+                const half2_t zp = (half2_t){(_Float16)(se.y + (_Float16)1024.0f),
+                                             (_Float16)(so.y * (_Float16)16.0f + (_Float16)1024.0f)};
+                zpair[h] = __builtin_bit_cast(uint32_t, zp);
+            }
+            *reinterpret_cast<uint2*>(&fw.zc[2 * lane]) = make_uint2(zpair[0], zpair[1]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const half2_t sz = as_h2(mw[r]);
+                fw.sc[fm_store_of(4 * lane + r)] = (r & 1) ? (float)sz.x * 0.0625f : (float)sz.x;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
         const int g = lane >> 4, li = lane & 15;   // A/B operand: depth quarter, row
         // zero codes of the lane's A rows: weight byte 16 b + li, b = 0..7
         uint32_t zq[8];
