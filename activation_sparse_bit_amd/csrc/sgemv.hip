@@ -1493,6 +1493,8 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     if (a.segs > 1) {
         if (!ws) return SGEMV_EINVAL;
         if (!aligned(ws, 256)) return SGEMV_EALIGN;
+        // the kernels address the partial sums with 32-bit buffer offsets
+        if (ws_fused_bytes(d, M) > 0xFFFFFFFFull) return SGEMV_ESIZE;
     }
     const uint8_t* blob = static_cast<const uint8_t*>(packed);
     a.w = blob + d->w_off;

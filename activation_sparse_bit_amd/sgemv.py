@@ -27,6 +27,8 @@ SGEMV_TILE_N = 512
 SGEMV_LAYOUT_PAIRS = 1    # layout version 1: (s, z) fp16 pairs
 SGEMV_LAYOUT_Z4 = 2       # layout version 2: fp16 scales, 4-bit zero-points
 SGEMV_MAX_BATCH = 16
+SGEMV_MAX_K = 65536
+SGEMV_MAX_N = 1 << 20
 
 EXPORTED = ["sgemv_pack_layout", "sgemv_pack_layout_z4", "sgemv_desc_from_header", "sgemv_gather_indices",
             "sgemv_run", "sgemv_run_batched", "sgemv_run_fused", "sgemv_workspace_bytes",

@@ -229,7 +229,10 @@ int sgemv_run(const sgemv_desc* d, const void* packed, const void* x_f16,
  *   x_f16 device fp16 [M][ldx], 16-byte aligned, ldx >= K, ldx % 8 == 0
  *   y     device fp16/fp32 [M][ldy], 16-byte aligned, ldy >= N, ldy % 8 == 0
  *   workspace: sgemv_workspace_bytes(d, M) bytes, same contract as above.
- * Other arguments as in sgemv_run.
+ * Other arguments as in sgemv_run.  SGEMV_ESIZE when the call's partial
+ * sums would exceed 4 GiB - 1 (half tiles x segments x M x 1 KiB; only
+ * near the largest N, K and M), which the kernels address with 32-bit
+ * offsets.
  */
 int sgemv_run_batched(const sgemv_desc* d, const void* packed,
                       const void* x_f16, int32_t M, int32_t ldx,

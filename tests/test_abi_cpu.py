@@ -255,3 +255,19 @@ def test_fused_projections_rejects_bad_parts():
         sgemv.FusedProjections([("a", q, s, z), ("b", q3, s3, z3)], device="cpu")
     with pytest.raises(ValueError):      # duplicate names
         sgemv.FusedProjections([("a", q, s, z), ("a", q, s, z)], device="cpu")
+
+
+def test_partials_beyond_32bit_offsets_rejected():
+    """A call whose partial sums would not fit 32-bit offsets (largest N, K
+    and M) is refused before any launch; a smaller M on the same matrix
+    passes validation up to the launch (not made here: no GPU)."""
+    L = sgemv.lib()
+    E = sgemv
+    d = sgemv.Desc()
+    N, K = sgemv.SGEMV_MAX_N, sgemv.SGEMV_MAX_K
+    assert L.sgemv_pack_layout(None, None, None, N, K, 128, 512, None, 0, ctypes.byref(d)) == E.SGEMV_OK
+    assert sgemv.sgemv_workspace_bytes(d, 16) > (1 << 32)
+    t = np.zeros(16, dtype=np.float32)
+    st = L.sgemv_run_fused(ctypes.byref(d), FAKE, FAKE, 16, K, t.ctypes.data, None, None, FAKE, N, 0,
+                           FAKE, None)
+    assert st == E.SGEMV_ESIZE
