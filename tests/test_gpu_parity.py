@@ -331,16 +331,18 @@ def test_run_batched_every_column(M):
 
 
 @pytest.mark.gpu
-def test_run_batched_given_list_edges():
-    """3+ rows over a given list (the many-row fused kernel in list mode):
-    an empty list, a hand-made list touching the first and last groups with
-    junk beyond its count, a ragged K, and a count above K (clamped)."""
+@pytest.mark.parametrize("M", [1, 2, 5])
+def test_run_batched_given_list_edges(M):
+    """Rows over a given list (the list builds of the fused kernels: one or
+    two rows on the vector units, 3+ on the matrix cores): an empty list, a
+    hand-made list touching the first and last groups with junk beyond its
+    count, a ragged K, and a count above K (clamped)."""
     from activation_sparse_bit_amd import sgemv
-    K, N, M = 1152, 1024, 5
+    K, N = 1152, 1024
     q, s, z = synth.random_int4_problem(77, N, K)
     pm = sgemv.PackedMatrix(q, s, z, device=G.torch_dev())
     X = np.stack([synth.plain_activation(60 + m, K) for m in range(M)])
-    ts = [0.2 * m for m in range(M)]
+    ts = [0.3 + 0.2 * m for m in range(M)]
     xd = G.to_dev(X)
     dev = G.torch_dev()
     lists = [np.zeros(0, dtype=np.int32),
@@ -376,13 +378,14 @@ def test_run_batched_given_list_edges():
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("M", [1, 4])
 @pytest.mark.parametrize("K,keep", [(28672, 0.95), (65536, 0.6), (65536, 0.002)])
-def test_run_batched_given_list_long(K, keep):
-    """3+ rows over a long given list: the window searched for each group
-    spans several rounds of loads when the count is above 16384, and a
-    near-empty list leaves most groups with no entry."""
+def test_run_batched_given_list_long(K, keep, M):
+    """Rows over a long given list: the window searched for each group spans
+    several rounds of loads when the count is above 16384, and a near-empty
+    list leaves most groups with no entry."""
     from activation_sparse_bit_amd import sgemv
-    N, M = 512, 4
+    N = 512
     q, s, z = synth.random_int4_problem(int(K * keep) + 5, N, K)
     pm = sgemv.PackedMatrix(q, s, z, device=G.torch_dev())
     X = np.stack([synth.plain_activation(90 + m, K) for m in range(M)])
