@@ -59,3 +59,59 @@ def test_graph_replays_match_eager():
             assert np.array_equal(a, b), f"eager after replay {rep}"
     tiles = N // 256
     assert int(torch.count_nonzero(pm.workspace[:tiles * 256]).item()) == 0
+
+
+def test_graph_replays_match_eager_many_rows_and_dense():
+    """The same for 4 rows (the matrix-core kernel with its list workgroups,
+    and over a given list), 2 rows over a given list, and the dense path."""
+    from activation_sparse_bit_amd import sgemv
+    K, N, M = 14336, 4096, 4
+    pm = G.packed(0, N, K, 0.02)
+    dev = G.torch_dev()
+    X1 = np.stack([synth.glu_activation(m, K) for m in range(M)])
+    X2 = np.stack([synth.glu_activation(10 + m, K) for m in range(M)])
+    T1 = [synth.percentile_threshold(X1[m], 0.7) for m in range(M)]
+    T2 = [synth.percentile_threshold(X2[m], 0.5) for m in range(M)]
+    x1, x2 = G.to_dev(X1), G.to_dev(X2)
+    idx = torch.zeros(K, dtype=torch.int32, device=dev)
+    cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+    yf = torch.zeros((M, N), dtype=torch.float32, device=dev)
+    yl = torch.zeros((M, N), dtype=torch.float32, device=dev)
+    y2 = torch.zeros((2, N), dtype=torch.float32, device=dev)
+    yd = torch.zeros(N, dtype=torch.float16, device=dev)
+
+    def step(x, t):
+        sgemv.sgemv_run_fused(pm.desc, pm.blob, x, t, yf, pm.workspace, idx, cnt)
+        sgemv.sgemv_run_batched(pm.desc, pm.blob, x, t, idx, cnt, yl, pm.workspace)
+        sgemv.sgemv_run_batched(pm.desc, pm.blob, x[:2], t[:2], idx, cnt, y2, pm.workspace)
+        sgemv.sgemv_run(pm.desc, pm.blob, x[0], None, None, yd, pm.workspace)
+
+    def snap():   # the list up to its count (entries past it keep older lists' values)
+        torch.cuda.synchronize()
+        c = int(cnt.item())
+        return (yf.cpu().numpy().view(np.uint32).copy(), yl.cpu().numpy().view(np.uint32).copy(),
+                y2.cpu().numpy().view(np.uint32).copy(), yd.cpu().numpy().view(np.uint16).copy(),
+                idx.cpu().numpy()[:c].copy(), c)
+
+    step(x1, T1)
+    ref = snap()
+    step(x2, T2)
+    other = snap()
+    assert not np.array_equal(ref[0], other[0]) and not np.array_equal(ref[3], other[3])
+
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step(x1, T1)
+    names = ("fused", "given list, 4 rows", "given list, 2 rows", "dense", "list", "count")
+    for rep in range(4):
+        g.replay()
+        got = snap()
+        for nm, a, b in zip(names, got, ref):
+            assert np.array_equal(a, b), f"replay {rep}: {nm} differs in {np.count_nonzero(np.asarray(a) != np.asarray(b))} entries"
+        step(x2, T2)
+        got = snap()
+        for nm, a, b in zip(names, got, other):
+            assert np.array_equal(a, b), f"eager after replay {rep}: {nm}"
+    tiles = N // 256
+    assert int(torch.count_nonzero(pm.workspace[:tiles * 256]).item()) == 0
