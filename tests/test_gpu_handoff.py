@@ -28,13 +28,13 @@ def _alternate(call, inputs, reps=20):
     assert not np.array_equal(first[0], first[1])
 
 
-@pytest.mark.parametrize("path", ["run", "batched4", "fused1", "fused16"])
+@pytest.mark.parametrize("path", ["run", "batched2", "batched4", "fused1", "fused4list", "fused16", "dense"])
 def test_alternating_inputs_bitwise(path):
     from activation_sparse_bit_amd import sgemv
     K, N = 14336, 4096
     pm = G.packed(0, N, K, 0.02)
     dev = G.torch_dev()
-    M = {"run": 1, "batched4": 4, "fused1": 1, "fused16": 16}[path]
+    M = {"run": 1, "batched2": 2, "batched4": 4, "fused1": 1, "fused4list": 4, "fused16": 16, "dense": 1}[path]
     inputs = []
     for j in range(2):
         X = np.stack([synth.glu_activation(7 * j + m, K) for m in range(M)])
@@ -49,9 +49,13 @@ def test_alternating_inputs_bitwise(path):
         if path == "run":
             sgemv.sgemv_gather_indices(xd, ts, idx, cnt)
             sgemv.sgemv_run(pm.desc, pm.blob, xd[0], idx, cnt, y[0], pm.workspace)
-        elif path == "batched4":
+        elif path in ("batched2", "batched4"):
             sgemv.sgemv_gather_indices(xd, ts, idx, cnt)
             sgemv.sgemv_run_batched(pm.desc, pm.blob, xd, ts, idx, cnt, y, pm.workspace)
+        elif path == "fused4list":
+            sgemv.sgemv_run_fused(pm.desc, pm.blob, xd, ts, y, pm.workspace, idx, cnt)
+        elif path == "dense":
+            sgemv.sgemv_run(pm.desc, pm.blob, xd[0], None, None, y[0], pm.workspace)
         else:
             sgemv.sgemv_run_fused(pm.desc, pm.blob, xd, ts, y, pm.workspace)
         return y
