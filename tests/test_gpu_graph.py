@@ -115,3 +115,37 @@ def test_graph_replays_match_eager_many_rows_and_dense():
             assert np.array_equal(a, b), f"eager after replay {rep}: {nm}"
     tiles = N // 256
     assert int(torch.count_nonzero(pm.workspace[:tiles * 256]).item()) == 0
+
+
+def test_calls_on_a_side_stream_match_the_default_stream():
+    """Every call enqueues on the stream it is given: the same calls on a
+    second stream (default priority) give the same bits as on the current
+    stream, with the work ordered by that stream alone."""
+    from activation_sparse_bit_amd import sgemv
+    K, N, M = 14336, 4096, 4
+    pm = G.packed(0, N, K, 0.02)
+    dev = G.torch_dev()
+    X = np.stack([synth.glu_activation(20 + m, K) for m in range(M)])
+    T = [synth.percentile_threshold(X[m], 0.6) for m in range(M)]
+
+    def run(stream):
+        with torch.cuda.stream(stream):
+            xd = G.to_dev(X)
+            idx = torch.zeros(K, dtype=torch.int32, device=dev)
+            cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+            y1 = torch.zeros(N, dtype=torch.float32, device=dev)
+            y4 = torch.zeros((M, N), dtype=torch.float32, device=dev)
+            yl = torch.zeros((M, N), dtype=torch.float32, device=dev)
+        sgemv.sgemv_run_fused(pm.desc, pm.blob, xd[0], T[:1], y1, pm.workspace, stream=stream)
+        sgemv.sgemv_gather_indices(xd, T, idx, cnt, stream=stream)
+        sgemv.sgemv_run_fused(pm.desc, pm.blob, xd, T, y4, pm.workspace, stream=stream)
+        sgemv.sgemv_run_batched(pm.desc, pm.blob, xd, T, idx, cnt, yl, pm.workspace, stream=stream)
+        stream.synchronize()
+        return [a.cpu().numpy().view(np.uint32).copy() for a in (y1, y4, yl)] + [idx.cpu().numpy()[:int(cnt.item())]]
+
+    torch.cuda.synchronize()
+    ref = run(torch.cuda.current_stream())
+    side = torch.cuda.Stream()
+    got = run(side)
+    for a, b in zip(got, ref):
+        assert np.array_equal(a, b)
