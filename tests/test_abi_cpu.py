@@ -271,3 +271,30 @@ def test_partials_beyond_32bit_offsets_rejected():
     st = L.sgemv_run_fused(ctypes.byref(d), FAKE, FAKE, 16, K, t.ctypes.data, None, None, FAKE, N, 0,
                            FAKE, None)
     assert st == E.SGEMV_ESIZE
+
+
+def test_plain_c_program_against_the_abi(tmp_path):
+    """The header and library from plain C (gcc, no Python, no GPU): size
+    queries, packing of both layout versions, the header round trip,
+    workspace sizes and argument checks of the device calls; the blobs it
+    writes equal the oracle's layout specification byte for byte."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    libdir = os.path.dirname(sgemv.LIB_PATH)
+    exe = tmp_path / "c_abi_host"
+    src = os.path.join(os.path.dirname(__file__), "c_abi_host.c")
+    inc = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+    subprocess.run([gcc, "-std=c99", "-O1", "-Wall", "-Werror", "-I", inc, src, "-L", libdir, "-lsgemv",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe), str(tmp_path)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
+    N, K = 1024, 384
+    q = np.fromfile(tmp_path / "q.bin", dtype=np.uint8).reshape(N, K)
+    s = np.fromfile(tmp_path / "s.bin", dtype=np.uint16).reshape(N, K // 128)
+    z = np.fromfile(tmp_path / "z.bin", dtype=np.uint16).reshape(N, K // 128)
+    for v in (1, 2):
+        blob = np.fromfile(tmp_path / f"blob{v}.bin", dtype=np.uint8)
+        assert np.array_equal(blob, np.asarray(oracle.pack_spec(q, s, z, 512, v)))
