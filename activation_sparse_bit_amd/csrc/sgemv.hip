@@ -249,20 +249,54 @@ __global__ __launch_bounds__(1024) void k_gather(const uint16_t* __restrict__ x,
 // slice's sums, adds them in slice order and writes y, then resets the
 // counter.  Its loads must not return a stale L2 copy of another XCD's slice:
 // the one- and two-row kernels use device-scope (sc1) loads, which miss in
-// L2; the many-row kernel, whose last read is up to 16 times larger, takes a
-// device-scope acquire (dropping its XCD's L2 copies) and then uses ordinary
-// loads, which is faster there but slows the one-row kernel, where other
-// workgroups on the XCD are still streaming when it runs.  The writers need
-// no whole-L2 write-back (a device-scope release would cost about 1.7 us per
-// call): their stores write through.  The result does not depend on which
-// workgroup arrives last.
+// L2.  The many-row kernel, whose last read is up to 16 times larger, reads
+// through L2: each of its workgroups reads its XCC id and counts itself on
+// that XCD's field of the arrival word, and when every slice came from the
+// last workgroup's own XCD the write-through stores went through its L2,
+// which is then current; otherwise it first takes a device-scope acquire
+// (dropping its XCD's L2 copies, including the weights other workgroups are
+// streaming, which is why the one-row kernel does not do this).  Counting
+// by XCD cost the one-row kernel more than its L2 reads saved.  The writers
+// need no whole-L2 write-back (a device-scope release would cost about
+// 1.7 us per call): their stores write through.  The result does not depend
+// on which workgroup arrives last or where the workgroups run.
 
 constexpr int kVTile = 256;            // outputs per workgroup (half a layout tile)
 constexpr int kHalfRun = kVTile / 2;   // bytes of one column for those outputs
 constexpr uint32_t kCacheSC1 = 16;     // cache policy: coherent at device scope
+constexpr uint32_t kCacheSC0 = 1;      // cache policy: miss in the CU's L1, may hit in L2
+constexpr int kHwRegXccId = (31 << 11) | 20;   // s_getreg operand: HW_REG_XCC_ID, 32 bits
 
-// The last workgroup's view of the slices the others published (before
-// ordinary loads of them).
+// The XCD (XCC) this wavefront runs on: the low four bits of HW_REG_XCC_ID.
+__device__ __forceinline__ uint32_t xcc_id() { return __builtin_amdgcn_s_getreg(kHwRegXccId) & 0xFu; }
+
+// Counts the calling workgroup (one thread of the many-row kernel) as an
+// arrival of half tile vt, whose S slices are published, and returns 0 if
+// others are still to come,
+// 1 for the last arrival, 2 for the last arrival when every slice was
+// published from its own XCD.  The half tile's 64-bit arrival word holds the
+// count in bits 0..7 and, in the 7-bit field at 8 + 7 x, the arrivals from
+// XCD x (x < 8).  When the last workgroup's own field holds all S arrivals,
+// every slice was written through one L2, its own, so L2 reads of them are
+// current; a field that overflows (S > 127) or an id past 7 only ever gives 1.
+// A workgroup's placement on the XCDs decides speed only, never the sums.
+__device__ __forceinline__ uint32_t count_arrival(uint32_t* counters, int vt, int S) {
+    const uint32_t x = xcc_id();
+    const uint64_t add = 1ull + (x < 8u ? 1ull << (8u + 7u * x) : 0ull);
+    const uint64_t old = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(&counters[vt * kCounterStride]), add,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(old & 0xFFu) != (uint32_t)(S - 1)) return 0u;
+    return x < 8u && (((old + add) >> (8u + 7u * x)) & 0x7Fu) == (uint64_t)S ? 2u : 1u;
+}
+
+// The last arrival leaves the arrival word at zero for the next call.
+__device__ __forceinline__ void reset_arrivals(uint32_t* counters, int vt) {
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(&counters[vt * kCounterStride]), 0ull, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The last workgroup's view of the slices the others published, when some
+// came through another XCD's L2 (before loads that may hit in its own).
 __device__ __forceinline__ void acquire_slices() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -1281,16 +1315,14 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     __builtin_amdgcn_s_waitcnt(0);  // this thread's stores acknowledged
     __syncthreads();                // ... and every thread's, before the count
     if (t == 0) {
-        const uint32_t old =
-            __hip_atomic_fetch_add(&a.counters[vt * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = (old == (uint32_t)(S - 1)) ? 1u : 0u;
+        last_flag = count_arrival(a.counters, vt, S);
     }
     __syncthreads();
     if (last_flag == 0u) return;
-    acquire_slices();
+    if (last_flag == 1u) acquire_slices();
 
     // last to arrive: thread t adds row t / 32, storage 8 (t % 32) .. + 7 of
-    // every slot, in segment order, 16 slots in flight
+    // every slot, in segment order, 16 slots in flight (past the CU's L1)
     const int om = t >> 5, os = 8 * (t & 31);
     if (om < a.M) {
         const uint32_t my = ((uint32_t)om * kVTile + os) * 4u;
@@ -1301,8 +1333,8 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
             for (int i = 0; i < 16; ++i) {
                 const int sl = sb + i < S ? sb + i : sb;
                 const uint32_t off = tile_base + (uint32_t)sl * slot_bytes + my;
-                u[i][0] = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, 0);
-                u[i][1] = __builtin_amdgcn_raw_buffer_load_b128(prs, off + 16u, 0, 0);
+                u[i][0] = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, kCacheSC0);
+                u[i][1] = __builtin_amdgcn_raw_buffer_load_b128(prs, off + 16u, 0, kCacheSC0);
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -1315,7 +1347,7 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int j = 0; j < 8; ++j) put_y(om, os + j, tot[j]);
     }
-    if (t == 0) __hip_atomic_store(&a.counters[vt * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == 0) reset_arrivals(a.counters, vt);
 }
 
 // ---------------------------------------------------------------------------
