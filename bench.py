@@ -178,7 +178,7 @@ def main():
         lst = idx[:c].cpu().numpy()
         return c, touched_groups(lst)
 
-    def measure_fused(p, steps, warmup, with_list=True, latency=False):
+    def measure_fused(p, steps, warmup, with_list=True, latency=False, cold=False):
         t = synth.percentile_threshold(x, p)
         il, cl = (idx, cnt) if with_list else (None, None)
         f = lambda i: sgemv.sgemv_run_fused(desc, copies[i % R], xd, [t], y, ws, il, cl)
@@ -190,6 +190,7 @@ def main():
                "GBps": fb / (us * 1e-6) / 1e9, "frac_hbm_peak": fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
         if latency:
             out["single_call_latency_us"] = eager_latency(f)
+        if latency or cold:
             out["cold_single_call_us"] = cold_latency(f)
         return out
 
@@ -213,7 +214,7 @@ def main():
         del cps, bd
         return res
 
-    def measure_split(p, steps, warmup, dense=False):
+    def measure_split(p, steps, warmup, dense=False, cold=False):
         t = synth.percentile_threshold(x, p)
         gat = lambda i: sgemv.sgemv_gather_indices(xd, [t], idx, cnt)
         run = lambda i: sgemv.sgemv_run(desc, copies[i % R], xd, None if dense else idx,
@@ -231,6 +232,8 @@ def main():
             A, Ag = list_now()
             rb = gemv_bytes(A, Ag, N_DOWN)
             out["gather_bytes"] = gather_bytes(K_DOWN, A)
+        if cold:
+            out["cold_single_call_us"] = cold_latency(run)
         out.update({"active": A, "groups_touched": Ag, "run_us": run_us, "run_bytes": rb,
                     "run_GBps": rb / (run_us * 1e-6) / 1e9,
                     "run_frac_hbm_peak": rb / (run_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
@@ -368,12 +371,12 @@ def main():
     shapes = None
     if not args.quick:
         for p in (0.7, 0.9):
-            sweep[f"fused_p{int(p * 100)}"] = measure_fused(p, args.steps, args.warmup)
+            sweep[f"fused_p{int(p * 100)}"] = measure_fused(p, args.steps, args.warmup, cold=True)
         sweep["fused_p50_no_list"] = measure_fused(0.5, args.steps, args.warmup, with_list=False)
         sweep.update(measure_fused_z4((0.5, 0.9), args.steps, args.warmup))
         for p in (0.5, 0.7, 0.9):
             sweep[f"split_p{int(p * 100)}"] = measure_split(p, args.steps, args.warmup)
-        sweep["dense_int4"] = measure_split(0.0, args.steps, args.warmup, dense=True)
+        sweep["dense_int4"] = measure_split(0.0, args.steps, args.warmup, dense=True, cold=True)
         dense_us = sweep["dense_int4"]["us_per_step"]
         for k in ("fused_p50", "fused_p70", "fused_p90", "split_p50", "split_p70", "split_p90"):
             sweep[k]["speedup_vs_dense_int4"] = dense_us / sweep[k]["us_per_step"]
