@@ -111,10 +111,12 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    def graph_time(launches, steps, warmup):
+    def graph_time(launches, steps, warmup, spread=None, spread_replays=5):
         """Capture `steps` steps (each step calls every launch with the step
         number, on the current stream) in one HIP graph, then time one replay
-        bracketed by synchronisations.  Returns microseconds per step.  A
+        bracketed by synchronisations.  Returns microseconds per step.  With
+        a dict `spread`, `spread_replays` more replays after the timed one
+        fill it with the p10 / p50 / p90 of their microseconds per step.  A
         graph replay puts the launches back to back, as a decode loop does;
         eager Python launches would leave the GPU waiting for the host."""
         for i in range(warmup):
@@ -134,8 +136,21 @@ def main():
         g.replay()
         t1.record(cur)
         torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1000.0 / steps
+        if spread is not None:   # more replays, after the timed one, for the spread
+            per = []
+            for _ in range(spread_replays):
+                a, b = ev(), ev()
+                a.record(cur)
+                g.replay()
+                b.record(cur)
+                torch.cuda.synchronize()
+                per.append(a.elapsed_time(b) * 1000.0 / steps)
+            q = np.percentile(per, [10, 50, 90])
+            spread.update({"p10": float(q[0]), "p50": float(q[1]), "p90": float(q[2]),
+                           "replays": spread_replays, "steps_per_replay": steps})
         del g
-        return t0.elapsed_time(t1) * 1000.0 / steps
+        return us
 
     def eager_latency(launch, n=50):
         """Mean duration of single launches issued one at a time (events
@@ -182,13 +197,15 @@ def main():
         t = synth.percentile_threshold(x, p)
         il, cl = (idx, cnt) if with_list else (None, None)
         f = lambda i: sgemv.sgemv_run_fused(desc, copies[i % R], xd, [t], y, ws, il, cl)
-        us = graph_time([f], steps, warmup)
+        spread = {} if latency else None
+        us = graph_time([f], steps, warmup, spread=spread)
         sgemv.sgemv_run_fused(desc, copies[0], xd, [t], y, ws, idx, cnt)
         A, Ag = list_now()
         fb = fused_bytes(A, Ag, N_DOWN, K_DOWN, with_list=with_list)
         out = {"p": p, "active": A, "groups_touched": Ag, "us_per_step": us, "bytes": fb,
                "GBps": fb / (us * 1e-6) / 1e9, "frac_hbm_peak": fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
         if latency:
+            out["replay_spread_us_per_step"] = spread
             out["single_call_latency_us"] = eager_latency(f)
         if latency or cold:
             out["cold_single_call_us"] = cold_latency(f)
