@@ -83,7 +83,7 @@ def main():
                     help="also run a plain 256 MiB device copy three times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only (there is no multi-GPU path); use --gpus 1"}))
         sys.exit(2)
 
     import torch
