@@ -235,9 +235,11 @@ __global__ __launch_bounds__(1024) void k_gather(const uint16_t* __restrict__ x,
 // makes the fp16 values 1024 + q exactly (high nibbles: 1024 + 16 q);
 // subtracting 1024 + z (or 1024 + 16 z) in packed fp16 leaves q - z (or
 // 16 (q - z)) exactly, and v_dot2_f32_f16 adds (q_a - z) x_a + (q_b - z) x_b
-// to an fp32 sum.  All fp16 operands are normal numbers or zero: the dot
-// instruction is only used where it is accurate (with subnormal fp16 inputs
-// it is not correctly rounded).  A chunk is computed in one pass per group
+// to an fp32 sum.  The weight operands are small integers (or 16 times
+// them), exact in fp16; the activations are any finite fp16 values the
+// threshold admits, subnormal ones included: the dot instruction and the
+// matrix cores take subnormal fp16 inputs at their value (fp16 denormals are
+// on), so every product is exact in fp32.  A chunk is computed in one pass per group
 // it touches, with x masked to that group's positions, so every pass uses
 // one scale and one zero-point and runs without branches.  The scale is
 // applied once per (pass, output); the 16 of the high nibbles at the end.
