@@ -9,9 +9,12 @@
 // own CDNA4 design; the page's kernels target other GPUs and are not given.
 //
 // Kernels
-//   k_gather   one 1024-thread workgroup: per-lane 8-element masks from
-//              16-byte loads, wavefront ballots and mbcnt for in-wave ranks,
-//              an LDS scan across the 16 wavefronts, ordered index writes.
+//   k_gather   the standalone gathering step: a few workgroups, each over
+//              its own column range, with no scratch and no communication
+//              (each recounts the active columns below its range from x);
+//              per-lane 8-element masks from 16-byte loads, bit-plane
+//              ballots and mbcnt for in-wave ranks, an LDS scan across the
+//              wavefronts, ordered index writes.
 //   k_fs, k_fs4  one or two rows, fused: threshold, compaction and GEMV in
 //              one launch, one quantization group per wavefront, 8 or (one
 //              row, small or short-K matrices) 4 wavefronts per workgroup
@@ -213,11 +216,67 @@ __device__ __forceinline__ void gather_body(const uint16_t* __restrict__ x, int 
     }
 }
 
-__global__ __launch_bounds__(1024) void k_gather(const uint16_t* __restrict__ x, int M, int K, int ldx,
-                                                 Codes tc, int32_t* __restrict__ idx,
-                                                 int32_t* __restrict__ count) {
-    __shared__ GatherShared gs;
-    gather_body<16>(x, M, K, ldx, tc, idx, count, gs);
+// The standalone gathering step over several workgroups, with no scratch
+// memory and no communication between them.  Workgroup j owns the columns
+// j R .. j R + R - 1 (R = 8 x its thread count, one 8-column chunk per
+// thread).  Its threads first count the union's active columns below j R
+// straight from x (every earlier range is read again; x is small, and the
+// loads are all in flight with the workgroup's own ones), then rank their own
+// chunk's columns with bit-plane ballots and an LDS scan of the wavefront
+// totals, and write them at that count plus their rank.  The last workgroup
+// also writes the count.  Deterministic, and nothing past the count is
+// touched.
+template <int WW>
+__global__ __launch_bounds__(WW * 64) void k_gather(const uint16_t* __restrict__ x, int M, int K, int ldx, Codes tc,
+                                                    int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+    constexpr int T = WW * 64;
+    constexpr int R = 8 * T;
+    __shared__ uint32_t wsum[WW], wtot[WW];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int k0 = blockIdx.x * R;
+    // the chunk of this thread (columns k0 + 8 t ..), if inside K
+    const int own = k0 + 8 * t;
+    uint32_t m8 = 0;
+    if (own < K)
+        m8 = M >= 8 ? union_mask8<8>(x, M, ldx, own, tc)
+           : M >= 4 ? union_mask8<4>(x, M, ldx, own, tc)
+                    : union_mask8<1>(x, M, ldx, own, tc);
+    // active columns below k0: chunks t, t + T, ... of [0, k0)
+    uint32_t below = 0;
+    for (int c = 8 * t; c < k0; c += 8 * T) {
+        const uint32_t u = M >= 8 ? union_mask8<8>(x, M, ldx, c, tc)
+                         : M >= 4 ? union_mask8<4>(x, M, ldx, c, tc)
+                                  : union_mask8<1>(x, M, ldx, c, tc);
+        below += (uint32_t)__popc(u);
+    }
+    // wavefront sums (butterfly over the 64 lanes), then the workgroup's
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) below += (uint32_t)__shfl_xor((int)below, d);
+    uint32_t pre, tot;
+    wave_scan16((uint32_t)__popc(m8), pre, tot);
+    if (lane == 0) {
+        wsum[wave] = below;
+        wtot[wave] = tot;
+    }
+    __syncthreads();
+    uint32_t base = 0, grand = 0;
+#pragma unroll
+    for (int w = 0; w < WW; ++w) {
+        base += wsum[w] + (w < wave ? wtot[w] : 0u);
+        grand += wtot[w];
+    }
+    if (blockIdx.x == gridDim.x - 1 && t == 0) {
+        uint32_t all = grand;
+#pragma unroll
+        for (int w = 0; w < WW; ++w) all += wsum[w];
+        *count = (int32_t)all;
+    }
+    uint32_t pos = base + pre;
+    while (m8) {
+        const int b = __builtin_ctz(m8);
+        idx[pos++] = own + b;
+        m8 &= m8 - 1u;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1579,6 +1638,9 @@ extern "C" int sgemv_run_fused(const sgemv_desc* d, const void* packed, const vo
     return run_fused(d, packed, x_f16, M, ldx, thresholds, idx, count, y, ldy, flags, workspace, stream);
 }
 
+// Rows x columns up to which the gathering uses 512-thread workgroups.
+constexpr long kGatherSmall = 2L * 16384;
+
 extern "C" int sgemv_gather_indices(const void* x_f16, int32_t M, int32_t K, int32_t ldx,
                                     const float* thresholds, int32_t* idx, int32_t* count,
                                     void* stream) {
@@ -1590,8 +1652,17 @@ extern "C" int sgemv_gather_indices(const void* x_f16, int32_t M, int32_t K, int
     Codes c;
     int st = fill_codes(thresholds, M, c);
     if (st) return st;
-    hipLaunchKernelGGL(k_gather, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const uint16_t*>(x_f16), (int)M, (int)K, (int)ldx, c, idx, count);
+    // 4096 columns per workgroup of 512 threads; with many rows (every
+    // workgroup rereads all earlier rows and columns) 8192 per workgroup of
+    // 1024, which halves the rereading
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* xp = static_cast<const uint16_t*>(x_f16);
+    if ((long)M * K <= kGatherSmall)
+        hipLaunchKernelGGL(k_gather<8>, dim3((K + 4095) / 4096), dim3(512), 0, s, xp, (int)M, (int)K, (int)ldx, c,
+                           idx, count);
+    else
+        hipLaunchKernelGGL(k_gather<16>, dim3((K + 8191) / 8192), dim3(1024), 0, s, xp, (int)M, (int)K, (int)ldx,
+                           c, idx, count);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         g_last_hip_error = (int)e;

@@ -166,8 +166,11 @@ int sgemv_desc_from_header(const void* header, size_t bytes, sgemv_desc* desc_ou
  * sgemv_gather_indices - the run-time step of the page's Abstract that
  * collects the indices of the surviving activations at low cost: threshold
  * every row, OR the rows' masks, and compact the union into an ascending
- * list.  One workgroup of 16 wavefronts: wavefront ballots and
- * bit counts give each lane its rank, an LDS scan orders the wavefronts.
+ * list.  A few workgroups (one per 4096 columns, or per 8192 with more
+ * rows), each over its own column range; every workgroup counts the active
+ * columns below its range straight from x, so they need no scratch memory
+ * and no communication; wavefront ballots and bit counts give each lane its
+ * rank, an LDS scan orders the wavefronts.
  *
  *   x_f16      device fp16 [M][ldx]; 16-byte aligned
  *   M          rows, 1..SGEMV_MAX_BATCH
