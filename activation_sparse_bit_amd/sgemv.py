@@ -30,7 +30,8 @@ SGEMV_MAX_BATCH = 16
 SGEMV_MAX_K = 65536
 SGEMV_MAX_N = 1 << 20
 
-EXPORTED = ["sgemv_pack_layout", "sgemv_pack_layout_z4", "sgemv_desc_from_header", "sgemv_gather_indices",
+EXPORTED = ["sgemv_pack_layout", "sgemv_pack_layout_z4", "sgemv_pack_layout_parts", "sgemv_desc_from_header",
+            "sgemv_gather_indices",
             "sgemv_run", "sgemv_run_batched", "sgemv_run_fused", "sgemv_workspace_bytes",
             "sgemv_strerror", "sgemv_last_hip_error"]
 
@@ -70,6 +71,8 @@ def lib():
     L.sgemv_pack_layout.restype = ctypes.c_int
     L.sgemv_pack_layout_z4.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, sz, pd]
     L.sgemv_pack_layout_z4.restype = ctypes.c_int
+    L.sgemv_pack_layout_parts.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, u32, vp, sz, pd]
+    L.sgemv_pack_layout_parts.restype = ctypes.c_int
     L.sgemv_desc_from_header.argtypes = [vp, sz, pd]
     L.sgemv_desc_from_header.restype = ctypes.c_int
     L.sgemv_gather_indices.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
@@ -117,6 +120,71 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
+def _require(t, what: str, dtypes, min_numel: int, rows: int | None = None):
+    """Check a device buffer before its address crosses the ABI: a torch
+    tensor of one of `dtypes` holding at least `min_numel` elements, its last
+    dimension contiguous (and, for `rows`, 1-D or 2-D with that many rows),
+    (the device is checked by _require_gpu, after every other check of a
+    call).  A plain integer is taken as a raw device address and passed
+    through unchecked.  Raises ValueError on the first failed check, before
+    any library call."""
+    if isinstance(t, int):
+        return
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{what}: expected a torch tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        names = ", ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{what}: dtype {str(t.dtype).replace('torch.', '')}, expected {names}")
+    if rows is not None:
+        if t.dim() not in (1, 2) or (t.dim() == 2 and t.shape[0] != rows) or (t.dim() == 1 and rows != 1):
+            raise ValueError(f"{what}: shape {tuple(t.shape)}, expected [{rows}][...] rows")
+    if t.dim() >= 1 and t.numel() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{what}: the last dimension must be contiguous")
+    if t.dim() == 2 and t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        raise ValueError(f"{what}: rows overlap (stride {t.stride(0)} < {t.shape[1]})")
+    if rows is None and t.dim() > 1 and not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if t.numel() < min_numel:
+        raise ValueError(f"{what}: {t.numel()} elements, at least {min_numel} needed")
+
+
+def _require_gpu(**bufs):
+    """Every tensor among `bufs` (name=tensor; None and raw addresses are
+    skipped) lives on a GPU."""
+    import torch
+    for what, t in bufs.items():
+        if isinstance(t, torch.Tensor) and not t.is_cuda:
+            raise ValueError(f"{what}: must be a GPU tensor")
+
+
+def _f16():
+    import torch
+    return (torch.float16,)
+
+
+def _i32():
+    import torch
+    return (torch.int32,)
+
+
+def _u8():
+    import torch
+    return (torch.uint8,)
+
+
+def _yt():
+    import torch
+    return (torch.float16, torch.float32)
+
+
+def _require_matrix(desc: "Desc", packed, workspace, M: int):
+    _require(packed, "packed", _u8(), int(desc.total_bytes))
+    if workspace is None:   # the library says whether the call needs one (SGEMV_EINVAL)
+        return
+    _require(workspace, "workspace", _u8(), sgemv_workspace_bytes(desc, M))
+
+
 def _thresholds(t, M):
     if t is None:
         return None
@@ -161,6 +229,40 @@ def sgemv_pack_layout_z4(q, scales_f16, zeros_f16, tile_n: int = SGEMV_TILE_N):
     return sgemv_pack_layout(q, scales_f16, zeros_f16, tile_n, _which="sgemv_pack_layout_z4")
 
 
+def sgemv_pack_layout_parts(parts, tile_n: int = SGEMV_TILE_N, version: int = SGEMV_LAYOUT_PAIRS):
+    """One blob for several projections sharing their input, rows stacked in
+    the order given.  `parts` is a list of (q, scales_f16, zeros_f16), each
+    with a row count that is a multiple of tile_n and the same K.  Returns
+    (Desc, uint8 blob)."""
+    qs, ss, zs, ns = [], [], [], []
+    for q, s_, z in parts:
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        s_ = np.asarray(s_)
+        z = np.asarray(z)
+        s_ = np.ascontiguousarray(s_.view(np.uint16) if s_.dtype == np.float16 else s_, dtype=np.uint16)
+        z = np.ascontiguousarray(z.view(np.uint16) if z.dtype == np.float16 else z, dtype=np.uint16)
+        if s_.shape != (q.shape[0], q.shape[1] // SGEMV_GROUP) or z.shape != s_.shape:
+            raise ValueError("scales/zeros must be [N][K/128] of their part")
+        qs.append(q); ss.append(s_); zs.append(z); ns.append(q.shape[0])
+    Ks = {q.shape[1] for q in qs}
+    if len(Ks) != 1:
+        raise ValueError("parts must share K")
+    K = Ks.pop()
+    n = len(qs)
+    qa = (ctypes.c_void_p * n)(*[a.ctypes.data for a in qs])
+    sa = (ctypes.c_void_p * n)(*[a.ctypes.data for a in ss])
+    za = (ctypes.c_void_p * n)(*[a.ctypes.data for a in zs])
+    na = np.ascontiguousarray(ns, dtype=np.int32)
+    d = Desc()
+    L = lib()
+    _check(L.sgemv_pack_layout_parts(n, None, None, None, na.ctypes.data, K, SGEMV_GROUP, tile_n, version,
+                                     None, 0, ctypes.byref(d)), "sgemv_pack_layout_parts(size)")
+    blob = np.empty(d.total_bytes, dtype=np.uint8)
+    _check(L.sgemv_pack_layout_parts(n, qa, sa, za, na.ctypes.data, K, SGEMV_GROUP, tile_n, version,
+                                     blob.ctypes.data, blob.nbytes, ctypes.byref(d)), "sgemv_pack_layout_parts")
+    return d, blob
+
+
 def sgemv_desc_from_header(blob) -> Desc:
     b = np.ascontiguousarray(np.asarray(blob, dtype=np.uint8)[:64])
     d = Desc()
@@ -175,6 +277,12 @@ def sgemv_gather_indices(x, thresholds, idx, count, K: int | None = None, stream
     M = 1 if x.dim() == 1 else x.shape[0]
     ldx = x.shape[-1] if x.dim() == 1 else x.stride(0)
     K = x.shape[-1] if K is None else K
+    _require(x, "x", _f16(), K, rows=M)
+    if K > x.shape[-1]:
+        raise ValueError(f"x: {x.shape[-1]} columns, K = {K}")
+    _require(idx, "idx", _i32(), K)
+    _require(count, "count", _i32(), 1)
+    _require_gpu(x=x, idx=idx, count=count)
     t = _thresholds(thresholds, M)
     _check(lib().sgemv_gather_indices(_ptr(x), M, K, ldx, _ptr(t), _ptr(idx), _ptr(count),
                                       _stream(stream)), "sgemv_gather_indices")
@@ -191,6 +299,13 @@ def _flags(y):
 
 def sgemv_run(desc: Desc, packed, x, idx, count, y, workspace, stream=None):
     """y = W . x over idx[:count] (idx None: all columns)."""
+    _require_matrix(desc, packed, workspace, 1)
+    _require(x, "x", _f16(), desc.K)
+    if idx is not None or count is not None:
+        _require(idx, "idx", _i32(), desc.K)
+        _require(count, "count", _i32(), 1)
+    _require(y, "y", _yt(), desc.N)
+    _require_gpu(packed=packed, workspace=workspace, x=x, idx=idx, count=count, y=y)
     _check(lib().sgemv_run(ctypes.byref(desc), _ptr(packed), _ptr(x), _ptr(idx), _ptr(count),
                            _ptr(y), _flags(y), _ptr(workspace), _stream(stream)), "sgemv_run")
 
@@ -198,6 +313,15 @@ def sgemv_run(desc: Desc, packed, x, idx, count, y, workspace, stream=None):
 def sgemv_run_batched(desc: Desc, packed, x, thresholds, idx, count, y, workspace, stream=None):
     """y[m] = W . xe[m] over the union list; x is [M][ldx], y is [M][ldy]."""
     M = x.shape[0]
+    _require_matrix(desc, packed, workspace, M)
+    _require(x, "x", _f16(), desc.K, rows=M)
+    _require(y, "y", _yt(), desc.N, rows=M)
+    if x.shape[-1] < desc.K or y.shape[-1] < desc.N:
+        raise ValueError(f"x/y: rows of {x.shape[-1]}/{y.shape[-1]}, need K = {desc.K} and N = {desc.N}")
+    if idx is not None or count is not None:
+        _require(idx, "idx", _i32(), desc.K)
+        _require(count, "count", _i32(), 1)
+    _require_gpu(packed=packed, workspace=workspace, x=x, idx=idx, count=count, y=y)
     t = _thresholds(thresholds, M)
     _check(lib().sgemv_run_batched(ctypes.byref(desc), _ptr(packed), _ptr(x), M, x.stride(0),
                                    _ptr(t), _ptr(idx), _ptr(count), _ptr(y), y.stride(0),
@@ -213,6 +337,17 @@ def sgemv_run_fused(desc: Desc, packed, x, thresholds, y, workspace, idx=None, c
     M = 1 if x.dim() == 1 else x.shape[0]
     ldx = desc.K if x.dim() == 1 else x.stride(0)
     ldy = desc.N if y.dim() == 1 else y.stride(0)
+    _require_matrix(desc, packed, workspace, M)
+    _require(x, "x", _f16(), desc.K, rows=M)
+    _require(y, "y", _yt(), desc.N, rows=M)
+    if x.shape[-1] < desc.K or y.shape[-1] < desc.N:
+        raise ValueError(f"x/y: rows of {x.shape[-1]}/{y.shape[-1]}, need K = {desc.K} and N = {desc.N}")
+    if (idx is None) != (count is None):
+        raise ValueError("idx and count: both or neither")
+    if idx is not None:
+        _require(idx, "idx", _i32(), desc.K)
+        _require(count, "count", _i32(), 1)
+    _require_gpu(packed=packed, workspace=workspace, x=x, idx=idx, count=count, y=y)
     t = _thresholds(thresholds, M)
     _check(lib().sgemv_run_fused(ctypes.byref(desc), _ptr(packed), _ptr(x), M, ldx, _ptr(t),
                                  _ptr(idx), _ptr(count), _ptr(y), ldy, _flags(y),
@@ -234,14 +369,23 @@ class PackedMatrix:
     """A packed matrix on the device with its workspace (torch tensors)."""
 
     def __init__(self, q, scales_f16, zeros_f16, device="cuda", max_batch: int = SGEMV_MAX_BATCH,
-                 z4: bool = False):
+                 z4: bool = False, _packed=None):
         import torch
-        pack = sgemv_pack_layout_z4 if z4 else sgemv_pack_layout
-        self.desc, blob = pack(q, scales_f16, zeros_f16)
+        if _packed is None:
+            pack = sgemv_pack_layout_z4 if z4 else sgemv_pack_layout
+            _packed = pack(q, scales_f16, zeros_f16)
+        self.desc, blob = _packed
         self.blob = torch.from_numpy(blob).to(device)
         self.workspace = torch.zeros(max(sgemv_workspace_bytes(self.desc, max_batch), 256),
                                      dtype=torch.uint8, device=device)
         self.N, self.K = self.desc.N, self.desc.K
+
+    @classmethod
+    def from_parts(cls, parts, device="cuda", max_batch: int = SGEMV_MAX_BATCH, z4: bool = False):
+        """Several projections sharing their input as one matrix (rows
+        stacked in order), packed by sgemv_pack_layout_parts."""
+        packed = sgemv_pack_layout_parts(parts, version=SGEMV_LAYOUT_Z4 if z4 else SGEMV_LAYOUT_PAIRS)
+        return cls(None, None, None, device=device, max_batch=max_batch, z4=z4, _packed=packed)
 
 
 class FusedProjections:
@@ -267,10 +411,7 @@ class FusedProjections:
                 raise ValueError(f"{name}: N = {n} is not a multiple of {SGEMV_TILE_N}")
             self.offsets[name] = (start, n)
             start += n
-        q = np.concatenate([np.asarray(p[1], dtype=np.uint8) for p in parts])
-        s = np.concatenate([np.asarray(p[2]).view(np.uint16) for p in parts])
-        z = np.concatenate([np.asarray(p[3]).view(np.uint16) for p in parts])
-        self.matrix = PackedMatrix(q, s, z, device=device, max_batch=max_batch, z4=z4)
+        self.matrix = PackedMatrix.from_parts([p[1:] for p in parts], device=device, max_batch=max_batch, z4=z4)
         self.N, self.K = self.matrix.N, self.matrix.K
 
     def split(self, y):
