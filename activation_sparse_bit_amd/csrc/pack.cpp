@@ -63,9 +63,41 @@ static int check_shape(int32_t N, int32_t K, int32_t group, int32_t tile_n) {
     return SGEMV_OK;
 }
 
-static int pack(const uint8_t* q, const uint16_t* scales_f16, const uint16_t* zeros_f16, int32_t N,
-                int32_t K, int32_t group, int32_t tile_n, uint32_t version, void* out, size_t out_capacity,
-                sgemv_desc* desc_out) {
+// The rows of the matrix being packed: one or more parts stacked along N
+// (part p holds rows n_part[p] of its own [rows][K] codes and [rows][K/128]
+// scales and zero-points).
+struct Rows {
+    int32_t parts;
+    const uint8_t* const* q;
+    const uint16_t* const* s;
+    const uint16_t* const* z;
+    const int32_t* n_part;
+
+    // part and row within it of matrix row n
+    void locate(uint64_t n, int32_t& p, uint64_t& r) const {
+        p = 0;
+        r = n;
+        while (p + 1 < parts && r >= (uint64_t)n_part[p]) r -= (uint64_t)n_part[p++];
+    }
+    const uint8_t* qrow(uint64_t n, int32_t K) const {
+        int32_t p; uint64_t r;
+        locate(n, p, r);
+        return q[p] + r * (uint64_t)K;
+    }
+    uint16_t scale(uint64_t n, int32_t Gk, int32_t g) const {
+        int32_t p; uint64_t r;
+        locate(n, p, r);
+        return s[p][r * Gk + g];
+    }
+    uint16_t zero(uint64_t n, int32_t Gk, int32_t g) const {
+        int32_t p; uint64_t r;
+        locate(n, p, r);
+        return z[p][r * Gk + g];
+    }
+};
+
+static int pack(const Rows& src, int32_t N, int32_t K, int32_t group, int32_t tile_n, uint32_t version, void* out,
+                size_t out_capacity, sgemv_desc* desc_out) {
     int st = check_shape(N, K, group, tile_n);
     if (st) return st;
     sgemv_desc d;
@@ -74,16 +106,20 @@ static int pack(const uint8_t* q, const uint16_t* scales_f16, const uint16_t* ze
         if (desc_out) *desc_out = d;
         return SGEMV_OK;
     }
-    if (!q || !scales_f16 || !zeros_f16) return SGEMV_EINVAL;
+    for (int32_t p = 0; p < src.parts; ++p)
+        if (!src.q[p] || !src.s[p] || !src.z[p]) return SGEMV_EINVAL;
     if (out_capacity < d.total_bytes) return SGEMV_ESIZE;
 
     const int32_t Gk = K / SGEMV_GROUP;
     // Validate every input before writing anything.
-    for (uint64_t i = 0, e = (uint64_t)N * K; i < e; ++i)
-        if (q[i] > 15) return SGEMV_EINVAL;
-    for (uint64_t i = 0, e = (uint64_t)N * Gk; i < e; ++i) {
-        if (!fp16_is_finite(scales_f16[i])) return SGEMV_EINVAL;
-        if (fp16_small_int(zeros_f16[i]) < 0) return SGEMV_EINVAL;
+    for (uint64_t n = 0; n < (uint64_t)N; ++n) {
+        const uint8_t* qr = src.qrow(n, K);
+        for (int32_t k = 0; k < K; ++k)
+            if (qr[k] > 15) return SGEMV_EINVAL;
+        for (int32_t g = 0; g < Gk; ++g) {
+            if (!fp16_is_finite(src.scale(n, Gk, g))) return SGEMV_EINVAL;
+            if (fp16_small_int(src.zero(n, Gk, g)) < 0) return SGEMV_EINVAL;
+        }
     }
 
     uint8_t* blob = static_cast<uint8_t*>(out);
@@ -101,10 +137,9 @@ static int pack(const uint8_t* q, const uint16_t* scales_f16, const uint16_t* ze
     const int32_t half = tile_n / 2;
     uint8_t* wr = blob + d.w_off;
     for (int32_t t = 0; t < T; ++t) {
-        const uint8_t* qt = q + (uint64_t)t * tile_n * K;
         for (int32_t j = 0; j < half; ++j) {
-            const uint8_t* r0 = qt + (uint64_t)(2 * j) * K;      // even row
-            const uint8_t* r1 = r0 + K;                          // odd row
+            const uint8_t* r0 = src.qrow((uint64_t)t * tile_n + 2 * j, K);       // even row
+            const uint8_t* r1 = src.qrow((uint64_t)t * tile_n + 2 * j + 1, K);   // odd row
             uint8_t* dst = wr + (uint64_t)t * K * half + j;
             for (int32_t k = 0; k < K; ++k)
                 dst[(uint64_t)k * half] = (uint8_t)(r0[k] | (r1[k] << 4));
@@ -119,10 +154,10 @@ static int pack(const uint8_t* q, const uint16_t* scales_f16, const uint16_t* ze
                 uint8_t* r = blob + d.m_off + ((uint64_t)t * Gk + g) * run;
                 for (int32_t i = 0; i < tile_n; ++i) {
                     const uint64_t n = (uint64_t)t * tile_n + i;
-                    const uint16_t sb = scales_f16[n * Gk + g];
+                    const uint16_t sb = src.scale(n, Gk, g);
                     r[2 * i] = (uint8_t)(sb & 0xFF);
                     r[2 * i + 1] = (uint8_t)(sb >> 8);
-                    const uint8_t z = (uint8_t)fp16_small_int(zeros_f16[n * Gk + g]);
+                    const uint8_t z = (uint8_t)fp16_small_int(src.zero(n, Gk, g));
                     r[2 * tile_n + i / 2] |= (uint8_t)(z << (4 * (i & 1)));
                 }
             }
@@ -134,8 +169,8 @@ static int pack(const uint8_t* q, const uint16_t* scales_f16, const uint16_t* ze
                 const uint64_t n = (uint64_t)t * tile_n + i;
                 for (int32_t g = 0; g < Gk; ++g) {
                     const uint64_t o = (((uint64_t)t * Gk + g) * tile_n + i) * 2;
-                    md[o] = scales_f16[n * Gk + g];
-                    md[o + 1] = zeros_f16[n * Gk + g];
+                    md[o] = src.scale(n, Gk, g);
+                    md[o + 1] = src.zero(n, Gk, g);
                 }
             }
     }
@@ -147,15 +182,35 @@ extern "C" int sgemv_pack_layout(const uint8_t* q, const uint16_t* scales_f16,
                                  const uint16_t* zeros_f16, int32_t N, int32_t K,
                                  int32_t group, int32_t tile_n, void* out,
                                  size_t out_capacity, sgemv_desc* desc_out) {
-    return pack(q, scales_f16, zeros_f16, N, K, group, tile_n, SGEMV_LAYOUT_PAIRS, out, out_capacity,
-                desc_out);
+    const Rows src{1, &q, &scales_f16, &zeros_f16, &N};
+    return pack(src, N, K, group, tile_n, SGEMV_LAYOUT_PAIRS, out, out_capacity, desc_out);
 }
 
 extern "C" int sgemv_pack_layout_z4(const uint8_t* q, const uint16_t* scales_f16,
                                     const uint16_t* zeros_f16, int32_t N, int32_t K,
                                     int32_t group, int32_t tile_n, void* out,
                                     size_t out_capacity, sgemv_desc* desc_out) {
-    return pack(q, scales_f16, zeros_f16, N, K, group, tile_n, SGEMV_LAYOUT_Z4, out, out_capacity, desc_out);
+    const Rows src{1, &q, &scales_f16, &zeros_f16, &N};
+    return pack(src, N, K, group, tile_n, SGEMV_LAYOUT_Z4, out, out_capacity, desc_out);
+}
+
+extern "C" int sgemv_pack_layout_parts(int32_t parts, const uint8_t* const* q,
+                                       const uint16_t* const* scales_f16,
+                                       const uint16_t* const* zeros_f16, const int32_t* n_part,
+                                       int32_t K, int32_t group, int32_t tile_n, uint32_t version,
+                                       void* out, size_t out_capacity, sgemv_desc* desc_out) {
+    if (parts < 1 || !n_part) return SGEMV_EINVAL;
+    if (version != SGEMV_LAYOUT_PAIRS && version != SGEMV_LAYOUT_Z4) return SGEMV_EINVAL;
+    if (out && (!q || !scales_f16 || !zeros_f16)) return SGEMV_EINVAL;
+    int64_t N = 0;
+    for (int32_t p = 0; p < parts; ++p) {
+        // every part whole tiles, so that no tile mixes two parts
+        if (n_part[p] <= 0 || tile_n <= 0 || n_part[p] % tile_n) return SGEMV_ESIZE;
+        N += n_part[p];
+    }
+    if (N > SGEMV_MAX_N) return SGEMV_ESIZE;
+    const Rows src{parts, q, scales_f16, zeros_f16, n_part};
+    return pack(src, (int32_t)N, K, group, tile_n, version, out, out_capacity, desc_out);
 }
 
 extern "C" int sgemv_desc_from_header(const void* header, size_t bytes, sgemv_desc* desc_out) {

@@ -1517,7 +1517,7 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
     if (ldx < d->K || ldy < d->N) return SGEMV_ESIZE;
     if (ldx % 8 || ldy % 8) return SGEMV_EALIGN;
     if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16)) return SGEMV_EALIGN;
-    if (idx && !aligned(idx, 16)) return SGEMV_EALIGN;
+    if (idx && !aligned(idx, 4)) return SGEMV_EALIGN;
     if (count && !aligned(count, 4)) return SGEMV_EALIGN;
     if (!idx)   // every column: the fused kernels with the whole list, which stream faster
         return run_fused(d, packed, x, M, ldx, thr, nullptr, nullptr, y, ldy, flags, ws, stream, true);

@@ -157,6 +157,36 @@ int sgemv_pack_layout_z4(const uint8_t* q, const uint16_t* scales_f16,
                          int32_t group, int32_t tile_n, void* out,
                          size_t out_capacity, sgemv_desc* desc_out);
 
+/*
+ * sgemv_pack_layout_parts - one blob for several projections that read the
+ * same activations (the query, key and value projections of an attention
+ * block; the gate and up projections of a gated feed-forward block), their
+ * rows stacked along N in the order given, so that one device call
+ * thresholds x once and computes all of them.  The blob is exactly the one
+ * sgemv_pack_layout (version SGEMV_LAYOUT_PAIRS) or sgemv_pack_layout_z4
+ * (SGEMV_LAYOUT_Z4) writes for the row-concatenated matrix; projection p's
+ * outputs are y[off_p .. off_p + n_part[p]) with off_p the sum of the
+ * earlier n_part.  Host only, no HIP call.
+ *
+ *   parts      number of projections, >= 1
+ *   q          host array of `parts` pointers, part p: uint8 [n_part[p]][K]
+ *   scales_f16 host array of `parts` pointers, part p: uint16 [n_part[p]][K/128]
+ *   zeros_f16  likewise for the zero-points
+ *   n_part     host int32 [parts]: rows of each part, each a multiple of
+ *              tile_n (no tile mixes two projections)
+ *   K, group, tile_n, out, out_capacity, desc_out as for sgemv_pack_layout
+ *   version    SGEMV_LAYOUT_PAIRS or SGEMV_LAYOUT_Z4
+ * Returns SGEMV_OK; EINVAL for parts < 1, NULL arrays or parts, a bad code,
+ * scale or zero-point, a bad version; ESIZE for a part that is not whole
+ * tiles, a total N out of range, or too small a capacity.  With out == NULL
+ * it is a size query (q, scales and zeros may then be NULL).
+ */
+int sgemv_pack_layout_parts(int32_t parts, const uint8_t* const* q,
+                            const uint16_t* const* scales_f16,
+                            const uint16_t* const* zeros_f16, const int32_t* n_part,
+                            int32_t K, int32_t group, int32_t tile_n, uint32_t version,
+                            void* out, size_t out_capacity, sgemv_desc* desc_out);
+
 /* Parse and check the 64-byte header of a blob held in host memory (for a
  * blob that was saved and reloaded; version 1 or 2).  EINVAL on a bad magic,
  * version or inconsistent offsets. */
@@ -200,7 +230,7 @@ int sgemv_gather_indices(const void* x_f16, int32_t M, int32_t K, int32_t ldx,
  *   d          host description of the packed matrix (tile_n = 512)
  *   packed     device blob from sgemv_pack_layout, 256-byte aligned
  *   x_f16      device fp16 [K], 16-byte aligned
- *   idx        device int32 buffer of K entries, 16-byte aligned, whose
+ *   idx        device int32 buffer of K entries, 4-byte aligned, whose
  *              first *count entries are ascending, unique and < K (as
  *              produced by sgemv_gather_indices); or NULL for all columns.
  *              Entries beyond *count may hold anything.

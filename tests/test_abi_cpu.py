@@ -67,6 +67,50 @@ def test_packer_z4_matches_spec(N, K, tile):
     assert b0[d.m_off + 2 * tile] & 0x0F == 0
 
 
+@pytest.mark.parametrize("version", [1, 2])
+@pytest.mark.parametrize("rows,tile", [((512, 1024, 512), 512), ((1024,), 512), ((256, 64, 128), 64)])
+def test_packer_parts_matches_spec(rows, tile, version):
+    """Projections packed as parts: byte for byte the layout specification
+    of the row-concatenated matrix."""
+    K = 384
+    parts = [synth.random_int4_problem(31 * i + n, n, K) for i, n in enumerate(rows)]
+    d, blob = sgemv.sgemv_pack_layout_parts(parts, tile_n=tile, version=version)
+    q = np.concatenate([p[0] for p in parts])
+    s = np.concatenate([p[1] for p in parts])
+    z = np.concatenate([p[2] for p in parts])
+    ref = oracle.pack_spec(q, s, z, tile, version)
+    assert blob.shape == ref.shape and np.array_equal(blob, ref)
+    assert d.N == sum(rows) and d.version == version
+
+
+def test_packer_parts_validation():
+    L = sgemv.lib()
+    E = sgemv
+    K = 256
+    q, s, z = synth.random_int4_problem(1, 512, K)
+    qa = (ctypes.c_void_p * 1)(q.ctypes.data)
+    sa = (ctypes.c_void_p * 1)(s.ctypes.data)
+    za = (ctypes.c_void_p * 1)(z.ctypes.data)
+    d = sgemv.Desc()
+    n_ok = np.array([512], dtype=np.int32)
+    n_bad = np.array([384], dtype=np.int32)       # not whole 512-row tiles
+    f = L.sgemv_pack_layout_parts
+    assert f(0, qa, sa, za, n_ok.ctypes.data, K, 128, 512, 1, None, 0, ctypes.byref(d)) == E.SGEMV_EINVAL
+    assert f(1, qa, sa, za, None, K, 128, 512, 1, None, 0, ctypes.byref(d)) == E.SGEMV_EINVAL
+    assert f(1, qa, sa, za, n_ok.ctypes.data, K, 128, 512, 3, None, 0, ctypes.byref(d)) == E.SGEMV_EINVAL
+    assert f(1, qa, sa, za, n_bad.ctypes.data, K, 128, 512, 1, None, 0, ctypes.byref(d)) == E.SGEMV_ESIZE
+    assert f(1, qa, sa, za, n_ok.ctypes.data, K, 128, 512, 1, None, 0, ctypes.byref(d)) == E.SGEMV_OK
+    blob = np.empty(d.total_bytes, dtype=np.uint8)
+    assert f(1, qa, sa, za, n_ok.ctypes.data, K, 128, 512, 1, blob.ctypes.data, blob.nbytes - 1,
+             ctypes.byref(d)) == E.SGEMV_ESIZE
+    assert f(1, None, sa, za, n_ok.ctypes.data, K, 128, 512, 1, blob.ctypes.data, blob.nbytes,
+             ctypes.byref(d)) == E.SGEMV_EINVAL
+    q2 = q.copy(); q2[3, 7] = 16
+    qb = (ctypes.c_void_p * 1)(q2.ctypes.data)
+    assert f(1, qb, sa, za, n_ok.ctypes.data, K, 128, 512, 1, blob.ctypes.data, blob.nbytes,
+             ctypes.byref(d)) == E.SGEMV_EINVAL
+
+
 def test_packer_quantized_weights():
     q, s, z = synth.quantized_weights(3, 1024, 2048, 0.02)
     d, blob = sgemv.sgemv_pack_layout(q, s, z)
@@ -165,6 +209,7 @@ def test_run_validation():
     assert L.sgemv_run(pd, FAKE + 16, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == E.SGEMV_EALIGN
     assert L.sgemv_run(pd, FAKE, FAKE + 2, FAKE, FAKE, FAKE, 0, FAKE, None) == E.SGEMV_EALIGN
     assert L.sgemv_run(pd, FAKE, FAKE, FAKE, FAKE, FAKE + 4, 0, FAKE, None) == E.SGEMV_EALIGN
+    assert L.sgemv_run(pd, FAKE, FAKE, FAKE + 2, FAKE, FAKE, 0, FAKE, None) == E.SGEMV_EALIGN   # idx: 4 bytes
     assert L.sgemv_run(pd, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE + 64, None) == E.SGEMV_EALIGN
     # a description the kernels do not run, and inconsistent ones
     d2 = _desc(N=4096, K=14336, tile=256)
