@@ -1,4 +1,5 @@
-"""Compile the HIP library ``lib/libsgemv.so`` in-tree for gfx950.
+"""Compile the HIP library ``lib/libsgemv.so`` (and the measurement-only
+``lib/libsgemv_bench.so``) in-tree for gfx950.
 
 The host packer (pack.cpp) is plain C++ built with g++; the kernels and the
 C ABI (sgemv.hip) are built with hipcc for gfx950.  All HIP code is
@@ -17,6 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsgemv.so")
+BENCH_LIB = os.path.join(LIBDIR, "libsgemv_bench.so")   # measurement-only read kernels
 
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -56,6 +58,12 @@ def build(verbose: bool = False) -> str:
     _run([_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", sgemv_o, pack_o,
           "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    # the measurement kernels (memory ceilings), a library of their own
+    bench_o = os.path.join(obj_dir, "bench_read.o")
+    _run([_hipcc(), *HIP_FLAGS, "-c", os.path.join(CSRC, "bench_read.hip"), "-o", bench_o], verbose)
+    tmp = BENCH_LIB + ".tmp"
+    _run([_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", bench_o, "-o", tmp], verbose)
+    os.replace(tmp, BENCH_LIB)
     return LIB
 
 

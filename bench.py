@@ -13,14 +13,19 @@ One step = one pass of the hot path on one activation vector: threshold,
 compact into the ascending list of active indices (written, with its
 count) and the sparse GEMV over those columns - one launch of
 sgemv_run_fused.  Every call reads the weights of the next of R packed
-copies whose total exceeds 1 GiB, so neither the L2 nor the 256 MB
-Infinity Cache can serve them.  Inputs are resident in HBM before timing.
+copies, R chosen so that at least 1 GiB of other weight bytes is read
+between two uses of one copy, and a 1 GiB read of a scratch buffer precedes
+every timed replay: neither the L2 nor the 256 MB Infinity Cache can serve
+the weights, whatever the step count.  Inputs are resident in HBM before timing.
 
 Prints one JSON line.  `value` is microseconds per step (lower is better).
 `roofline` gives, for the step's kernel, the algorithmic bytes of one
-launch divided by its average duration, against the 8 TB/s HBM peak.  The
-K timed steps are one HIP graph replay (launches back to back, as in a
-decode loop) bracketed by HIP events on the stream the kernels run on.
+launch divided by its average duration, against the 8 TB/s HBM peak and
+against the read ceiling measured in the same process (a 2 GiB sequential
+stream).  The K timed steps are one HIP graph replay (launches back to back,
+as in a decode loop) bracketed by HIP events on the stream the kernels run
+on; the warm-up steps are graph replays too, so that a kernel trace of the
+run holds replayed dispatches only.
 """
 from __future__ import annotations
 
@@ -37,7 +42,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-ROTATE_BYTES = 1 << 30
+ROTATE_BYTES = 1 << 30          # other weight bytes read between two uses of one copy
+FLUSH_BYTES = 1 << 30           # scratch written before every timed replay
+STREAM_BYTES = 2 << 30          # the sequential read ceiling's buffer
 K_DOWN, N_DOWN = 14336, 4096
 KERNEL_SRC = os.path.join(ROOT, "activation_sparse_bit_amd", "csrc", "sgemv.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fs_down14336_p50_traffic.json")
@@ -72,6 +79,55 @@ def touched_groups(idx: np.ndarray) -> int:
     return int(np.unique(np.asarray(idx) // 128).size)
 
 
+CPU_SCRIPT = r"""
+import json, os, sys, time
+sys.path.insert(0, sys.argv[1])
+import numpy as np
+import oracle, synth
+K, N, runs, calls = 14336, 4096, int(sys.argv[2]), int(sys.argv[3])
+q, s, z = synth.quantized_weights(0, N, K, 0.02)
+x = synth.glu_activation(0, K)
+t = synth.percentile_threshold(x, 0.5)
+oracle.gemv_masked(q, s, z, x, t)            # warm-up call
+per, cpu_wall = [], []
+for r in range(runs):
+    w0, c0 = time.perf_counter(), time.process_time()
+    for _ in range(calls):
+        oracle.active_indices(x, t)
+        oracle.gemv_masked(q, s, z, x, t)
+    w1, c1 = time.perf_counter(), time.process_time()
+    per.append((w1 - w0) / calls)
+    cpu_wall.append((c1 - c0) / (w1 - w0))
+print(json.dumps({"per_call_s": per, "cpu_per_wall": cpu_wall}))
+"""
+
+
+def cpu_baseline(runs: int = 5, calls: int = 20) -> dict:
+    """The fp64 oracle (threshold, compact, per-column dequantize and
+    accumulate) on the step's input, in a child process whose OpenMP / BLAS
+    thread counts are set to the host cores this process may use: `runs`
+    runs of `calls` calls, the median of the runs' per-call times.  `cores`
+    is the threads it actually kept busy (process CPU time over wall time,
+    rounded): NumPy's element-wise work runs on one."""
+    import subprocess
+    n = len(os.sched_getaffinity(0))
+    env = dict(os.environ)
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        env[k] = str(n)
+    r = subprocess.run([sys.executable, "-c", CPU_SCRIPT, ROOT, str(runs), str(calls)], env=env,
+                       stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, check=True)
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    per = sorted(res["per_call_s"])
+    used = float(np.median(res["cpu_per_wall"]))
+    return {"value": float(np.median(per)) * 1e6, "unit": "us/call", "cores": max(1, round(used)),
+            "kind": "oracle",
+            "sample": (f"median of {runs} runs x {calls} full calls of the fp64 oracle (threshold, compact, "
+                       f"per-column dequantize and accumulate) on the 14336->4096 @50% input; "
+                       f"OMP/OpenBLAS/MKL threads = {n} (host cores available); "
+                       f"measured CPU/wall = {used:.2f}"),
+            "runs_us_per_call": [p * 1e6 for p in res["per_call_s"]]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,12 +150,27 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    def rotation(touched_bytes: int) -> int:
+        """Copies needed so that at least ROTATE_BYTES of other weight bytes
+        are read between two uses of one copy."""
+        return max(2, 1 + -(-ROTATE_BYTES // max(1, touched_bytes)))
+
     # ---------------- inputs, resident in HBM ----------------
     q, s, z = synth.quantized_weights(0, N_DOWN, K_DOWN, 0.02)
     desc, blob = sgemv.sgemv_pack_layout(q, s, z)
-    R = max(2, -(-ROTATE_BYTES // desc.total_bytes))
     blob_d = torch.from_numpy(blob).to(dev)
+    # the 90 % step touches the fewest bytes: enough copies for it serve every step
+    x_probe = synth.glu_activation(0, K_DOWN)
+    A90 = int(np.count_nonzero(np.abs(x_probe.astype(np.float32)) >= np.float32(synth.percentile_threshold(x_probe, 0.9))))
+    R = rotation(fused_bytes(A90, K_DOWN // 128, N_DOWN, K_DOWN))
     copies = [blob_d] + [blob_d.clone() for _ in range(R - 1)]
+    flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+
+    def flush():
+        """Read FLUSH_BYTES (a reduction with ordinary loads): the L2 and the
+        Infinity Cache then hold the flush buffer's lines, and no dirty data
+        is left to be written back while the next kernels run."""
+        flush_buf.sum()
     ws = torch.zeros(max(sgemv.sgemv_workspace_bytes(desc, 16), 256), dtype=torch.uint8, device=dev)
 
     x = synth.glu_activation(0, K_DOWN)
@@ -113,23 +184,30 @@ def main():
 
     def graph_time(launches, steps, warmup, spread=None, spread_replays=5):
         """Capture `steps` steps (each step calls every launch with the step
-        number, on the current stream) in one HIP graph, then time one replay
-        bracketed by synchronisations.  Returns microseconds per step.  With
-        a dict `spread`, `spread_replays` more replays after the timed one
-        fill it with the p10 / p50 / p90 of their microseconds per step.  A
-        graph replay puts the launches back to back, as a decode loop does;
-        eager Python launches would leave the GPU waiting for the host."""
-        for i in range(warmup):
-            for f in launches:
-                f(i)
+        number, on the current stream) in one HIP graph; replay it at least
+        three times and until at least `warmup` steps have run (untimed; the
+        first replays of a new graph ran slower than later ones), then
+        synchronise, enqueue a read of the 1 GiB flush buffer and time one
+        replay right behind it with HIP events on the replay stream, and
+        synchronise again.  The flush keeps the weights out of every cache;
+        enqueuing it just before the timed steps keeps the GPU busy up to
+        them, as in a decode loop (after an idle wait for the host, the first
+        timed steps ran up to 15 % slower).  Returns microseconds per step.  With a dict
+        `spread`, `spread_replays` more replays after the timed one (each
+        after a flush) fill it with the p10 / p50 / p90 of their microseconds
+        per step.  A graph replay puts the launches back to back, as a decode
+        loop does; eager Python launches would leave the GPU waiting for the
+        host."""
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(steps):
                 for f in launches:
                     f(i)
-        g.replay()                      # upload and first replay, untimed
+        for _ in range(max(3, -(-warmup // steps))):   # upload and warm-up replays, untimed
+            g.replay()
         torch.cuda.synchronize()
+        flush()                  # enqueued right before the timed replay: cold weights, busy GPU
         t0, t1 = ev(), ev()
         cur = torch.cuda.current_stream()
         t0.record(cur)
@@ -140,6 +218,7 @@ def main():
         if spread is not None:   # more replays, after the timed one, for the spread
             per = []
             for _ in range(spread_replays):
+                flush()
                 a, b = ev(), ev()
                 a.record(cur)
                 g.replay()
@@ -167,14 +246,13 @@ def main():
         return float(np.mean(ms) * 1000.0)
 
     def cold_latency(launch, n=20):
-        """Single calls with the caches cold: a 1 GiB scratch write before
+        """Single calls with the caches cold: a 1 GiB scratch read before
         each (so neither L2 nor the Infinity Cache holds anything of the
         call), then HIP events around the call.  Returns p10/p50/p90 in
         microseconds."""
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         ms = []
         for i in range(n + 2):
-            scratch.fill_(i & 0xFF)
+            flush()
             a, b = ev(), ev()
             cur = torch.cuda.current_stream()
             a.record(cur)
@@ -183,8 +261,6 @@ def main():
             torch.cuda.synchronize()
             if i >= 2:
                 ms.append(a.elapsed_time(b) * 1000.0)
-        del scratch
-        torch.cuda.empty_cache()
         q = np.percentile(ms, [10, 50, 90])
         return {"p10": float(q[0]), "p50": float(q[1]), "p90": float(q[2]), "calls": n}
 
@@ -215,7 +291,7 @@ def main():
         """The step on the same matrix packed with compact metadata (layout
         version 2: fp16 scales, 4-bit zero-points)."""
         d2, b2 = sgemv.sgemv_pack_layout_z4(q, s, z)
-        R2 = max(2, -(-ROTATE_BYTES // d2.total_bytes))
+        R2 = rotation(fused_bytes(A90, K_DOWN // 128, N_DOWN, K_DOWN, z4=True))
         bd = torch.from_numpy(b2).to(dev)
         cps = [bd] + [bd.clone() for _ in range(R2 - 1)]
         res = {}
@@ -290,8 +366,11 @@ def main():
         fused = {g: sgemv.FusedProjections([(n, *W[n]) for n in names], device=dev, max_batch=1)
                  for g, names, _ in groups}
         single = {n: sgemv.PackedMatrix(*W[n], device=dev, max_batch=1) for n in P}
-        total = sum(f.matrix.desc.total_bytes for f in fused.values())
-        RL = max(2, -(-ROTATE_BYTES // total))
+        touched = 0
+        for g, names, xin in groups:
+            A = int(np.count_nonzero(np.abs(X[xin].astype(np.float32)) >= np.float32(T[xin])))
+            touched += fused_bytes(A, fused[g].K // 128, fused[g].N, fused[g].K)
+        RL = rotation(touched)
         fcopies = {g: [f.matrix.blob] + [f.matrix.blob.clone() for _ in range(RL - 1)] for g, f in fused.items()}
         scopies = {n: [m.blob] + [m.blob.clone() for _ in range(RL - 1)] for n, m in single.items()}
         Y = {g: torch.empty(f.N, dtype=torch.float16, device=dev) for g, f in fused.items()}
@@ -340,11 +419,13 @@ def main():
         qq, ss, zz = synth.quantized_weights(j, N, K, sigma)
         dsc, bl = sgemv.sgemv_pack_layout(qq, ss, zz)
         del qq, ss, zz
-        RR = max(2, -(-ROTATE_BYTES // dsc.total_bytes))
+        xv = synth.activation(kind, 0, K)
+        pmax = max(ps)
+        Amin = int(np.count_nonzero(np.abs(xv.astype(np.float32)) >= np.float32(synth.percentile_threshold(xv, pmax))))
+        RR = rotation(fused_bytes(Amin, K // 128, N, K))
         bd = torch.from_numpy(bl).to(dev)
         cps = [bd] + [bd.clone() for _ in range(RR - 1)]
         w = torch.zeros(max(sgemv.sgemv_workspace_bytes(dsc, 1), 256), dtype=torch.uint8, device=dev)
-        xv = synth.activation(kind, 0, K)
         xdv = torch.from_numpy(xv).to(dev)
         iv = torch.zeros(K, dtype=torch.int32, device=dev)
         cv = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -379,9 +460,77 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    def stream_ceiling(reps=5):
+        """Sequential read ceiling: a STREAM_BYTES buffer read with 16-byte
+        non-temporal loads over the whole chip (measurement-only kernel),
+        best of `reps` launches, each after the flush."""
+        import ctypes
+        bl = ctypes.CDLL(os.path.join(ROOT, "activation_sparse_bit_amd", "lib", "libsgemv_bench.so"))
+        bl.sgemv_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+        buf = torch.empty(STREAM_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+        cur = torch.cuda.current_stream()
+        best = 1e30
+        for r in range(reps + 1):
+            flush()
+            a, b = ev(), ev()
+            a.record(cur)
+            if bl.sgemv_bench_stream_read(buf.data_ptr(), STREAM_BYTES, sink.data_ptr(), cur.cuda_stream) != 0:
+                raise RuntimeError("sgemv_bench_stream_read failed")
+            b.record(cur)
+            torch.cuda.synchronize()
+            if r:
+                best = min(best, a.elapsed_time(b) * 1e-3)
+        del buf
+        return {"GBps": STREAM_BYTES / best / 1e9, "bytes": STREAM_BYTES, "us": best * 1e6,
+                "kernel": "sequential 16-byte non-temporal loads, 4096 x 512 threads, best of %d" % reps}
+
+    def listed_read_ceiling(p, steps, warmup):
+        """The step's weight reads alone: for every half tile the 128-byte run
+        of each column in the step's list, with the GEMV's lanes and grid, no
+        activations, scales, arithmetic or sums (measurement-only kernel),
+        graph-timed over the same rotated copies as the step."""
+        import ctypes
+        bl = ctypes.CDLL(os.path.join(ROOT, "activation_sparse_bit_amd", "lib", "libsgemv_bench.so"))
+        bl.sgemv_bench_listed_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        t = synth.percentile_threshold(x, p)
+        lst = np.flatnonzero(np.abs(x.astype(np.float32)) >= np.float32(t)).astype(np.int32)
+        starts = np.searchsorted(lst, np.arange(0, K_DOWN + 1, 128)).astype(np.int32)
+        ld, sd = torch.from_numpy(lst).to(dev), torch.from_numpy(starts).to(dev)
+        sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+
+        def f(i):
+            st = torch.cuda.current_stream().cuda_stream
+            if bl.sgemv_bench_listed_read(copies[i % R].data_ptr() + desc.w_off, sd.data_ptr(), ld.data_ptr(),
+                                          K_DOWN, N_DOWN, sink.data_ptr(), st) != 0:
+                raise RuntimeError("sgemv_bench_listed_read failed")
+        us = graph_time([f], steps, warmup)
+        wb = len(lst) * N_DOWN // 2
+        return {"p": p, "active": int(len(lst)), "us_per_launch": us, "weight_bytes": wb,
+                "GBps": wb / (us * 1e-6) / 1e9}
+
+    def settle(ms: float = 50.0):
+        """Untimed fused steps for about `ms` milliseconds before the first
+        measurement, so that it does not catch the GPU still raising its
+        clocks (the first short replay of a fresh process ran up to 20 %
+        slower than the same replay a moment later)."""
+        t = synth.percentile_threshold(x, 0.5)
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(100):
+                sgemv.sgemv_run_fused(desc, copies[i % R], xd, [t], y, ws, idx, cnt)
+        t_end = time.perf_counter() + ms * 1e-3
+        while time.perf_counter() < t_end:
+            g.replay()
+            torch.cuda.synchronize()
+        del g
+
     # ---------------- the timed step: 50 %, fused, list written ----------------
-    torch.cuda.synchronize()
+    settle()
     main_res = measure_fused(0.5, args.steps, args.warmup, latency=not args.quick)
+    ceiling = stream_ceiling()
     sweep = {"fused_p50": main_res}
     batched = []
     layer = None
@@ -394,6 +543,8 @@ def main():
         for p in (0.5, 0.7, 0.9):
             sweep[f"split_p{int(p * 100)}"] = measure_split(p, args.steps, args.warmup)
         sweep["dense_int4"] = measure_split(0.0, args.steps, args.warmup, dense=True, cold=True)
+        for p in (0.5, 0.9):
+            sweep[f"listed_read_p{int(p * 100)}"] = listed_read_ceiling(p, args.steps, args.warmup)
         dense_us = sweep["dense_int4"]["us_per_step"]
         for k in ("fused_p50", "fused_p70", "fused_p90", "split_p50", "split_p70", "split_p90"):
             sweep[k]["speedup_vs_dense_int4"] = dense_us / sweep[k]["us_per_step"]
@@ -418,20 +569,7 @@ def main():
     # ---------------- CPU baseline: the oracle on the host ----------------
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        t = synth.percentile_threshold(x, 0.5)
-        n_calls, t_start = 0, time.perf_counter()
-        while True:
-            oracle.active_indices(x, t)
-            oracle.gemv_masked(q, s, z, x, t)
-            n_calls += 1
-            if time.perf_counter() - t_start > 10.0 or n_calls >= 50:
-                break
-        el = time.perf_counter() - t_start
-        cpu = {"value": el / n_calls * 1e6, "unit": "us/call", "cores": 1, "kind": "oracle",
-               "sample": f"{n_calls} full calls of the fp64 oracle (threshold, compact, per-column "
-                         f"dequantize and accumulate) on the 14336->4096 @50% input; "
-                         f"single-threaded NumPy"}
+        cpu = cpu_baseline()
 
     kmean = main_res["us_per_step"]   # one launch per step
     out = {
@@ -453,7 +591,10 @@ def main():
                      "achieved": round(main_res["GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(main_res["frac_hbm_peak"], 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": main_res["bytes"],
-                     "avg_launch_us": round(kmean, 3)},
+                     "avg_launch_us": round(kmean, 3),
+                     "ceiling_GBps": round(ceiling["GBps"], 1),
+                     "frac_of_ceiling": round(main_res["GBps"] / ceiling["GBps"], 4),
+                     "ceiling": ceiling},
         "cpu_baseline": cpu,
         "sweep": sweep,
         "batched_p70": batched,
