@@ -32,6 +32,7 @@
 // reproducible.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
 
@@ -1501,8 +1502,54 @@ constexpr int kFsSmallGrid = 160;
 // partial sums grows too long (70B down, 56 segments: slower).
 constexpr int kFsSmallMaxSegs = 32;
 
+// Argument checks of the fused call (no HIP call); `no_thr_ok` when the
+// call may go without thresholds (every column, or a given list).
+int check_fused_args(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx, const float* thr,
+                     const int32_t* idx, const int32_t* count, const void* y, int ldy, uint32_t flags,
+                     bool no_thr_ok) {
+    int st = check_desc(d);
+    if (st) return st;
+    if (!packed || !x || !y || (!thr && !no_thr_ok)) return SGEMV_EINVAL;
+    if ((idx == nullptr) != (count == nullptr)) return SGEMV_EINVAL;
+    if (flags & ~SGEMV_OUT_F32) return SGEMV_EINVAL;
+    if (M < 1 || M > SGEMV_MAX_BATCH) return SGEMV_ESIZE;
+    if (ldx < d->K || ldy < d->N) return SGEMV_ESIZE;
+    if (ldx % 8 || ldy % 8) return SGEMV_EALIGN;
+    if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16)) return SGEMV_EALIGN;
+    if (idx && (!aligned(idx, 4) || !aligned(count, 4))) return SGEMV_EALIGN;
+    if (thr) {
+        Codes c;
+        st = fill_codes(thr, M, c);
+        if (st) return st;
+    }
+    return SGEMV_OK;
+}
+
+// Where a call's scratch regions are: the arrival counters (zero between
+// calls), the many-row list workgroups' line and list (its first word zero
+// between calls), and the partial sums (any contents), with room for
+// partial_cap bytes.
+struct WsRegions {
+    uint32_t* counters;
+    uint32_t* gsync;
+    int32_t* gscratch;
+    float* partials;
+    size_t partial_cap;
+};
+
+// The regions inside a caller's workspace for matrix d and M rows (the
+// layout sgemv_workspace_bytes sizes).
+WsRegions ws_regions(void* ws, const sgemv_desc* d, int M) {
+    if (!ws) return WsRegions{nullptr, nullptr, nullptr, nullptr, 0};
+    uint8_t* b = static_cast<uint8_t*>(ws);
+    const size_t c = ws_counters_bytes(d->N / kVTile);
+    return WsRegions{reinterpret_cast<uint32_t*>(b), reinterpret_cast<uint32_t*>(b + c),
+                     reinterpret_cast<int32_t*>(b + c + 256), reinterpret_cast<float*>(b + ws_head_bytes(d)),
+                     ws_fused_bytes(d, M)};
+}
+
 int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx, const float* thr,
-              int32_t* idx, int32_t* count, void* y, int ldy, uint32_t flags, void* ws, void* stream,
+              int32_t* idx, int32_t* count, void* y, int ldy, uint32_t flags, const WsRegions* ws, void* stream,
               bool all_cols = false, const int32_t* lidx = nullptr, const int32_t* lcount = nullptr);
 
 int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx,
@@ -1519,10 +1566,13 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
     if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16)) return SGEMV_EALIGN;
     if (idx && !aligned(idx, 4)) return SGEMV_EALIGN;
     if (count && !aligned(count, 4)) return SGEMV_EALIGN;
+    if (ws && !aligned(ws, 256)) return SGEMV_EALIGN;
+    const WsRegions r = ws_regions(ws, d, M);
     if (!idx)   // every column: the fused kernels with the whole list, which stream faster
-        return run_fused(d, packed, x, M, ldx, thr, nullptr, nullptr, y, ldy, flags, ws, stream, true);
+        return run_fused(d, packed, x, M, ldx, thr, nullptr, nullptr, y, ldy, flags, ws ? &r : nullptr, stream, true);
     // over a given list the fused kernels read the list themselves
-    return run_fused(d, packed, x, M, ldx, thr, nullptr, nullptr, y, ldy, flags, ws, stream, false, idx, count);
+    return run_fused(d, packed, x, M, ldx, thr, nullptr, nullptr, y, ldy, flags, ws ? &r : nullptr, stream, false,
+                     idx, count);
 
 }
 
@@ -1545,18 +1595,10 @@ void launch_fused(int M, int W, bool one_round, dim3 grid, const RunArgs& a, hip
 }
 
 int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx, const float* thr,
-              int32_t* idx, int32_t* count, void* y, int ldy, uint32_t flags, void* ws, void* stream,
+              int32_t* idx, int32_t* count, void* y, int ldy, uint32_t flags, const WsRegions* ws, void* stream,
               bool all_cols, const int32_t* lidx, const int32_t* lcount) {
-    int st = check_desc(d);
+    int st = check_fused_args(d, packed, x, M, ldx, thr, idx, count, y, ldy, flags, all_cols || lidx);
     if (st) return st;
-    if (!packed || !x || !y || (!thr && !all_cols && !lidx)) return SGEMV_EINVAL;
-    if ((idx == nullptr) != (count == nullptr)) return SGEMV_EINVAL;
-    if (flags & ~SGEMV_OUT_F32) return SGEMV_EINVAL;
-    if (M < 1 || M > SGEMV_MAX_BATCH) return SGEMV_ESIZE;
-    if (ldx < d->K || ldy < d->N) return SGEMV_ESIZE;
-    if (ldx % 8 || ldy % 8) return SGEMV_EALIGN;
-    if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16)) return SGEMV_EALIGN;
-    if (idx && (!aligned(idx, 4) || !aligned(count, 4))) return SGEMV_EALIGN;
 
     RunArgs a;
     std::memset(&a, 0, sizeof a);
@@ -1585,9 +1627,8 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     a.slices = a.segs;   // stride of the partial sums
     if (a.segs > 1) {
         if (!ws) return SGEMV_EINVAL;
-        if (!aligned(ws, 256)) return SGEMV_EALIGN;
         // the kernels address the partial sums with 32-bit buffer offsets
-        if (ws_fused_bytes(d, M) > 0xFFFFFFFFull) return SGEMV_ESIZE;
+        if (ws_fused_bytes(d, M) > 0xFFFFFFFFull || ws_fused_bytes(d, M) > ws->partial_cap) return SGEMV_ESIZE;
     }
     const uint8_t* blob = static_cast<const uint8_t*>(packed);
     a.w = blob + d->w_off;
@@ -1597,11 +1638,11 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     a.y = y;
     a.idx_out = idx;
     a.count_out = count;
-    a.counters = static_cast<uint32_t*>(ws);
-    a.partials = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ws_head_bytes(d)) : nullptr;
     if (ws) {
-        a.gsync = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + ws_counters_bytes(a.tiles));
-        a.gscratch = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + ws_counters_bytes(a.tiles) + 256);
+        a.counters = ws->counters;
+        a.partials = ws->partials;
+        a.gsync = ws->gsync;
+        a.gscratch = ws->gscratch;
     }
     // list workgroups of the many-row kernel: about 64 KiB of activations each, at most 8
     a.gblocks = idx ? 1 : 0;
@@ -1635,7 +1676,12 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
 extern "C" int sgemv_run_fused(const sgemv_desc* d, const void* packed, const void* x_f16, int32_t M,
                                int32_t ldx, const float* thresholds, int32_t* idx, int32_t* count,
                                void* y, int32_t ldy, uint32_t flags, void* workspace, void* stream) {
-    return run_fused(d, packed, x_f16, M, ldx, thresholds, idx, count, y, ldy, flags, workspace, stream);
+    if (check_desc(d)) return check_desc(d);
+    if (workspace && !aligned(workspace, 256)) return SGEMV_EALIGN;
+    if (M < 1 || M > SGEMV_MAX_BATCH) return SGEMV_ESIZE;
+    const WsRegions r = ws_regions(workspace, d, M);
+    return run_fused(d, packed, x_f16, M, ldx, thresholds, idx, count, y, ldy, flags, workspace ? &r : nullptr,
+                     stream);
 }
 
 // Rows x columns up to which the gathering uses 512-thread workgroups.
@@ -1710,3 +1756,103 @@ extern "C" const char* sgemv_strerror(int status) {
 }
 
 extern "C" int sgemv_last_hip_error(void) { return g_last_hip_error; }
+
+// ---------------------------------------------------------------------------
+// the fused call without a workspace argument
+// ---------------------------------------------------------------------------
+//
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops, harnesses that forbid it): the scratch regions live in
+// one fixed-size device array per GPU, here called `scratch`, with a fixed
+// layout, so that calls on matrices of any shape that fits can follow each
+// other: the arrival counters of up to kScratchTiles half tiles, the many-row
+// list workgroups' line and list for up to SGEMV_MAX_K columns, then the
+// partial sums.  Its device address is taken once per GPU with
+// hipGetSymbolAddress (host code never passes the array's name itself to a
+// kernel); the first call on a GPU also clears the counters and the line on
+// the caller's stream.  Every call leaves them at zero again, as with a
+// workspace.  Calls that overlap on one GPU share the array and race.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kScratchTiles = 1024;   // half tiles: N up to 262144
+constexpr size_t kScratchCounters = (size_t)kScratchTiles * kCounterStride * 4;
+constexpr size_t kScratchGather = 256 + (size_t)SGEMV_MAX_K * 4;
+constexpr size_t kScratchHead = kScratchCounters + kScratchGather;
+static_assert(kScratchHead % 256 == 0, "the partial sums start on a 256-byte boundary");
+
+__global__ __launch_bounds__(256) void k_zero_words(uint32_t* __restrict__ p, uint32_t n) {
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<uint8_t*> g_scratch_addr[kMaxDevices];
+
+// The address of this GPU's `scratch` (device of the stream), taken with the
+// device current; `fresh` when it has not been kept yet (the caller keeps it
+// with keep_scratch once the array is cleared).
+int scratch_of(hipStream_t s, uint8_t** out, bool* fresh, int* device) {
+    int dev = 0;
+    hipError_t e = hipStreamGetDevice(s, &dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return SGEMV_EHIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return SGEMV_EUNSUPPORTED;
+    *device = dev;
+    uint8_t* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    *fresh = false;
+    if (!p) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        void* q = nullptr;
+        if (e == hipSuccess) e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !q) {
+            g_last_hip_error = (int)e;
+            return SGEMV_EHIP;
+        }
+        p = static_cast<uint8_t*>(q);
+        *fresh = true;
+    }
+    *out = p;
+    return SGEMV_OK;
+}
+
+}  // namespace
+
+extern "C" int sgemv_run_fused_static(const sgemv_desc* d, const void* packed, const void* x_f16, int32_t M,
+                                      int32_t ldx, const float* thresholds, int32_t* idx, int32_t* count,
+                                      void* y, int32_t ldy, uint32_t flags, void* stream) {
+    int st = check_fused_args(d, packed, x_f16, M, ldx, thresholds, idx, count, y, ldy, flags, false);
+    if (st) return st;
+    if (d->N / kVTile > kScratchTiles || ws_fused_bytes(d, M) > kScratchBytes - kScratchHead) return SGEMV_ESIZE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* p = nullptr;
+    bool fresh = false;
+    int dev = 0;
+    st = scratch_of(s, &p, &fresh, &dev);
+    if (st) return st;
+    if (fresh) {   // counters and the list workgroups' line start at zero
+        const uint32_t n = (uint32_t)((kScratchCounters + 256) / 4);
+        hipLaunchKernelGGL(k_zero_words, dim3((n + 255) / 256), dim3(256), 0, s, reinterpret_cast<uint32_t*>(p), n);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) {
+            g_last_hip_error = (int)e;
+            return SGEMV_EHIP;
+        }
+        g_scratch_addr[dev].store(p, std::memory_order_release);   // cleared: kept for later calls
+    }
+    const WsRegions r{reinterpret_cast<uint32_t*>(p), reinterpret_cast<uint32_t*>(p + kScratchCounters),
+                      reinterpret_cast<int32_t*>(p + kScratchCounters + 256), reinterpret_cast<float*>(p + kScratchHead),
+                      kScratchBytes - kScratchHead};
+    return run_fused(d, packed, x_f16, M, ldx, thresholds, idx, count, y, ldy, flags, &r, s);
+}

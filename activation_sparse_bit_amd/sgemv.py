@@ -32,7 +32,7 @@ SGEMV_MAX_N = 1 << 20
 
 EXPORTED = ["sgemv_pack_layout", "sgemv_pack_layout_z4", "sgemv_pack_layout_parts", "sgemv_desc_from_header",
             "sgemv_gather_indices",
-            "sgemv_run", "sgemv_run_batched", "sgemv_run_fused", "sgemv_workspace_bytes",
+            "sgemv_run", "sgemv_run_batched", "sgemv_run_fused", "sgemv_run_fused_static", "sgemv_workspace_bytes",
             "sgemv_strerror", "sgemv_last_hip_error"]
 
 
@@ -83,6 +83,8 @@ def lib():
     L.sgemv_run_batched.restype = ctypes.c_int
     L.sgemv_run_fused.argtypes = [pd, vp, vp, i32, i32, vp, vp, vp, vp, i32, u32, vp, vp]
     L.sgemv_run_fused.restype = ctypes.c_int
+    L.sgemv_run_fused_static.argtypes = [pd, vp, vp, i32, i32, vp, vp, vp, vp, i32, u32, vp]
+    L.sgemv_run_fused_static.restype = ctypes.c_int
     L.sgemv_workspace_bytes.argtypes = [pd, i32]
     L.sgemv_workspace_bytes.restype = sz
     L.sgemv_strerror.argtypes = [ctypes.c_int]
@@ -352,6 +354,30 @@ def sgemv_run_fused(desc: Desc, packed, x, thresholds, y, workspace, idx=None, c
     _check(lib().sgemv_run_fused(ctypes.byref(desc), _ptr(packed), _ptr(x), M, ldx, _ptr(t),
                                  _ptr(idx), _ptr(count), _ptr(y), ldy, _flags(y),
                                  _ptr(workspace), _stream(stream)), "sgemv_run_fused")
+
+
+def sgemv_run_fused_static(desc: Desc, packed, x, thresholds, y, idx=None, count=None, stream=None):
+    """sgemv_run_fused without a workspace: the library's fixed device array
+    holds the scratch (for callers that cannot allocate); no call may overlap
+    another such call on the same GPU."""
+    M = 1 if x.dim() == 1 else x.shape[0]
+    ldx = desc.K if x.dim() == 1 else x.stride(0)
+    ldy = desc.N if y.dim() == 1 else y.stride(0)
+    _require(packed, "packed", _u8(), int(desc.total_bytes))
+    _require(x, "x", _f16(), desc.K, rows=M)
+    _require(y, "y", _yt(), desc.N, rows=M)
+    if x.shape[-1] < desc.K or y.shape[-1] < desc.N:
+        raise ValueError(f"x/y: rows of {x.shape[-1]}/{y.shape[-1]}, need K = {desc.K} and N = {desc.N}")
+    if (idx is None) != (count is None):
+        raise ValueError("idx and count: both or neither")
+    if idx is not None:
+        _require(idx, "idx", _i32(), desc.K)
+        _require(count, "count", _i32(), 1)
+    _require_gpu(packed=packed, x=x, idx=idx, count=count, y=y)
+    t = _thresholds(thresholds, M)
+    _check(lib().sgemv_run_fused_static(ctypes.byref(desc), _ptr(packed), _ptr(x), M, ldx, _ptr(t),
+                                        _ptr(idx), _ptr(count), _ptr(y), ldy, _flags(y), _stream(stream)),
+           "sgemv_run_fused_static")
 
 
 def sgemv_workspace_bytes(desc: Desc, M: int = 1) -> int:

@@ -303,6 +303,30 @@ int sgemv_run_fused(const sgemv_desc* d, const void* packed, const void* x_f16,
                     int32_t* idx, int32_t* count, void* y, int32_t ldy,
                     uint32_t flags, void* workspace, void* stream);
 
+/*
+ * sgemv_run_fused_static - sgemv_run_fused without a workspace argument, for
+ * callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The scratch
+ * (arrival counters, the list workgroups' line and list, partial sums) is a
+ * fixed 16 MiB device array inside the library, one per GPU, held until the
+ * process ends; its address is taken once per GPU (on the first call there,
+ * which also clears its counters on `stream`); nothing is allocated.
+ *   - Sizes beyond the array: N above 262144 (1024 half tiles), or partial
+ *     sums above its 15.5 MiB (half tiles x segments x M x 1 KiB; segments
+ *     of 512 columns for one or two rows, 1024 for more) return
+ *     SGEMV_ESIZE before any HIP call.  Every configuration of 8192- to
+ *     28672-wide Llama-3 projections with up to 16 rows fits.
+ *   - Every call on a GPU shares that GPU's array and leaves its counters
+ *     at zero again; calls that overlap on one GPU (other streams, other host
+ *     threads) race and must not be made.
+ * Other arguments, results and errors as for sgemv_run_fused, which it
+ * equals bit for bit.
+ */
+int sgemv_run_fused_static(const sgemv_desc* d, const void* packed, const void* x_f16,
+                           int32_t M, int32_t ldx, const float* thresholds,
+                           int32_t* idx, int32_t* count, void* y, int32_t ldy,
+                           uint32_t flags, void* stream);
+
 /* Bytes of workspace needed by sgemv_run (M = 1), sgemv_run_batched or
  * sgemv_run_fused with up to M rows on matrix d; 0 for an invalid
  * description. */
