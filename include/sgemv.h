@@ -240,9 +240,14 @@ int sgemv_gather_indices(const void* x_f16, int32_t M, int32_t K, int32_t ldx,
  *   workspace  device, sgemv_workspace_bytes(d, 1) bytes, 256-byte
  *              aligned, zero-filled once by the caller.  It holds one
  *              arrival counter per 256 outputs, which every call returns to
- *              zero, and scratch sums that need no clearing; so it can be
- *              reused by any later call on the same stream.  May be NULL
- *              when sgemv_workspace_bytes returns 0.
+ *              zero, then scratch (lists, sums) that needs no clearing, at
+ *              offsets that depend on N: so it can be reused by any later
+ *              call on the same stream for a matrix with the same N (sized
+ *              for the largest K and row count among them).  A workspace
+ *              that has served one N must be zero-filled again before it
+ *              serves another.  May be NULL when the call has a single
+ *              column segment (K up to 512 for one or two rows, 1024 for
+ *              more); the call returns SGEMV_EINVAL when it needs one.
  */
 int sgemv_run(const sgemv_desc* d, const void* packed, const void* x_f16,
               const int32_t* idx, const int32_t* count, void* y,
