@@ -171,6 +171,8 @@ def main():
         Infinity Cache then hold the flush buffer's lines, and no dirty data
         is left to be written back while the next kernels run."""
         flush_buf.sum()
+    flush()                      # loads the reduction kernel now: its first call
+    torch.cuda.synchronize()     # waits ~20 ms on the host, with the GPU idle
     ws = torch.zeros(max(sgemv.sgemv_workspace_bytes(desc, 16), 256), dtype=torch.uint8, device=dev)
 
     x = synth.glu_activation(0, K_DOWN)
@@ -511,7 +513,7 @@ def main():
                 "GBps": wb / (us * 1e-6) / 1e9}
 
     def settle(ms: float = 50.0):
-        """Untimed fused steps for about `ms` milliseconds before the first
+        """Flushes and untimed fused steps for about `ms` milliseconds before the first
         measurement, so that it does not catch the GPU still raising its
         clocks (the first short replay of a fresh process ran up to 20 %
         slower than the same replay a moment later)."""
@@ -523,6 +525,7 @@ def main():
                 sgemv.sgemv_run_fused(desc, copies[i % R], xd, [t], y, ws, idx, cnt)
         t_end = time.perf_counter() + ms * 1e-3
         while time.perf_counter() < t_end:
+            flush()
             g.replay()
             torch.cuda.synchronize()
         del g
