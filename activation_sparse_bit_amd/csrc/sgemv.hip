@@ -157,12 +157,10 @@ __device__ __forceinline__ uint32_t union_mask8(const uint16_t* __restrict__ x, 
 }
 
 // Wavefronts W and above of the workgroup only join the barrier.  The
-// entries written are kbase + column (x points at column kbase).  The list
-// and count are stored device-coherent (written through): a workgroup on
-// another XCD may read them (the many-row kernel's join), and written-through
-// lines leave nothing for the end of the kernel to write back (the one-row
-// step measured 0.1 us faster than with write-back stores).
-template <int W>
+// entries written are kbase + column (x points at column kbase); with COH
+// the list and count are stored device-coherent (written through), for a
+// workgroup on another XCD to read.
+template <int W, bool COH = false>
 __device__ __forceinline__ void gather_body(const uint16_t* __restrict__ x, int M, int K, int ldx, const Codes& tc,
                                             int32_t* __restrict__ idx, int32_t* __restrict__ count,
                                             GatherShared& gs, int kbase = 0) {
@@ -198,7 +196,8 @@ __device__ __forceinline__ void gather_body(const uint16_t* __restrict__ x, int 
         grand += t;
     }
     if (threadIdx.x == 0) {
-        __hip_atomic_store(count, (int32_t)grand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (COH) __hip_atomic_store(count, (int32_t)grand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else *count = (int32_t)grand;
     }
 
     uint32_t running = wbase;
@@ -210,7 +209,8 @@ __device__ __forceinline__ void gather_body(const uint16_t* __restrict__ x, int 
         uint32_t pos = running + pre;
         while (m8) {
             const int b = __builtin_ctz(m8);
-            __hip_atomic_store(&idx[pos++], kbase + base + off + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (COH) __hip_atomic_store(&idx[pos++], kbase + base + off + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else idx[pos++] = kbase + base + off + b;
             m8 &= m8 - 1u;
         }
         running += tot;
@@ -511,8 +511,8 @@ __device__ __forceinline__ void sp_finish(const RunArgs& a, int vt, int slice, i
     const size_t n = (size_t)vt * kVTile + sp_out(o >> 2, o & 3);
     if (S == 1) {
         if (own && m < a.M) {
-            if (a.out_f32) __builtin_nontemporal_store(sum, &static_cast<float*>(a.y)[(size_t)m * a.ldy + n]);
-            else __builtin_nontemporal_store((_Float16)sum, &static_cast<_Float16*>(a.y)[(size_t)m * a.ldy + n]);
+            if (a.out_f32) static_cast<float*>(a.y)[(size_t)m * a.ldy + n] = sum;
+            else static_cast<_Float16*>(a.y)[(size_t)m * a.ldy + n] = (_Float16)sum;
         }
         return;
     }
@@ -561,8 +561,8 @@ __device__ __forceinline__ void sp_finish(const RunArgs& a, int vt, int slice, i
         }
     }
     if (own && m < a.M) {
-        if (a.out_f32) __builtin_nontemporal_store(tot, &static_cast<float*>(a.y)[(size_t)m * a.ldy + n]);
-        else __builtin_nontemporal_store((_Float16)tot, &static_cast<_Float16*>(a.y)[(size_t)m * a.ldy + n]);
+        if (a.out_f32) static_cast<float*>(a.y)[(size_t)m * a.ldy + n] = tot;
+        else static_cast<_Float16*>(a.y)[(size_t)m * a.ldy + n] = (_Float16)tot;
     }
     if (t == 0) __hip_atomic_store(&a.counters[vt * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1053,7 +1053,7 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
             // list of columns k0 .. k0 + kr - 1 into the scratch at k0, and its length
             const int k0 = bid * a.grange;
             const int kr = a.K - k0 < a.grange ? a.K - k0 : a.grange;
-            gather_body<fm::kWaves>(a.x + k0, a.M, kr, a.ldx, a.tc, a.gscratch + k0,
+            gather_body<fm::kWaves, true>(a.x + k0, a.M, kr, a.ldx, a.tc, a.gscratch + k0,
                                           reinterpret_cast<int32_t*>(a.gsync) + 16 + bid, lds.gl, k0);
             __builtin_amdgcn_s_waitcnt(0);  // this thread's stores acknowledged
             __syncthreads();                // ... and every thread's, before the count
