@@ -43,7 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 1 << 30          # other weight bytes read between two uses of one copy
-FLUSH_BYTES = 1 << 30           # scratch written before every timed replay
+FLUSH_BYTES = 1 << 30           # scratch read before every timed replay
 STREAM_BYTES = 2 << 30          # the sequential read ceiling's buffer
 K_DOWN, N_DOWN = 14336, 4096
 KERNEL_SRC = os.path.join(ROOT, "activation_sparse_bit_amd", "csrc", "sgemv.hip")
@@ -167,10 +167,13 @@ def main():
     flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
 
     def flush():
-        """Read FLUSH_BYTES (a reduction with ordinary loads): the L2 and the
-        Infinity Cache then hold the flush buffer's lines, and no dirty data
-        is left to be written back while the next kernels run."""
-        flush_buf.sum()
+        """Read FLUSH_BYTES (a max reduction with ordinary loads): the L2 and
+        the Infinity Cache then hold the flush buffer's lines, and no dirty
+        data is left to be written back while the next kernels run.  (An
+        int32 sum would first widen the buffer into a 2 GiB int64 copy, and
+        the dirty lines of that copy slowed the replay right after it by
+        ~5 %.)"""
+        flush_buf.max()
     flush()                      # loads the reduction kernel now: its first call
     torch.cuda.synchronize()     # waits ~20 ms on the host, with the GPU idle
     ws = torch.zeros(max(sgemv.sgemv_workspace_bytes(desc, 16), 256), dtype=torch.uint8, device=dev)
