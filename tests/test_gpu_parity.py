@@ -164,7 +164,7 @@ def test_run_mlp_70b_sampled(K, N, glu, p):
 
 @pytest.mark.parametrize("K,N", [(128, 512), (384, 1536), (1152, 512), (2176, 2560)])
 def test_run_ragged_shapes(K, N):
-    """K not a multiple of the 256-column workgroup slice, tiny K, several tiles."""
+    """K not a multiple of the 1024- (or 512-) column workgroup segment, tiny K, several tiles."""
     q, s, z = synth.random_int4_problem(K + N, N, K)
     from activation_sparse_bit_amd import sgemv
     pm = sgemv.PackedMatrix(q, s, z, device=G.torch_dev())
