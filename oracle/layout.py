@@ -46,6 +46,18 @@ It stores the same numbers in 2.5 instead of 4 bytes per row and group, so
 the metadata read per touched group shrinks by 37.5 %; the page's call for a
 layout that serves sparse reads applies to this region as much as to the
 weights.
+
+Version 3 (groups along N) stores a different quantization: one scale and
+one zero-point per input column k and group of 128 consecutive outputs, so
+s_bits and z_bits are [N/128][K].  The weight region is the same as in
+version 1; the metadata region holds, per 256 outputs (groups b = 2h and
+2h + 1) and column k, 8 contiguous bytes: s, z of group 2h, then s, z of
+group 2h + 1.  A column's metadata is then read only with the column, so
+metadata bytes fall with the sparsity.  tile_n must be at least 256:
+
+  m_bytes = (N/128)*K*4
+  metadata     m_off + ((h*K + k)*2 + e)*4 : fp16 bits of s[2h + e][k], then
+               fp16 bits of z[2h + e][k]    (h < N/256, e in {0, 1})
 """
 from __future__ import annotations
 
@@ -58,6 +70,7 @@ HEADER_BYTES = 256
 MAGIC = b"SGV1"
 VERSION = 1
 VERSION_Z4 = 2
+VERSION_NG = 3
 
 
 def _roundup(v: int, a: int) -> int:
@@ -68,25 +81,29 @@ def header_fields(N: int, K: int, tile_n: int, version: int = VERSION) -> dict:
     w_off = HEADER_BYTES
     w_bytes = N * K // 2
     m_off = w_off + _roundup(w_bytes, 256)
-    m_bytes = (K // GROUP) * N * 4 if version == VERSION else (K // GROUP) * N * 5 // 2
+    m_bytes = (K // GROUP) * N * 5 // 2 if version == VERSION_Z4 else (K // GROUP) * N * 4
     total = m_off + _roundup(m_bytes, 256)
     return dict(N=N, K=K, group=GROUP, tile_n=tile_n, w_off=w_off,
                 w_bytes=w_bytes, m_off=m_off, m_bytes=m_bytes, total_bytes=total)
 
 
-def _check(q, s_bits, z_bits, tile_n):
+def _check(q, s_bits, z_bits, tile_n, version=VERSION):
     q = np.asarray(q, dtype=np.uint8)
     N, K = q.shape
     if K % GROUP or K <= 0 or N <= 0:
         raise ValueError("K must be a positive multiple of 128")
     if tile_n < 64 or tile_n > 1024 or tile_n & (tile_n - 1) or N % tile_n:
         raise ValueError("tile_n must be a power of two in [64, 1024] dividing N")
+    if version == VERSION_NG and tile_n < 256:
+        raise ValueError("groups along N need tile_n >= 256")
     if q.max(initial=0) > 15:
         raise ValueError("codes must be 4-bit")
     s_bits = np.asarray(s_bits, dtype=np.uint16)
     z_bits = np.asarray(z_bits, dtype=np.uint16)
-    if s_bits.shape != (N, K // GROUP) or z_bits.shape != (N, K // GROUP):
-        raise ValueError("scale/zero shape must be [N][K/128]")
+    shape = (N // GROUP, K) if version == VERSION_NG else (N, K // GROUP)
+    if s_bits.shape != shape or z_bits.shape != shape:
+        raise ValueError("scale/zero shape must be [N/128][K]" if version == VERSION_NG
+                         else "scale/zero shape must be [N][K/128]")
     return q, s_bits, z_bits, N, K
 
 
@@ -102,10 +119,11 @@ def zero_codes(z_bits) -> np.ndarray:
 def pack_spec(q, s_bits, z_bits, tile_n: int, version: int = VERSION) -> np.ndarray:
     """Return the blob (uint8 array) for codes ``q`` [N][K] and fp16 bit
     patterns ``s_bits``, ``z_bits`` [N][K/128]; version 1 (scale/zero pairs)
-    or 2 (scales, then 4-bit zero-points)."""
-    if version not in (VERSION, VERSION_Z4):
+    or 2 (scales, then 4-bit zero-points); version 3 takes them as
+    [N/128][K] (groups along N)."""
+    if version not in (VERSION, VERSION_Z4, VERSION_NG):
         raise ValueError("unknown layout version")
-    q, s_bits, z_bits, N, K = _check(q, s_bits, z_bits, tile_n)
+    q, s_bits, z_bits, N, K = _check(q, s_bits, z_bits, tile_n, version)
     h = header_fields(N, K, tile_n, version)
     blob = np.zeros(h["total_bytes"], dtype=np.uint8)
     head = (MAGIC + struct.pack("<I", version)
@@ -121,6 +139,14 @@ def pack_spec(q, s_bits, z_bits, tile_n: int, version: int = VERSION) -> np.ndar
     blob[h["w_off"]:h["w_off"] + h["w_bytes"]] = byte.reshape(-1)
 
     Gk = K // GROUP
+    if version == VERSION_NG:
+        H = N // 256
+        pair = np.empty((H, K, 2, 2), dtype=np.uint16)             # [h][k][e][s|z]
+        pair[..., 0] = s_bits.reshape(H, 2, K).transpose(0, 2, 1)
+        pair[..., 1] = z_bits.reshape(H, 2, K).transpose(0, 2, 1)
+        blob[h["m_off"]:h["m_off"] + h["m_bytes"]] = \
+            pair.astype("<u2").reshape(-1).view(np.uint8)
+        return blob
     if version == VERSION:
         pair = np.empty((T, Gk, tile_n, 2), dtype=np.uint16)     # [t][g][i][s|z]
         pair[..., 0] = s_bits.reshape(T, tile_n, Gk).transpose(0, 2, 1)
@@ -161,6 +187,12 @@ def unpack_spec(blob):
     qt[:, :, 1::2] = byte >> 4
     q = qt.transpose(0, 2, 1).reshape(N, K)
     md = blob[h["m_off"]:h["m_off"] + h["m_bytes"]]
+    if h["version"] == VERSION_NG:
+        H = N // 256
+        pair = md.view("<u2").reshape(H, K, 2, 2)
+        s_bits = pair[..., 0].transpose(0, 2, 1).reshape(N // GROUP, K).astype(np.uint16)
+        z_bits = pair[..., 1].transpose(0, 2, 1).reshape(N // GROUP, K).astype(np.uint16)
+        return np.ascontiguousarray(q), s_bits, z_bits, h
     if h["version"] == VERSION:
         pair = md.view("<u2").reshape(T, Gk, tile_n, 2)
         s_bits = pair[..., 0].transpose(0, 2, 1).reshape(N, Gk).astype(np.uint16)

@@ -132,9 +132,31 @@ def quantize_int4_g128(W: np.ndarray, group: int = GROUP, chunk_rows: int = 1024
     return q, s_bits, z_bits
 
 
+def quantize_int4_ng128(W: np.ndarray, group: int = GROUP):
+    """The same asymmetric min-max int4 quantizer with its groups along the
+    outputs: one (s, z) per input column k and block of ``group`` consecutive
+    outputs (the format of layout version 3).  It is the groups-along-inputs
+    quantizer applied to W transposed.
+
+    Returns q (uint8 [N][K]), s and z (uint16 fp16 bit patterns,
+    [N/group][K]).
+    """
+    W = np.asarray(W, dtype=np.float32)
+    if W.shape[0] % group:
+        raise ValueError("N must be a multiple of the group size")
+    qT, sT, zT = quantize_int4_g128(np.ascontiguousarray(W.T), group)
+    return np.ascontiguousarray(qT.T), np.ascontiguousarray(sT.T), np.ascontiguousarray(zT.T)
+
+
 def quantized_weights(j: int, N: int, K: int, sigma: float):
     """Weights of projection ``j`` ~ N(0, sigma^2), quantized to int4 g128."""
     return quantize_int4_g128(normal_f32(SEED_W + j, (N, K), sigma))
+
+
+def quantized_weights_ng(j: int, N: int, K: int, sigma: float):
+    """The same draw as ``quantized_weights``, quantized with groups of 128
+    outputs per input column (layout version 3)."""
+    return quantize_int4_ng128(normal_f32(SEED_W + j, (N, K), sigma))
 
 
 # --------------------------------------------------------------------------
@@ -229,4 +251,14 @@ def random_int4_problem(seed: int, N: int, K: int, group: int = GROUP):
     q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
     z = rng.integers(0, 16, size=(N, K // group)).astype(np.float16)
     s = (rng.uniform(0.5, 2.0, size=(N, K // group)) * 0.01).astype(np.float16)
+    return q, s.view(np.uint16), z.view(np.uint16)
+
+
+def random_int4_problem_ng(seed: int, N: int, K: int, group: int = GROUP):
+    """As ``random_int4_problem``, with the scales and zero-points of the
+    groups-along-outputs format ([N/group][K])."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    z = rng.integers(0, 16, size=(N // group, K)).astype(np.float16)
+    s = (rng.uniform(0.5, 2.0, size=(N // group, K)) * 0.01).astype(np.float16)
     return q, s.view(np.uint16), z.view(np.uint16)

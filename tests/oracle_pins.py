@@ -405,9 +405,137 @@ def pin_layout_z4_roundtrip(impl):
     raise AssertionError("a zero-point that is not an integer 0..15 was packed in 4 bits")
 
 
+# --------------------------------------------------------------------------
+# groups along N (layout version 3)
+# --------------------------------------------------------------------------
+def _ng_problem(seed, N, K, exact=False):
+    """Codes, and scale/zero-point bit patterns per (group of 128 outputs,
+    column): [N/128][K].  ``exact``: power-of-two scales, so every product
+    with an fp16 activation of small exponent range is exact."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    if exact:
+        s = (2.0 ** rng.integers(-8, -2, size=(N // 128, K))).astype(np.float16).view(np.uint16)
+    else:
+        s = rng.uniform(0.001, 0.1, size=(N // 128, K)).astype(np.float16).view(np.uint16)
+    z = rng.integers(0, 16, size=(N // 128, K)).astype(np.float16).view(np.uint16)
+    return q, s, z
+
+
+def pin_ng_transpose_duality(impl):
+    """Groups along N of W are groups along K of W transposed: the matrix
+    that version 3 dequantizes from (q, s, z) is the transpose of what the
+    groups-along-K product dequantizes from (q^T, s^T, z^T), and for any u, x
+    u . (W x) = (W^T u) . x.  Shapes are not square, so a transposed lookup
+    cannot pass."""
+    for (N, K, seed) in ((384, 256, 31), (256, 640, 32)):
+        q, s, z = _ng_problem(seed, N, K, exact=True)
+        W3 = impl.dequantize_columns(q, s, z, np.arange(K), along="n")
+        W1 = impl.dequantize_columns(np.ascontiguousarray(q.T), np.ascontiguousarray(s.T),
+                                     np.ascontiguousarray(z.T), np.arange(N))
+        assert W3.shape == (N, K) and np.array_equal(W3, W1.T)
+        rng = np.random.default_rng(seed + 100)
+        # small integers: every sum below is exact in float64
+        x = rng.integers(-3, 4, size=K).astype(np.float16)
+        u = rng.integers(-3, 4, size=N).astype(np.float16)
+        y3, _ = impl.gemv_dense(q, s, z, x, along="n")
+        y1, _ = impl.gemv_dense(np.ascontiguousarray(q.T), np.ascontiguousarray(s.T),
+                                np.ascontiguousarray(z.T), u)
+        lhs = float(np.dot(u.astype(np.float64), y3[0]))
+        rhs = float(np.dot(y1[0], x.astype(np.float64)))
+        assert lhs == rhs, (N, K, lhs, rhs)
+
+
+def pin_ng_exact_rational(impl):
+    """Brute force with exact rationals on a tiny problem (struct-decoded
+    fp16, pure-Python loops)."""
+    for seed in range(2):
+        N, K, M = 256, 256, 2
+        q, s, z = _ng_problem(40 + seed, N, K, exact=True)
+        _, _, _, xb, ts = _exact_problem(60 + seed, N=6, K=K, M=M)
+        y, B, U = impl.gemv_masked(q, s, z, bits_to_f16(xb), ts, along="n")
+        act = [[abs(f16_value(xb[m, k])) >= f32_round(ts[m]) for k in range(K)] for m in range(M)]
+        assert list(U) == [k for k in range(K) if any(act[m][k] for m in range(M))]
+        for n in range(0, N, 37):
+            b = n // 128
+            for m in range(M):
+                acc, accB = Fraction(0), Fraction(0)
+                for k in range(K):
+                    if act[m][k]:
+                        w = Fraction(f16_value(s[b, k])) * (int(q[n, k]) - Fraction(f16_value(z[b, k])))
+                        xv = Fraction(f16_value(xb[m, k]))
+                        acc += w * xv
+                        accB += abs(w) * abs(xv)
+                assert y[m, n] == float(acc) and B[m, n] == float(accB), (seed, m, n)
+
+
+def pin_ng_constant_metadata(impl):
+    """One scale and one zero-point for the whole matrix: groups along N and
+    along K describe the same weights, and the two products agree bit for bit
+    (same columns, same order)."""
+    rng = np.random.default_rng(33)
+    N, K = 256, 384
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    s0 = np.float16(0.0372).view(np.uint16)
+    z0 = np.float16(6.0).view(np.uint16)
+    x = rng.standard_normal((2, K)).astype(np.float16)
+    y1, B1, U1 = impl.gemv_masked(q, np.full((N, K // 128), s0, np.uint16),
+                                  np.full((N, K // 128), z0, np.uint16), x, [0.4, 1.1])
+    y3, B3, U3 = impl.gemv_masked(q, np.full((N // 128, K), s0, np.uint16),
+                                  np.full((N // 128, K), z0, np.uint16), x, [0.4, 1.1], along="n")
+    assert np.array_equal(U1, U3) and np.array_equal(y1, y3) and np.array_equal(B1, B3)
+
+
+def pin_layout_ng_closed_form(impl):
+    """Version 3: the weight bytes of version 1; per 256 outputs and column,
+    8 bytes: s, z of the even group, then s, z of the odd one."""
+    for (N, K, Tn) in ((256, 128, 256), (512, 384, 512), (1024, 256, 1024)):
+        n = np.arange(N)[:, None]
+        k = np.arange(K)[None, :]
+        q = ((n + 3 * k) % 16).astype(np.uint8)
+        b = np.arange(N // 128)[:, None]
+        s = ((0x3000 + 7 * b + 13 * k) & 0x7BFF).astype(np.uint16)
+        z = ((b + 5 * k) % 16).astype(np.float16).view(np.uint16)
+        b3 = np.asarray(impl.pack_spec(q, s, z, Tn, 3))
+        b1 = np.asarray(impl.pack_spec(q, np.zeros((N, K // 128), np.uint16),
+                                       np.zeros((N, K // 128), np.uint16), Tn))
+        h = impl.read_header(b3)
+        m_off = 256 + ((N * K // 2 + 255) // 256) * 256
+        assert h["version"] == 3 and h["m_off"] == m_off and h["m_bytes"] == (N // 128) * K * 4
+        assert h["total_bytes"] == m_off + ((N // 128) * K * 4 + 255) // 256 * 256 == len(b3)
+        assert np.array_equal(b3[256:m_off], b1[256:m_off])
+        for hh in range(N // 256):
+            for kk in (0, 1, K // 2, K - 1):
+                base = m_off + (hh * K + kk) * 8
+                for e in (0, 1):
+                    bb = 2 * hh + e
+                    sb = int(b3[base + 4 * e]) | int(b3[base + 4 * e + 1]) << 8
+                    zb = int(b3[base + 4 * e + 2]) | int(b3[base + 4 * e + 3]) << 8
+                    assert sb == ((0x3000 + 7 * bb + 13 * kk) & 0x7BFF), (N, K, hh, kk, e)
+                    assert f16_value(zb) == (bb + 5 * kk) % 16
+    try:
+        impl.pack_spec(q[:128], s[:1], z[:1], 128, 3)
+    except ValueError:
+        return
+    raise AssertionError("groups along N were packed with tiles narrower than 256 outputs")
+
+
+def pin_layout_ng_roundtrip(impl):
+    rng = np.random.default_rng(34)
+    for Tn in (256, 512, 1024):
+        N, K = 1024, 384
+        q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+        s = rng.integers(0, 0x7C00, size=(N // 128, K)).astype(np.uint16)
+        z = rng.integers(0, 16, size=(N // 128, K)).astype(np.float16).view(np.uint16)
+        q2, s2, z2, h = impl.unpack_spec(impl.pack_spec(q, s, z, Tn, 3))
+        assert h["version"] == 3
+        assert np.array_equal(q, q2) and np.array_equal(s, s2) and np.array_equal(z, z2)
+
+
 ALL_PINS = [pin_select_bruteforce, pin_select_golden, pin_gemv_exact_rational,
             pin_gemv_q_equals_z, pin_gemv_one_hot, pin_gemv_constant_group,
             pin_gemv_scale_equivariance, pin_gemv_matches_matrix_product,
             pin_batched_rows, pin_dequantize, pin_layout_closed_form,
             pin_layout_roundtrip, pin_layout_golden, pin_layout_z4_closed_form,
-            pin_layout_z4_roundtrip]
+            pin_layout_z4_roundtrip, pin_ng_transpose_duality, pin_ng_exact_rational,
+            pin_ng_constant_metadata, pin_layout_ng_closed_form, pin_layout_ng_roundtrip]

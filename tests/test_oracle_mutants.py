@@ -37,6 +37,16 @@ MUTANTS = [
      "run[:, :, 2 * tile_n:] = (zt[:, :, 0::2] << 4) | zt[:, :, 1::2]", "compact zero-point nibble order"),
     ("layout.py", "zt = zc.reshape(T, tile_n, Gk).transpose(0, 2, 1)",
      "zt = zc.reshape(T, Gk, tile_n)", "compact zero-points not transposed to [t][g][i]"),
+    ("gemv.py", "        blk = np.arange(N) // GROUP\n", "        blk = np.arange(N) % (N // GROUP)\n",
+     "groups along N: output blocks interleaved"),
+    ("gemv.py", "w = sC[k][blk] * (qT[pos[k]].astype(np.float64) - zC[k][blk])",
+     "w = sC[k][blk] * (qT[pos[k]].astype(np.float64) - zC[k][blk[::-1]])", "groups along N: zero-point of another block"),
+    ("gemv.py", "        s = _f16_bits_to_f64(s_bits)[blk][:, cols]\n", "        s = _f16_bits_to_f64(s_bits)[:, cols][blk % 1]\n",
+     "groups along N: one block's scale for every output in dequantize"),
+    ("layout.py", "pair[..., 0] = s_bits.reshape(H, 2, K).transpose(0, 2, 1)",
+     "pair[..., 0] = s_bits.reshape(2, H, K).transpose(1, 2, 0)", "groups along N: groups paired across halves"),
+    ("layout.py", "pair[..., 1] = z_bits.reshape(H, 2, K).transpose(0, 2, 1)",
+     "pair[..., 1] = s_bits.reshape(H, 2, K).transpose(0, 2, 1)", "groups along N: scale written as zero-point"),
 ]
 
 
