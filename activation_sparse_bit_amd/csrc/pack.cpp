@@ -9,7 +9,10 @@
 // Scales and zero-points of one (tile, group) pair are one contiguous run:
 // tile_n (s, z) fp16 pairs (version 1), or tile_n fp16 scales followed by
 // the integer zero-points as 4-bit codes, two per byte (version 2, 37.5 %
-// fewer metadata bytes for the same numbers).  The byte formulas are
+// fewer metadata bytes for the same numbers).  Version 3 packs the other
+// quantization, with groups along the outputs (one (s, z) per input column
+// and 128 outputs): per 256 outputs and column, 8 contiguous bytes, so a
+// column's metadata is read only with the column.  The byte formulas are
 // documented in sgemv.h.
 #include "sgemv.h"
 
@@ -65,7 +68,7 @@ static int check_shape(int32_t N, int32_t K, int32_t group, int32_t tile_n) {
 
 // The rows of the matrix being packed: one or more parts stacked along N
 // (part p holds rows n_part[p] of its own [rows][K] codes and [rows][K/128]
-// scales and zero-points).
+// scales and zero-points, or [rows/128][K] with groups along the outputs).
 struct Rows {
     int32_t parts;
     const uint8_t* const* q;
@@ -94,12 +97,26 @@ struct Rows {
         locate(n, p, r);
         return z[p][r * Gk + g];
     }
+    // groups along the outputs: the (s, z) of column k for the 128 outputs
+    // that hold row n (parts are whole tiles of at least 256 rows)
+    uint16_t scale_ng(uint64_t n, int32_t K, int32_t k) const {
+        int32_t p; uint64_t r;
+        locate(n, p, r);
+        return s[p][(r / SGEMV_GROUP) * (uint64_t)K + k];
+    }
+    uint16_t zero_ng(uint64_t n, int32_t K, int32_t k) const {
+        int32_t p; uint64_t r;
+        locate(n, p, r);
+        return z[p][(r / SGEMV_GROUP) * (uint64_t)K + k];
+    }
 };
 
 static int pack(const Rows& src, int32_t N, int32_t K, int32_t group, int32_t tile_n, uint32_t version, void* out,
                 size_t out_capacity, sgemv_desc* desc_out) {
     int st = check_shape(N, K, group, tile_n);
     if (st) return st;
+    const bool ng = version == SGEMV_LAYOUT_NG;
+    if (ng && tile_n < 2 * SGEMV_GROUP) return SGEMV_ESIZE;
     sgemv_desc d;
     sgemv_layout_fill_desc(N, K, tile_n, version, &d);
     if (!out) {  // size query
@@ -116,6 +133,14 @@ static int pack(const Rows& src, int32_t N, int32_t K, int32_t group, int32_t ti
         const uint8_t* qr = src.qrow(n, K);
         for (int32_t k = 0; k < K; ++k)
             if (qr[k] > 15) return SGEMV_EINVAL;
+        if (ng) {
+            if (n % SGEMV_GROUP == 0)
+                for (int32_t k = 0; k < K; ++k) {
+                    if (!fp16_is_finite(src.scale_ng(n, K, k))) return SGEMV_EINVAL;
+                    if (fp16_small_int(src.zero_ng(n, K, k)) < 0) return SGEMV_EINVAL;
+                }
+            continue;
+        }
         for (int32_t g = 0; g < Gk; ++g) {
             if (!fp16_is_finite(src.scale(n, Gk, g))) return SGEMV_EINVAL;
             if (fp16_small_int(src.zero(n, Gk, g)) < 0) return SGEMV_EINVAL;
@@ -145,7 +170,21 @@ static int pack(const Rows& src, int32_t N, int32_t K, int32_t group, int32_t ti
                 dst[(uint64_t)k * half] = (uint8_t)(r0[k] | (r1[k] << 4));
         }
     }
-    if (version == SGEMV_LAYOUT_Z4) {
+    if (ng) {
+        // metadata: outputs 256 h .. 256 h + 255, column k -> (s, z) of group
+        // 2 h, then (s, z) of group 2 h + 1
+        uint16_t* md = reinterpret_cast<uint16_t*>(blob + d.m_off);
+        const int32_t H = N / (2 * SGEMV_GROUP);
+        for (int32_t h = 0; h < H; ++h)
+            for (int32_t e = 0; e < 2; ++e) {
+                const uint64_t n = ((uint64_t)2 * h + e) * SGEMV_GROUP;
+                for (int32_t k = 0; k < K; ++k) {
+                    const uint64_t o = (((uint64_t)h * K + k) * 2 + e) * 2;
+                    md[o] = src.scale_ng(n, K, k);
+                    md[o + 1] = src.zero_ng(n, K, k);
+                }
+            }
+    } else if (version == SGEMV_LAYOUT_Z4) {
         // metadata: tile t, group g -> tile_n scales, then tile_n / 2 bytes of
         // 4-bit zero-points (even row in the low nibble)
         const uint64_t run = (uint64_t)tile_n * 5 / 2;
@@ -194,13 +233,22 @@ extern "C" int sgemv_pack_layout_z4(const uint8_t* q, const uint16_t* scales_f16
     return pack(src, N, K, group, tile_n, SGEMV_LAYOUT_Z4, out, out_capacity, desc_out);
 }
 
+extern "C" int sgemv_pack_layout_ng(const uint8_t* q, const uint16_t* scales_f16,
+                                    const uint16_t* zeros_f16, int32_t N, int32_t K,
+                                    int32_t group, int32_t tile_n, void* out,
+                                    size_t out_capacity, sgemv_desc* desc_out) {
+    const Rows src{1, &q, &scales_f16, &zeros_f16, &N};
+    return pack(src, N, K, group, tile_n, SGEMV_LAYOUT_NG, out, out_capacity, desc_out);
+}
+
 extern "C" int sgemv_pack_layout_parts(int32_t parts, const uint8_t* const* q,
                                        const uint16_t* const* scales_f16,
                                        const uint16_t* const* zeros_f16, const int32_t* n_part,
                                        int32_t K, int32_t group, int32_t tile_n, uint32_t version,
                                        void* out, size_t out_capacity, sgemv_desc* desc_out) {
     if (parts < 1 || !n_part) return SGEMV_EINVAL;
-    if (version != SGEMV_LAYOUT_PAIRS && version != SGEMV_LAYOUT_Z4) return SGEMV_EINVAL;
+    if (version != SGEMV_LAYOUT_PAIRS && version != SGEMV_LAYOUT_Z4 && version != SGEMV_LAYOUT_NG)
+        return SGEMV_EINVAL;
     if (out && (!q || !scales_f16 || !zeros_f16)) return SGEMV_EINVAL;
     int64_t N = 0;
     for (int32_t p = 0; p < parts; ++p) {
@@ -220,11 +268,13 @@ extern "C" int sgemv_desc_from_header(const void* header, size_t bytes, sgemv_de
     if (std::memcmp(h, "SGV1", 4) != 0) return SGEMV_EINVAL;
     uint32_t version;
     std::memcpy(&version, h + 4, 4);
-    if (version != SGEMV_LAYOUT_PAIRS && version != SGEMV_LAYOUT_Z4) return SGEMV_EINVAL;
+    if (version != SGEMV_LAYOUT_PAIRS && version != SGEMV_LAYOUT_Z4 && version != SGEMV_LAYOUT_NG)
+        return SGEMV_EINVAL;
     int32_t hv[4];
     std::memcpy(hv, h + 8, 16);
     int st = check_shape(hv[0], hv[1], hv[2], hv[3]);
     if (st) return SGEMV_EINVAL;
+    if (version == SGEMV_LAYOUT_NG && hv[3] < 2 * SGEMV_GROUP) return SGEMV_EINVAL;
     uint64_t ho[5];
     std::memcpy(ho, h + 24, 40);
     sgemv_desc d;

@@ -835,7 +835,182 @@ __device__ __forceinline__ void fs_dense(const RunArgs& a, FsShared<MT, W>& fs, 
     fs_compute<MT, NP, W>(fs, wave, lane, blk, w, xp, mdv, mdh.z4, v4);
 }
 
-template <int MT, bool Z4, int W, bool LIST>
+// ---------------------------------------------------------------------------
+// layout version 3: groups along the outputs
+// ---------------------------------------------------------------------------
+//
+// One (s, z) per input column and 128 outputs; a half tile's two groups of
+// column k are 8 bytes at md3[k] (md3 = the half tile's metadata row).  A
+// wavefront loads the metadata of its listed positions lane and lane + 64
+// (both loads unconditional: positions past the list re-read the first
+// column), issued before its weight loads, and keeps it in the LDS rows that
+// version 1's scales would use.  Lane (slot c, block o) then takes, for each
+// column pair, the (s, z) of its outputs' group (o / 4): it folds the scales
+// into the activations (s * x, rounded once to fp16) and subtracts
+// 1024 + z (1024 + 16 z for high nibbles) from the magic-number codes, so
+// q - z stays exact and each pair is one v_dot2 per output as in version 1;
+// the 1/16 of the high nibbles is applied after the slot sums.
+
+// Column pair (A, B) of one lane against its 8 outputs 8d .. 8d + 7, groups
+// along the outputs: zl = (1024 + z_A, 1024 + z_B), zh = (1024 + 16 z_A,
+// 1024 + 16 z_B), xq = the scaled activations of A and B.
+template <int MT>
+__device__ __forceinline__ void fs_pair8_ng(uint32_t Ad, uint32_t Bd, uint32_t zl, uint32_t zh, const uint32_t (&xq)[MT],
+                                            uint32_t vmagic, float (&acc)[MT][8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t sel = (0x0Cu << 24) | ((uint32_t)i << 16) | (0x0Cu << 8) | (4u + i);
+        const uint32_t R = __builtin_amdgcn_perm(Ad, Bd, sel);
+        const half2_t lo = as_h2(and_or(R, 0x000F000Fu, vmagic)) - as_h2(zl);   // q - z
+        const half2_t hi = as_h2(and_or(R, 0x00F000F0u, vmagic)) - as_h2(zh);   // 16 (q - z)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            acc[m][2 * i] = __builtin_amdgcn_fdot2(lo, as_h2(xq[m]), acc[m][2 * i], false);
+            acc[m][2 * i + 1] = __builtin_amdgcn_fdot2(hi, as_h2(xq[m]), acc[m][2 * i + 1], false);
+        }
+    }
+}
+
+// The weights' arithmetic of NP column pairs per lane (pair pr at list
+// position 2 NP slot + 2 pr), groups along the outputs; mdl holds the
+// metadata of positions lane and lane + 64.
+template <int MT, int NP, int W>
+__device__ __forceinline__ void fs_compute_ng(FsShared<MT, W>& fs, int wave, int lane, int slot, int blk,
+                                              const u32x4 (&w)[2 * NP], const uint32_t (&xp)[NP][MT],
+                                              const uint2 (&mdl)[2], float (&v4)[MT][4]) {
+    uint2* md3s = reinterpret_cast<uint2*>(&fs.sc[wave][0]);   // 128 positions
+    md3s[lane] = mdl[0];
+    md3s[lane + 64] = mdl[1];
+    __builtin_amdgcn_wave_barrier();
+    const bool second = blk >= 4;   // the lane's 32 outputs lie in the half tile's second group
+    const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    const half2_t k16 = {(_Float16)16.0f, (_Float16)16.0f};
+    uint32_t zl[NP], zh[NP], xq[NP][MT];
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+        const int p = 2 * NP * slot + 2 * pr;
+        const uint2 ma = md3s[p], mb = md3s[p + 1];
+        const uint32_t wa = second ? ma.y : ma.x, wb = second ? mb.y : mb.x;   // s bits | z bits << 16
+        const half2_t s2 = as_h2((wa & 0xFFFFu) | (wb << 16));
+        const half2_t z2 = as_h2((wa >> 16) | (wb & 0xFFFF0000u));
+        zl[pr] = __builtin_bit_cast(uint32_t, z2 + k1024);
+        zh[pr] = __builtin_bit_cast(uint32_t, z2 * k16 + k1024);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) xq[pr][m] = __builtin_bit_cast(uint32_t, as_h2(xp[pr][m]) * s2);
+    }
+    const uint32_t vmagic = 0x64006400u | __builtin_amdgcn_mbcnt_lo(0u, 0u);  // per-lane (VGPR) copy
+    // the lane's final outputs sp_out(lane, d) are odd (high nibbles) when lane bit 3 is set
+    const float f = ((lane >> 3) & 1) ? 0.0625f : 1.0f;
+    if constexpr (MT == 1) {
+        float acc[4][MT][8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int r = 0; r < 8; ++r) acc[d][0][r] = 0.f;
+#pragma unroll
+        for (int pr = 0; pr < NP; ++pr) {
+            const u32x4 A = w[2 * pr], B = w[2 * pr + 1];
+            const uint32_t Ad[4] = {A.x, A.y, A.z, A.w}, Bd[4] = {B.x, B.y, B.z, B.w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) fs_pair8_ng<MT>(Ad[d], Bd[d], zl[pr], zh[pr], xq[pr], vmagic, acc[d]);
+        }
+#pragma unroll
+        for (int d = 0; d < 4; ++d) v4[0][d] = f * sp_reduce8(acc[d][0], lane);
+    } else {  // two rows: 8 outputs at a time (register budget)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            float acc[MT][8];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) acc[m][r] = 0.f;
+#pragma unroll
+            for (int pr = 0; pr < NP; ++pr) {
+                const u32x4 A = w[2 * pr], B = w[2 * pr + 1];
+                const uint32_t Ad = d == 0 ? A.x : d == 1 ? A.y : d == 2 ? A.z : A.w;
+                const uint32_t Bd = d == 0 ? B.x : d == 1 ? B.y : d == 2 ? B.z : B.w;
+                fs_pair8_ng<MT>(Ad, Bd, zl[pr], zh[pr], xq[pr], vmagic, acc);
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) v4[m][d] = f * sp_reduce8(acc[m], lane);
+        }
+    }
+}
+
+// fs_block for groups along the outputs: the metadata of the listed
+// positions, then the weights, then the arithmetic.
+template <int MT, int NP, int W>
+__device__ __forceinline__ void fs_block_ng(FsShared<MT, W>& fs, int wave, int lane, int slot, int blk, int nact,
+                                            int K, const uint8_t* __restrict__ wcol, const uint2* __restrict__ md3,
+                                            float (&v4)[MT][4]) {
+    const int kfirst = fs.k[wave][0];
+    int kk[2 * NP];
+    uint32_t xp[NP][MT];
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+        const int p = 2 * NP * slot + 2 * pr;          // even, below kFsCols: 8-byte aligned pairs
+        const int2 k2 = *reinterpret_cast<const int2*>(&fs.k[wave][p]);
+        const bool ok0 = p < nact, ok1 = p + 1 < nact;
+        const int k0 = ok0 ? k2.x : kfirst, k1 = ok1 ? k2.y : kfirst;
+        kk[2 * pr] = (unsigned)k0 < (unsigned)K ? k0 : K - 1;
+        kk[2 * pr + 1] = (unsigned)k1 < (unsigned)K ? k1 : K - 1;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint32_t x2 = *reinterpret_cast<const uint32_t*>(&fs.xs[wave][m][p]);
+            xp[pr][m] = (ok0 ? (x2 & 0xFFFFu) : 0u) | (ok1 ? (x2 & 0xFFFF0000u) : 0u);
+        }
+    }
+    uint2 mdl[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int pos = lane + 64 * h;
+        int k = pos < nact ? fs.k[wave][pos] : kfirst;
+        k = (unsigned)k < (unsigned)K ? k : K - 1;
+        mdl[h] = md3[k];
+    }
+    u32x4 w[2 * NP];
+#pragma unroll
+    for (int j = 0; j < 2 * NP; ++j)
+        w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wcol + (size_t)kk[j] * (2 * kHalfRun)) + blk);
+    fs_compute_ng<MT, NP, W>(fs, wave, lane, slot, blk, w, xp, mdl, v4);
+}
+
+// The dense path for groups along the outputs (every column of the group).
+template <int MT, int W>
+__device__ __forceinline__ void fs_dense_ng(const RunArgs& a, FsShared<MT, W>& fs, int wave, int lane, int slot,
+                                            int blk, int kw, const uint8_t* __restrict__ wcol,
+                                            const uint2* __restrict__ md3, float (&v4)[MT][4]) {
+    constexpr int NP = kFsCols / 16;        // 8 column pairs per lane
+    const int k0 = kw + 2 * NP * slot;      // the lane's 16 consecutive columns
+    uint32_t xp[NP][MT];
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int mr = m < a.M ? m : a.M - 1;
+            xp[pr][m] = *reinterpret_cast<const uint32_t*>(a.x + (size_t)mr * a.ldx + k0 + 2 * pr);
+        }
+    const uint2 mdl[2] = {md3[kw + lane], md3[kw + lane + 64]};
+    u32x4 w[2 * NP];
+#pragma unroll
+    for (int j = 0; j < 2 * NP; ++j)
+        w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wcol + (size_t)(k0 + j) * (2 * kHalfRun)) + blk);
+    if (!a.unmasked) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint32_t code = code_of(a.tc, m < a.M ? m : a.M - 1);
+#pragma unroll
+            for (int pr = 0; pr < NP; ++pr) {
+                const uint32_t v = xp[pr][m];
+                xp[pr][m] = (is_active(v & 0xFFFFu, code) ? (v & 0xFFFFu) : 0u) |
+                            (is_active(v >> 16, code) ? (v & 0xFFFF0000u) : 0u);
+            }
+        }
+    }
+    fs_compute_ng<MT, NP, W>(fs, wave, lane, slot, blk, w, xp, mdl, v4);
+}
+
+template <int MT, int V, int W, bool LIST>
 __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
     int bid = blockIdx.x;
     if (a.idx_out) {  // block 0 writes the list
@@ -862,11 +1037,16 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
 
     const int tt = vt >> 1, hh = vt & 1;
     const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
-    const MdHalf mdh = md_half<Z4>(a, tt, hh);
+    const MdHalf mdh = md_half<V == SGEMV_LAYOUT_Z4>(a, tt, hh);
+    const uint2* __restrict__ md3 = reinterpret_cast<const uint2*>(a.md) + (size_t)vt * K;   // version 3
 
     if (a.all_cols) {  // every column listed: the dense path
         float v4[MT][4] = {};
-        if (has) fs_dense<MT, W>(a, fs, wave, lane, slot, blk, kw, wcol, mdh, g, v4);
+        if constexpr (V == SGEMV_LAYOUT_NG) {
+            if (has) fs_dense_ng<MT, W>(a, fs, wave, lane, slot, blk, kw, wcol, md3, v4);
+        } else if (has) {
+            fs_dense<MT, W>(a, fs, wave, lane, slot, blk, kw, wcol, mdh, g, v4);
+        }
         sp_finish<MT, W>(a, vt, seg, S, wave, lane, v4, lds.g.sh);
         return;
     }
@@ -935,6 +1115,23 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
     // 4. np column pairs per lane (straight-line code per np, so that every
     //      pair waits only for its own loads)
     float v4[MT][4] = {};
+    if constexpr (V == SGEMV_LAYOUT_NG) {
+#define SG_NG(n) fs_block_ng<MT, n, W>(fs, wave, lane, slot, blk, nact, K, wcol, md3, v4)
+        switch (np) {
+            case 1: SG_NG(1); break;
+            case 2: SG_NG(2); break;
+            case 3: SG_NG(3); break;
+            case 4: SG_NG(4); break;
+            case 5: SG_NG(5); break;
+            case 6: SG_NG(6); break;
+            case 7: SG_NG(7); break;
+            case 8: SG_NG(8); break;
+            default: break;
+        }
+#undef SG_NG
+        sp_finish<MT, W>(a, vt, seg, S, wave, lane, v4, lds.g.sh);
+        return;
+    }
     switch (np) {
         case 1: fs_block<MT, 1, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdh, g, v4); break;
         case 2: fs_block<MT, 2, W>(fs, wave, lane, slot, blk, nact, K, wcol, mdh, g, v4); break;
@@ -953,16 +1150,16 @@ __device__ __forceinline__ void fs_body(const RunArgs& a, FsLds<MT, W>& lds) {
 // budget, for grids of at most one workgroup per CU), and four (two
 // workgroups per CU, so that one's loads overlap the other's latency in
 // grids that take several rounds).
-template <int MT, bool Z4, int W, bool LIST>
+template <int MT, int V, int W, bool LIST>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fs(RunArgs a) {
     __shared__ FsLds<MT, W> lds;
-    fs_body<MT, Z4, W, LIST>(a, lds);
+    fs_body<MT, V, W, LIST>(a, lds);
 }
 
-template <int MT, bool Z4, bool LIST>
+template <int MT, int V, bool LIST>
 __global__ __launch_bounds__(kFsW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_fs4(RunArgs a) {
     __shared__ FsLds<MT, kFsW> lds;
-    fs_body<MT, Z4, kFsW, LIST>(a, lds);
+    fs_body<MT, V, kFsW, LIST>(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1453,7 +1650,8 @@ int check_desc(const sgemv_desc* d) {
     if (d->tile_n < 64 || d->tile_n > 1024 || (d->tile_n & (d->tile_n - 1)) || d->N % d->tile_n)
         return SGEMV_ESIZE;
     sgemv_desc ref;
-    if (d->version != SGEMV_LAYOUT_PAIRS && d->version != SGEMV_LAYOUT_Z4) return SGEMV_EINVAL;
+    if (d->version != SGEMV_LAYOUT_PAIRS && d->version != SGEMV_LAYOUT_Z4 && d->version != SGEMV_LAYOUT_NG)
+        return SGEMV_EINVAL;
     sgemv_layout_fill_desc(d->N, d->K, d->tile_n, d->version, &ref);
     if (d->w_off != ref.w_off || d->w_bytes != ref.w_bytes || d->m_off != ref.m_off ||
         d->m_bytes != ref.m_bytes || d->total_bytes != ref.total_bytes)
@@ -1578,20 +1776,26 @@ int run_common(const sgemv_desc* d, const void* packed, const void* x, int M, in
 
 // The fused kernels; with all_cols every column is listed (the dense GEMV,
 // rows masked by their thresholds unless thr is NULL).
-template <bool Z4, bool LIST>
+template <int V, bool LIST>
 void launch_fs(int M, int W, bool one_round, dim3 grid, const RunArgs& a, hipStream_t s) {
-    if (M == 1 && W == kFsWSmall) hipLaunchKernelGGL((k_fs<1, Z4, kFsWSmall, LIST>), grid, dim3(kFsWSmall * 64), 0, s, a);
-    else if (M == 1 && one_round) hipLaunchKernelGGL((k_fs<1, Z4, kFsW, LIST>), grid, dim3(kFsW * 64), 0, s, a);
-    else if (M == 1) hipLaunchKernelGGL((k_fs4<1, Z4, LIST>), grid, dim3(kFsW * 64), 0, s, a);
-    else if (one_round) hipLaunchKernelGGL((k_fs<2, Z4, kFsW, LIST>), grid, dim3(kFsW * 64), 0, s, a);
-    else hipLaunchKernelGGL((k_fs4<2, Z4, LIST>), grid, dim3(kFsW * 64), 0, s, a);
+    if (M == 1 && W == kFsWSmall) hipLaunchKernelGGL((k_fs<1, V, kFsWSmall, LIST>), grid, dim3(kFsWSmall * 64), 0, s, a);
+    else if (M == 1 && one_round) hipLaunchKernelGGL((k_fs<1, V, kFsW, LIST>), grid, dim3(kFsW * 64), 0, s, a);
+    else if (M == 1) hipLaunchKernelGGL((k_fs4<1, V, LIST>), grid, dim3(kFsW * 64), 0, s, a);
+    else if (one_round) hipLaunchKernelGGL((k_fs<2, V, kFsW, LIST>), grid, dim3(kFsW * 64), 0, s, a);
+    else hipLaunchKernelGGL((k_fs4<2, V, LIST>), grid, dim3(kFsW * 64), 0, s, a);
 }
 
-template <bool Z4>
+// Version 3 has no many-row kernel: the host rejects M > 2 for it.
+template <int V>
 void launch_fused(int M, int W, bool one_round, dim3 grid, const RunArgs& a, hipStream_t s) {
-    if (M > 2) hipLaunchKernelGGL(k_fm<Z4>, grid, dim3(fm::kWaves * 64), 0, s, a);
-    else if (a.lidx) launch_fs<Z4, true>(M, W, one_round, grid, a, s);
-    else launch_fs<Z4, false>(M, W, one_round, grid, a, s);
+    if constexpr (V != SGEMV_LAYOUT_NG) {
+        if (M > 2) {
+            hipLaunchKernelGGL(k_fm<V == SGEMV_LAYOUT_Z4>, grid, dim3(fm::kWaves * 64), 0, s, a);
+            return;
+        }
+    }
+    if (a.lidx) launch_fs<V, true>(M, W, one_round, grid, a, s);
+    else launch_fs<V, false>(M, W, one_round, grid, a, s);
 }
 
 int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int ldx, const float* thr,
@@ -1599,6 +1803,7 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
               bool all_cols, const int32_t* lidx, const int32_t* lcount) {
     int st = check_fused_args(d, packed, x, M, ldx, thr, idx, count, y, ldy, flags, all_cols || lidx);
     if (st) return st;
+    if (d->version == SGEMV_LAYOUT_NG && M > 2) return SGEMV_EUNSUPPORTED;
 
     RunArgs a;
     std::memset(&a, 0, sizeof a);
@@ -1661,8 +1866,9 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
     const dim3 grid((unsigned)(a.tiles * a.segs + a.gblocks));  // + the list's workgroups
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool one_round = a.tiles * a.segs <= kFsOneRound;
-    if (a.md_z4) launch_fused<true>(M, W, one_round, grid, a, s);
-    else launch_fused<false>(M, W, one_round, grid, a, s);
+    if (d->version == SGEMV_LAYOUT_NG) launch_fused<SGEMV_LAYOUT_NG>(M, W, one_round, grid, a, s);
+    else if (a.md_z4) launch_fused<SGEMV_LAYOUT_Z4>(M, W, one_round, grid, a, s);
+    else launch_fused<SGEMV_LAYOUT_PAIRS>(M, W, one_round, grid, a, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         g_last_hip_error = (int)e;

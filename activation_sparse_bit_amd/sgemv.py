@@ -26,11 +26,13 @@ SGEMV_GROUP = 128
 SGEMV_TILE_N = 512
 SGEMV_LAYOUT_PAIRS = 1    # layout version 1: (s, z) fp16 pairs
 SGEMV_LAYOUT_Z4 = 2       # layout version 2: fp16 scales, 4-bit zero-points
+SGEMV_LAYOUT_NG = 3       # layout version 3: groups along N, (s, z) per column and 128 outputs
 SGEMV_MAX_BATCH = 16
 SGEMV_MAX_K = 65536
 SGEMV_MAX_N = 1 << 20
 
-EXPORTED = ["sgemv_pack_layout", "sgemv_pack_layout_z4", "sgemv_pack_layout_parts", "sgemv_desc_from_header",
+EXPORTED = ["sgemv_pack_layout", "sgemv_pack_layout_z4", "sgemv_pack_layout_ng", "sgemv_pack_layout_parts",
+            "sgemv_desc_from_header",
             "sgemv_gather_indices",
             "sgemv_run", "sgemv_run_batched", "sgemv_run_fused", "sgemv_run_fused_static", "sgemv_workspace_bytes",
             "sgemv_strerror", "sgemv_last_hip_error"]
@@ -71,6 +73,8 @@ def lib():
     L.sgemv_pack_layout.restype = ctypes.c_int
     L.sgemv_pack_layout_z4.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, sz, pd]
     L.sgemv_pack_layout_z4.restype = ctypes.c_int
+    L.sgemv_pack_layout_ng.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, sz, pd]
+    L.sgemv_pack_layout_ng.restype = ctypes.c_int
     L.sgemv_pack_layout_parts.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, u32, vp, sz, pd]
     L.sgemv_pack_layout_parts.restype = ctypes.c_int
     L.sgemv_desc_from_header.argtypes = [vp, sz, pd]
@@ -214,7 +218,10 @@ def sgemv_pack_layout(q, scales_f16, zeros_f16, tile_n: int = SGEMV_TILE_N, _whi
     s = np.ascontiguousarray(s, dtype=np.uint16)
     z = np.ascontiguousarray(z, dtype=np.uint16)
     N, K = q.shape
-    if s.shape != (N, K // SGEMV_GROUP) or z.shape != (N, K // SGEMV_GROUP):
+    if _which == "sgemv_pack_layout_ng":
+        if s.shape != (N // SGEMV_GROUP, K) or z.shape != (N // SGEMV_GROUP, K) or N % SGEMV_GROUP:
+            raise ValueError("scales/zeros must be [N/128][K] (groups along N)")
+    elif s.shape != (N, K // SGEMV_GROUP) or z.shape != (N, K // SGEMV_GROUP):
         raise ValueError("scales/zeros must be [N][K/128]")
     d = Desc()
     fn = getattr(lib(), _which)
@@ -231,6 +238,13 @@ def sgemv_pack_layout_z4(q, scales_f16, zeros_f16, tile_n: int = SGEMV_TILE_N):
     return sgemv_pack_layout(q, scales_f16, zeros_f16, tile_n, _which="sgemv_pack_layout_z4")
 
 
+def sgemv_pack_layout_ng(q, scales_f16, zeros_f16, tile_n: int = SGEMV_TILE_N):
+    """Layout version 3, for weights quantized with groups along N: scales
+    and zero-points are uint16 [N/128][K] (one per input column and 128
+    outputs).  The device calls take it with one or two rows."""
+    return sgemv_pack_layout(q, scales_f16, zeros_f16, tile_n, _which="sgemv_pack_layout_ng")
+
+
 def sgemv_pack_layout_parts(parts, tile_n: int = SGEMV_TILE_N, version: int = SGEMV_LAYOUT_PAIRS):
     """One blob for several projections sharing their input, rows stacked in
     the order given.  `parts` is a list of (q, scales_f16, zeros_f16), each
@@ -243,8 +257,11 @@ def sgemv_pack_layout_parts(parts, tile_n: int = SGEMV_TILE_N, version: int = SG
         z = np.asarray(z)
         s_ = np.ascontiguousarray(s_.view(np.uint16) if s_.dtype == np.float16 else s_, dtype=np.uint16)
         z = np.ascontiguousarray(z.view(np.uint16) if z.dtype == np.float16 else z, dtype=np.uint16)
-        if s_.shape != (q.shape[0], q.shape[1] // SGEMV_GROUP) or z.shape != s_.shape:
-            raise ValueError("scales/zeros must be [N][K/128] of their part")
+        want = ((q.shape[0] // SGEMV_GROUP, q.shape[1]) if version == SGEMV_LAYOUT_NG
+                else (q.shape[0], q.shape[1] // SGEMV_GROUP))
+        if s_.shape != want or z.shape != s_.shape:
+            raise ValueError("scales/zeros of a part must be " +
+                             ("[N/128][K]" if version == SGEMV_LAYOUT_NG else "[N][K/128]"))
         qs.append(q); ss.append(s_); zs.append(z); ns.append(q.shape[0])
     Ks = {q.shape[1] for q in qs}
     if len(Ks) != 1:
@@ -395,10 +412,10 @@ class PackedMatrix:
     """A packed matrix on the device with its workspace (torch tensors)."""
 
     def __init__(self, q, scales_f16, zeros_f16, device="cuda", max_batch: int = SGEMV_MAX_BATCH,
-                 z4: bool = False, _packed=None):
+                 z4: bool = False, _packed=None, ng: bool = False):
         import torch
         if _packed is None:
-            pack = sgemv_pack_layout_z4 if z4 else sgemv_pack_layout
+            pack = sgemv_pack_layout_ng if ng else sgemv_pack_layout_z4 if z4 else sgemv_pack_layout
             _packed = pack(q, scales_f16, zeros_f16)
         self.desc, blob = _packed
         self.blob = torch.from_numpy(blob).to(device)

@@ -11,7 +11,8 @@
  * this library provides one call for each, plus the batched variant:
  *
  *   sgemv_pack_layout     host: int4 codes + fp16 scale/zero -> packed blob
- *                         (sgemv_pack_layout_z4: the same with 4-bit zeros)
+ *                         (sgemv_pack_layout_z4: the same with 4-bit zeros;
+ *                         sgemv_pack_layout_ng: groups along the outputs)
  *   sgemv_gather_indices  device: threshold x, emit the ascending list of
  *                         active indices and its length
  *   sgemv_run             device: y = W . x over the listed columns (M = 1)
@@ -69,7 +70,7 @@ typedef struct sgemv_desc {
     uint64_t m_off;        /* byte offset of the scale/zero region         */
     uint64_t m_bytes;      /* (K/128)*N*4, or (K/128)*N*5/2 for version 2  */
     uint64_t total_bytes;  /* size of the whole blob                       */
-    uint32_t version;      /* SGEMV_LAYOUT_PAIRS or SGEMV_LAYOUT_Z4        */
+    uint32_t version;      /* SGEMV_LAYOUT_PAIRS, _Z4 or _NG               */
     uint32_t reserved;     /* 0                                            */
 } sgemv_desc;
 
@@ -90,6 +91,7 @@ enum sgemv_status {
 #define SGEMV_OUT_F32     1u    /* flag: y is fp32 instead of fp16         */
 #define SGEMV_LAYOUT_PAIRS 1u   /* layout version 1: (s, z) fp16 pairs     */
 #define SGEMV_LAYOUT_Z4    2u   /* layout version 2: fp16 s, 4-bit z       */
+#define SGEMV_LAYOUT_NG    3u   /* layout version 3: groups along N        */
 
 /*
  * sgemv_pack_layout - re-lay int4 weights so that each active input index
@@ -158,24 +160,60 @@ int sgemv_pack_layout_z4(const uint8_t* q, const uint16_t* scales_f16,
                          size_t out_capacity, sgemv_desc* desc_out);
 
 /*
+ * sgemv_pack_layout_ng - layout version 3, for weights quantized with their
+ * groups along the outputs: one fp16 scale s and one integer zero-point z
+ * per input column k and group b of 128 consecutive outputs,
+ *   w^[n][k] = s[n/128][k] * (q[n][k] - z[n/128][k]).
+ * The page asks for a quantization layout consistent with activation
+ * sparsity (Abstract); with groups along the outputs a column's scale and
+ * zero-point belong to that column alone, so they are read only when the
+ * column is active and the metadata bytes fall with the sparsity, as the
+ * weight bytes do.
+ *
+ *   header as above with version 3; m_bytes = (N/128)*K*4
+ *   weight bytes exactly those of sgemv_pack_layout
+ *   metadata     m_off + ((h*K + k)*2 + e)*4 : fp16 bits of s[2h + e][k],
+ *                then fp16 bits of z[2h + e][k]  (h < N/256, e in {0, 1}):
+ *                per 256 outputs and column, 8 contiguous bytes
+ *
+ *   q          host uint8 [N][K], row-major, values 0..15
+ *   scales_f16 host uint16 [N/128][K], fp16 bit patterns of finite values
+ *   zeros_f16  host uint16 [N/128][K], fp16 bit patterns of integers 0..15
+ *   tile_n     power of two in [256, 1024] dividing N
+ * Other arguments, ownership and errors as for sgemv_pack_layout (ESIZE
+ * also for tile_n < 256).  The device calls take this version with one or
+ * two rows; with 3..16 rows they return SGEMV_EUNSUPPORTED.  There the
+ * kernels fold each column's scale into its activation (s * x rounded once
+ * to fp16) and subtract the zero-point exactly, so y differs from the exact
+ * product by at most 2^-11 * sum_k |w^[n][k]| |x[k]| before the final
+ * rounding of y (versions 1 and 2: fp32 accumulation error only).
+ */
+int sgemv_pack_layout_ng(const uint8_t* q, const uint16_t* scales_f16,
+                         const uint16_t* zeros_f16, int32_t N, int32_t K,
+                         int32_t group, int32_t tile_n, void* out,
+                         size_t out_capacity, sgemv_desc* desc_out);
+
+/*
  * sgemv_pack_layout_parts - one blob for several projections that read the
  * same activations (the query, key and value projections of an attention
  * block; the gate and up projections of a gated feed-forward block), their
  * rows stacked along N in the order given, so that one device call
  * thresholds x once and computes all of them.  The blob is exactly the one
- * sgemv_pack_layout (version SGEMV_LAYOUT_PAIRS) or sgemv_pack_layout_z4
- * (SGEMV_LAYOUT_Z4) writes for the row-concatenated matrix; projection p's
+ * sgemv_pack_layout (version SGEMV_LAYOUT_PAIRS), sgemv_pack_layout_z4
+ * (SGEMV_LAYOUT_Z4) or sgemv_pack_layout_ng (SGEMV_LAYOUT_NG) writes for the
+ * row-concatenated matrix; projection p's
  * outputs are y[off_p .. off_p + n_part[p]) with off_p the sum of the
  * earlier n_part.  Host only, no HIP call.
  *
  *   parts      number of projections, >= 1
  *   q          host array of `parts` pointers, part p: uint8 [n_part[p]][K]
  *   scales_f16 host array of `parts` pointers, part p: uint16 [n_part[p]][K/128]
+ *              ([n_part[p]/128][K] for SGEMV_LAYOUT_NG)
  *   zeros_f16  likewise for the zero-points
  *   n_part     host int32 [parts]: rows of each part, each a multiple of
  *              tile_n (no tile mixes two projections)
  *   K, group, tile_n, out, out_capacity, desc_out as for sgemv_pack_layout
- *   version    SGEMV_LAYOUT_PAIRS or SGEMV_LAYOUT_Z4
+ *   version    SGEMV_LAYOUT_PAIRS, SGEMV_LAYOUT_Z4 or SGEMV_LAYOUT_NG
  * Returns SGEMV_OK; EINVAL for parts < 1, NULL arrays or parts, a bad code,
  * scale or zero-point, a bad version; ESIZE for a part that is not whole
  * tiles, a total N out of range, or too small a capacity.  With out == NULL
@@ -188,7 +226,7 @@ int sgemv_pack_layout_parts(int32_t parts, const uint8_t* const* q,
                             void* out, size_t out_capacity, sgemv_desc* desc_out);
 
 /* Parse and check the 64-byte header of a blob held in host memory (for a
- * blob that was saved and reloaded; version 1 or 2).  EINVAL on a bad magic,
+ * blob that was saved and reloaded; version 1, 2 or 3).  EINVAL on a bad magic,
  * version or inconsistent offsets. */
 int sgemv_desc_from_header(const void* header, size_t bytes, sgemv_desc* desc_out);
 

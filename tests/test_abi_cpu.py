@@ -67,13 +67,39 @@ def test_packer_z4_matches_spec(N, K, tile):
     assert b0[d.m_off + 2 * tile] & 0x0F == 0
 
 
-@pytest.mark.parametrize("version", [1, 2])
+@pytest.mark.parametrize("N,K,tile", [(512, 128, 512), (1024, 384, 512), (256, 256, 256),
+                                      (2048, 256, 1024), (4096, 1024, 512)])
+def test_packer_ng_matches_spec(N, K, tile):
+    """Layout version 3 (groups along N) byte for byte against the spec, its
+    weight region equal to version 1's, and tiles below 256 outputs refused."""
+    q, s, z = synth.random_int4_problem_ng(N * 3 + K, N, K)
+    d, blob = sgemv.sgemv_pack_layout_ng(q, s, z, tile)
+    ref = oracle.pack_spec(q, s, z, tile, 3)
+    assert blob.shape == ref.shape and np.array_equal(blob, ref)
+    for k, v in oracle.header_fields(N, K, tile, 3).items():
+        assert getattr(d, k) == v, k
+    assert d.version == sgemv.SGEMV_LAYOUT_NG
+    q1, s1, z1 = synth.random_int4_problem(1, N, K)
+    d1, blob1 = sgemv.sgemv_pack_layout(q, s1, z1, tile)
+    assert np.array_equal(blob[d.w_off:d.m_off], blob1[d1.w_off:d1.m_off])
+    assert sgemv.sgemv_desc_from_header(blob).as_dict() == d.as_dict()
+    with pytest.raises(sgemv.SgemvError, match="size"):
+        sgemv.sgemv_pack_layout_ng(q, s, z, 128)
+    bad = z.copy(); bad[0, 5] = np.float16(2.5).view(np.uint16)
+    with pytest.raises(sgemv.SgemvError):
+        sgemv.sgemv_pack_layout_ng(q, s, bad, tile)
+
+
+@pytest.mark.parametrize("version", [1, 2, 3])
 @pytest.mark.parametrize("rows,tile", [((512, 1024, 512), 512), ((1024,), 512), ((256, 64, 128), 64)])
 def test_packer_parts_matches_spec(rows, tile, version):
     """Projections packed as parts: byte for byte the layout specification
     of the row-concatenated matrix."""
     K = 384
-    parts = [synth.random_int4_problem(31 * i + n, n, K) for i, n in enumerate(rows)]
+    if version == 3 and tile < 256:
+        pytest.skip("groups along N need tiles of at least 256 outputs")
+    gen = synth.random_int4_problem_ng if version == 3 else synth.random_int4_problem
+    parts = [gen(31 * i + n, n, K) for i, n in enumerate(rows)]
     d, blob = sgemv.sgemv_pack_layout_parts(parts, tile_n=tile, version=version)
     q = np.concatenate([p[0] for p in parts])
     s = np.concatenate([p[1] for p in parts])
@@ -97,7 +123,7 @@ def test_packer_parts_validation():
     f = L.sgemv_pack_layout_parts
     assert f(0, qa, sa, za, n_ok.ctypes.data, K, 128, 512, 1, None, 0, ctypes.byref(d)) == E.SGEMV_EINVAL
     assert f(1, qa, sa, za, None, K, 128, 512, 1, None, 0, ctypes.byref(d)) == E.SGEMV_EINVAL
-    assert f(1, qa, sa, za, n_ok.ctypes.data, K, 128, 512, 3, None, 0, ctypes.byref(d)) == E.SGEMV_EINVAL
+    assert f(1, qa, sa, za, n_ok.ctypes.data, K, 128, 512, 4, None, 0, ctypes.byref(d)) == E.SGEMV_EINVAL
     assert f(1, qa, sa, za, n_bad.ctypes.data, K, 128, 512, 1, None, 0, ctypes.byref(d)) == E.SGEMV_ESIZE
     assert f(1, qa, sa, za, n_ok.ctypes.data, K, 128, 512, 1, None, 0, ctypes.byref(d)) == E.SGEMV_OK
     blob = np.empty(d.total_bytes, dtype=np.uint8)
