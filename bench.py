@@ -67,11 +67,13 @@ def gather_bytes(K: int, A: int, M: int = 1) -> int:
     return M * K * 2 + A * 4 + 4
 
 
-def fused_bytes(A: int, Ag: int, N: int, K: int, M: int = 1, with_list: bool = True, z4: bool = False) -> int:
+def fused_bytes(A: int, Ag: int, N: int, K: int, M: int = 1, with_list: bool = True, z4: bool = False,
+                ng: bool = False) -> int:
     """One fused step: weight columns and metadata as above (2.5 instead of
-    4 bytes per output and touched group with the compact metadata), every
+    4 bytes per output and touched group with the compact metadata; with
+    groups along N, 4 bytes per active column and 128 outputs), every
     activation once, the list and count (when written) and the output."""
-    md = Ag * N * 5 // 2 if z4 else Ag * N * 4
+    md = A * (N // 128) * 4 if ng else Ag * N * 5 // 2 if z4 else Ag * N * 4
     return A * N // 2 + md + M * K * 2 + (A * 4 + 4 if with_list else 0) + M * N * 2
 
 
@@ -312,6 +314,28 @@ def main():
         del cps, bd
         return res
 
+    def measure_fused_ng(ps, steps, warmup):
+        """The step on the same draw quantized with groups along N (layout
+        version 3: one scale and zero-point per input column and 128
+        outputs, read only with an active column)."""
+        q3, s3, z3 = synth.quantized_weights_ng(0, N_DOWN, K_DOWN, 0.02)
+        d3, b3 = sgemv.sgemv_pack_layout_ng(q3, s3, z3)
+        R3 = rotation(fused_bytes(A90, K_DOWN // 128, N_DOWN, K_DOWN, ng=True))
+        bd = torch.from_numpy(b3).to(dev)
+        cps = [bd] + [bd.clone() for _ in range(R3 - 1)]
+        res = {}
+        for p in ps:
+            t = synth.percentile_threshold(x, p)
+            us = graph_time([lambda i: sgemv.sgemv_run_fused(d3, cps[i % R3], xd, [t], y, ws, idx, cnt)],
+                            steps, warmup)
+            A, Ag = list_now()
+            fb = fused_bytes(A, Ag, N_DOWN, K_DOWN, ng=True)
+            res[f"fused_p{int(p * 100)}_ng"] = {"p": p, "active": A, "groups_touched": Ag, "us_per_step": us,
+                                               "bytes": fb, "GBps": fb / (us * 1e-6) / 1e9,
+                                               "frac_hbm_peak": fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        del cps, bd
+        return res
+
     def measure_split(p, steps, warmup, dense=False, cold=False):
         t = synth.percentile_threshold(x, p)
         gat = lambda i: sgemv.sgemv_gather_indices(xd, [t], idx, cnt)
@@ -546,6 +570,7 @@ def main():
             sweep[f"fused_p{int(p * 100)}"] = measure_fused(p, args.steps, args.warmup, cold=True)
         sweep["fused_p50_no_list"] = measure_fused(0.5, args.steps, args.warmup, with_list=False)
         sweep.update(measure_fused_z4((0.5, 0.9), args.steps, args.warmup))
+        sweep.update(measure_fused_ng((0.5, 0.9), args.steps, args.warmup))
         for p in (0.5, 0.7, 0.9):
             sweep[f"split_p{int(p * 100)}"] = measure_split(p, args.steps, args.warmup)
         sweep["dense_int4"] = measure_split(0.0, args.steps, args.warmup, dense=True, cold=True)
