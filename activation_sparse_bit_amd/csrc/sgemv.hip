@@ -20,6 +20,9 @@
 //              row, small or short-K matrices) 4 wavefronts per workgroup
 //              (k_fs4: the 8-wavefront build for grids of several rounds);
 //              with every column listed, also the dense GEMV (no compaction).
+//              Every layout version: groups along K with (s, z) pairs or
+//              compact zero-points, or groups along N (one (s, z) per column
+//              and 128 outputs, the scale folded into the activation).
 //   k_fm       3 to 16 rows, fused (or over a given list): the union of the
 //              rows' active columns, exact fp16 dequantization in registers
 //              and v_mfma_f32_16x16x32_f16 on the matrix cores.
