@@ -1238,7 +1238,7 @@ union FmLds {
 };
 
 
-template <bool Z4>
+template <int V>
 __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fm(RunArgs a) {
     __shared__ FmLds lds;
     __shared__ uint32_t last_flag;
@@ -1313,7 +1313,8 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
 
     const int tt = vt >> 1, hh = vt & 1;
     const uint8_t* __restrict__ wcol = a.w + (size_t)tt * K * (2 * kHalfRun) + hh * kHalfRun;
-    const MdHalf mdh = md_half<Z4>(a, tt, hh);
+    const MdHalf mdh = md_half<V == SGEMV_LAYOUT_Z4>(a, tt, hh);
+    constexpr bool NG = V == SGEMV_LAYOUT_NG;   // groups along N: (s, z) per column and 128 outputs
 
     // 1. over a given list, its length (without a list the same load reads
     //    the activations and is unused, so that no path waits for it early);
@@ -1330,7 +1331,8 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int i = 0; i < 4; ++i)
         xv[i] = *reinterpret_cast<const uint4*>(a.x + (size_t)xmr * a.ldx + (has ? kw : 0) + 32 * xq + 8 * i);
     __builtin_amdgcn_sched_barrier(0);   // keeps the scale/zero load behind the activations'
-    const u32x4 mdv = md_raw4(mdh, g, 4 * lane);
+    u32x4 mdv = {0u, 0u, 0u, 0u};
+    if constexpr (!NG) mdv = md_raw4(mdh, g, 4 * lane);
 
     const uint32_t code = code_of(a.tc, xmr);
     const bool row_ok = has && xm < a.M;
@@ -1414,6 +1416,19 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
         const int lc = lane >> 3, lo = lane & 7;
         u32x4 wl[fm::kMaxCh][4];
         const int kfirst = fw.k[0];
+        // groups along N: the 8-byte metadata of union positions lane and
+        // lane + 64 (past the union: the first column), before the weights
+        uint2 md3l[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
+        if constexpr (NG) {
+            const uint2* __restrict__ md3 = reinterpret_cast<const uint2*>(a.md) + (size_t)vt * K;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int pos = lane + 64 * h;
+                int k = pos < nact ? fw.k[pos] : kfirst;
+                k = (unsigned)k < (unsigned)K ? k : K - 1;
+                md3l[h] = md3[k];
+            }
+        }
 #pragma unroll
         for (int c = 0; c < fm::kMaxCh; ++c)
 #pragma unroll
@@ -1425,8 +1440,13 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
                     reinterpret_cast<const u32x4*>(wcol + (size_t)k * (2 * kHalfRun)) + lo);
             }
         // 3a. zero codes of the weight bytes 2 lane, 2 lane + 1 (outputs 4 lane ..
-        //     4 lane + 3) and their scales in storage order
-        {
+        //     4 lane + 3) and their scales in storage order (groups along N:
+        //     the union's metadata by position, in the scales' rows)
+        if constexpr (NG) {
+            uint2* md3s = reinterpret_cast<uint2*>(&fw.sc[0]);
+            md3s[lane] = md3l[0];
+            md3s[lane + 64] = md3l[1];
+        } else {
             const u32x4 mc = md_cook4(mdv, mdh.z4);
             const uint32_t mw[4] = {mc.x, mc.y, mc.z, mc.w};
             uint32_t zpair[2];
@@ -1449,7 +1469,7 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
         // zero codes of the lane's A rows: weight byte 16 b + li, b = 0..7
         uint32_t zq[8];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) zq[b] = fw.zc[16 * b + li];
+        for (int b = 0; b < 8; ++b) zq[b] = NG ? 0u : fw.zc[16 * b + li];
         // B operands of every chunk: activations of batch row li at positions
         // c * 32 + 8 g .. + 7 (all LDS reads issued together)
         uint32_t Bx[fm::kMaxCh][4];
@@ -1492,10 +1512,42 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
                     rb[b] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                         (__attribute__((address_space(3))) i2_t*)&fw.r[8 * g + (li >> 1)][16 * b + 8 * (li & 1)]);
                 __builtin_amdgcn_sched_barrier(0);  // keep the 8 reads ahead of the products
-                const h8_t B = __builtin_bit_cast(h8_t, (u32x4){Bx[c][0], Bx[c][1], Bx[c][2], Bx[c][3]});
+                h8_t B = __builtin_bit_cast(h8_t, (u32x4){Bx[c][0], Bx[c][1], Bx[c][2], Bx[c][3]});
+                // groups along N: per group e of the half tile (output blocks
+                // 4 e .. 4 e + 3), the activations scaled by their columns'
+                // s (B operand) and the columns' zero codes by pair
+                h8_t Bg[2] = {B, B};
+                uint32_t zlg[2][4] = {}, zhg[2][4] = {};
+                if constexpr (NG) {
+                    const u32x4* mp = reinterpret_cast<const u32x4*>(&fw.sc[0]) + (c * fm::kCh + 8 * g) / 2;
+                    uint32_t mwv[8][2];   // position 8 g + j: (s | z << 16) of groups 0 and 1
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const u32x4 m4 = mp[i];
+                        mwv[2 * i][0] = m4.x; mwv[2 * i][1] = m4.y;
+                        mwv[2 * i + 1][0] = m4.z; mwv[2 * i + 1][1] = m4.w;
+                    }
+                    const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+                    const half2_t k16 = {(_Float16)16.0f, (_Float16)16.0f};
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        uint32_t bw[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t wa = mwv[2 * j][e], wb = mwv[2 * j + 1][e];
+                            const half2_t s2 = as_h2((wa & 0xFFFFu) | (wb << 16));
+                            const half2_t z2 = as_h2((wa >> 16) | (wb & 0xFFFF0000u));
+                            zlg[e][j] = __builtin_bit_cast(uint32_t, z2 + k1024);
+                            zhg[e][j] = __builtin_bit_cast(uint32_t, z2 * k16 + k1024);
+                            bw[j] = __builtin_bit_cast(uint32_t, as_h2(Bx[c][j]) * s2);
+                        }
+                        Bg[e] = __builtin_bit_cast(h8_t, (u32x4){bw[0], bw[1], bw[2], bw[3]});
+                    }
+                }
 #pragma unroll
                 for (int b = 0; b < 8; ++b) {
                     const half2_t z2 = as_h2(zq[b]);
+                    if constexpr (NG) B = Bg[b >> 2];
                     const uint32_t dw2[2] = {(uint32_t)rb[b].x, (uint32_t)rb[b].y};
                     uint32_t ae[4], ao[4];
 #pragma unroll
@@ -1504,8 +1556,10 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
                         const uint32_t Dd = dw2[j >> 1];
                         const uint32_t b0 = 2 * (j & 1);
                         const uint32_t P = __builtin_amdgcn_perm(Dd, Dd, (0x0Cu << 24) | ((b0 + 1) << 16) | (0x0Cu << 8) | b0);
-                        const half2_t e = as_h2(and_or(P, 0x000F000Fu, vmagic)) - (half2_t){z2.x, z2.x};  // q - z
-                        const half2_t o = as_h2(and_or(P, 0x00F000F0u, vmagic)) - (half2_t){z2.y, z2.y};  // 16 (q - z)
+                        const half2_t zl = NG ? as_h2(zlg[b >> 2][j]) : (half2_t){z2.x, z2.x};
+                        const half2_t zh = NG ? as_h2(zhg[b >> 2][j]) : (half2_t){z2.y, z2.y};
+                        const half2_t e = as_h2(and_or(P, 0x000F000Fu, vmagic)) - zl;  // q - z
+                        const half2_t o = as_h2(and_or(P, 0x00F000F0u, vmagic)) - zh;  // 16 (q - z)
                         ae[j] = __builtin_bit_cast(uint32_t, e);
                         ao[j] = __builtin_bit_cast(uint32_t, o);
                     }
@@ -1518,11 +1572,17 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
             }
         }
         // 4. one scale per output: D[2 b + p] row 4 g + e is storage index
-        //    32 b + 16 p + 4 g + e
+        //    32 b + 16 p + 4 g + e (groups along N: the scales are in B; the
+        //    high nibbles' 1/16 is left)
+        if constexpr (NG) {
 #pragma unroll
-        for (int bp = 0; bp < 16; ++bp) {
-            const float4 s4 = *reinterpret_cast<const float4*>(&fw.sc[16 * bp + 4 * g]);
-            D[bp].x *= s4.x; D[bp].y *= s4.y; D[bp].z *= s4.z; D[bp].w *= s4.w;
+            for (int b = 0; b < 8; ++b) D[2 * b + 1] *= 0.0625f;
+        } else {
+#pragma unroll
+            for (int bp = 0; bp < 16; ++bp) {
+                const float4 s4 = *reinterpret_cast<const float4*>(&fw.sc[16 * bp + 4 * g]);
+                D[bp].x *= s4.x; D[bp].y *= s4.y; D[bp].z *= s4.z; D[bp].w *= s4.w;
+            }
         }
     }
 
@@ -1788,14 +1848,11 @@ void launch_fs(int M, int W, bool one_round, dim3 grid, const RunArgs& a, hipStr
     else hipLaunchKernelGGL((k_fs4<2, V, LIST>), grid, dim3(kFsW * 64), 0, s, a);
 }
 
-// Version 3 has no many-row kernel: the host rejects M > 2 for it.
 template <int V>
 void launch_fused(int M, int W, bool one_round, dim3 grid, const RunArgs& a, hipStream_t s) {
-    if constexpr (V != SGEMV_LAYOUT_NG) {
-        if (M > 2) {
-            hipLaunchKernelGGL(k_fm<V == SGEMV_LAYOUT_Z4>, grid, dim3(fm::kWaves * 64), 0, s, a);
-            return;
-        }
+    if (M > 2) {
+        hipLaunchKernelGGL(k_fm<V>, grid, dim3(fm::kWaves * 64), 0, s, a);
+        return;
     }
     if (a.lidx) launch_fs<V, true>(M, W, one_round, grid, a, s);
     else launch_fs<V, false>(M, W, one_round, grid, a, s);
@@ -1806,7 +1863,6 @@ int run_fused(const sgemv_desc* d, const void* packed, const void* x, int M, int
               bool all_cols, const int32_t* lidx, const int32_t* lcount) {
     int st = check_fused_args(d, packed, x, M, ldx, thr, idx, count, y, ldy, flags, all_cols || lidx);
     if (st) return st;
-    if (d->version == SGEMV_LAYOUT_NG && M > 2) return SGEMV_EUNSUPPORTED;
 
     RunArgs a;
     std::memset(&a, 0, sizeof a);

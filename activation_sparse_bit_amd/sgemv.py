@@ -241,7 +241,7 @@ def sgemv_pack_layout_z4(q, scales_f16, zeros_f16, tile_n: int = SGEMV_TILE_N):
 def sgemv_pack_layout_ng(q, scales_f16, zeros_f16, tile_n: int = SGEMV_TILE_N):
     """Layout version 3, for weights quantized with groups along N: scales
     and zero-points are uint16 [N/128][K] (one per input column and 128
-    outputs).  The device calls take it with one or two rows."""
+    outputs)."""
     return sgemv_pack_layout(q, scales_f16, zeros_f16, tile_n, _which="sgemv_pack_layout_ng")
 
 

@@ -181,12 +181,12 @@ int sgemv_pack_layout_z4(const uint8_t* q, const uint16_t* scales_f16,
  *   zeros_f16  host uint16 [N/128][K], fp16 bit patterns of integers 0..15
  *   tile_n     power of two in [256, 1024] dividing N
  * Other arguments, ownership and errors as for sgemv_pack_layout (ESIZE
- * also for tile_n < 256).  The device calls take this version with one or
- * two rows; with 3..16 rows they return SGEMV_EUNSUPPORTED.  There the
+ * also for tile_n < 256).  Every device call takes this version.  The
  * kernels fold each column's scale into its activation (s * x rounded once
  * to fp16) and subtract the zero-point exactly, so y differs from the exact
- * product by at most 2^-11 * sum_k |w^[n][k]| |x[k]| before the final
- * rounding of y (versions 1 and 2: fp32 accumulation error only).
+ * product by at most 2^-11 * sum_k |w^[n][k]| |x[k]| plus fp32 accumulation
+ * before the final rounding of y (versions 1 and 2: fp32 accumulation
+ * error only).
  */
 int sgemv_pack_layout_ng(const uint8_t* q, const uint16_t* scales_f16,
                          const uint16_t* zeros_f16, int32_t N, int32_t K,

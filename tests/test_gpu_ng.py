@@ -1,6 +1,7 @@
 """Layout version 3 (groups along N: one scale and one zero-point per input
-column and 128 outputs) on the one- and two-row device paths: fused (with
-and without the list), over a gathered list, and every column.
+column and 128 outputs) on every device path: one and two rows (vector
+kernels) and 3..16 rows (matrix cores), fused (with and without the list),
+over a gathered list, and every column.
 
 The kernels fold each column's scale into its activation (s * x rounded
 once to fp16, relative error at most 2^-11) and keep q - z exact, so with
@@ -125,20 +126,39 @@ def test_ng_list_and_dense_paths(M):
     _check(yd, y_ref, B, f"ng dense M={M}", True)
 
 
-def test_ng_many_rows_unsupported():
-    """Three or more rows have no kernel for this layout: refused before any
-    launch, the outputs untouched."""
+@pytest.mark.parametrize("M", [3, 4, 8, 16])
+def test_ng_many_rows(M):
+    """3..16 rows on the matrix cores (k_fm): fused with the list, over the
+    gathered list (bit for bit the fused result) and every column, at
+    14336 -> 4096 with 70 % per row."""
     from activation_sparse_bit_amd import sgemv
-    K, N = 2048, 1024
-    _, pm = _matrix(2, N, K)
+    K, N = 14336, 4096
+    print(f"ng many rows M={M}", flush=True)
+    (q, s, z), pm = _matrix(0, N, K)
     dev = G.torch_dev()
-    X = np.stack([synth.plain_activation(40 + m, K) for m in range(3)])
-    y = torch.full((3, N), 5.0, dtype=torch.float32, device=dev)
-    with pytest.raises(sgemv.SgemvError) as e:
-        sgemv.sgemv_run_fused(pm.desc, pm.blob, G.to_dev(X), [0.5] * 3, y, pm.workspace)
-    assert e.value.status == sgemv.SGEMV_EUNSUPPORTED
-    with pytest.raises(sgemv.SgemvError) as e:
-        sgemv.sgemv_run_batched(pm.desc, pm.blob, G.to_dev(X), None, None, None, y, pm.workspace)
-    assert e.value.status == sgemv.SGEMV_EUNSUPPORTED
+    X = np.stack([synth.glu_activation(m, K) for m in range(M)])
+    ts = [synth.percentile_threshold(X[m], 0.7) for m in range(M)]
+    yf, idx = _fused(pm, X, ts, True)
+    y_ref, B, U = oracle.gemv_masked(q, s, z, X, ts, along="n")
+    assert np.array_equal(idx, U)
+    _check(yf, y_ref, B, f"ng fused M={M}", True)
+    xd = G.to_dev(X)
+    li = torch.zeros(K, dtype=torch.int32, device=dev)
+    lc = torch.zeros(1, dtype=torch.int32, device=dev)
+    sgemv.sgemv_gather_indices(xd, ts, li, lc)
+    yl = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    sgemv.sgemv_run_batched(pm.desc, pm.blob, xd, ts, li, lc, yl, pm.workspace)
+    yh = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    sgemv.sgemv_run_fused(pm.desc, pm.blob, xd, ts, yh, pm.workspace)
     torch.cuda.synchronize()
-    assert bool((y == 5.0).all())
+    yl = yl.cpu().numpy()
+    assert np.array_equal(yl.view(np.uint32), yf.view(np.uint32)), "list path and fused differ"
+    _check(yh.float().cpu().numpy(), y_ref, B, f"ng fused fp16 M={M}", False)
+    if M in (3, 16):
+        Xd = X[:, :2048].copy()
+        (q2, s2, z2), pm2 = _matrix(5, 1024, 2048)
+        yd = torch.full((M, 1024), float("nan"), dtype=torch.float32, device=dev)
+        sgemv.sgemv_run_batched(pm2.desc, pm2.blob, G.to_dev(Xd), None, None, None, yd, pm2.workspace)
+        torch.cuda.synchronize()
+        y_ref, B = oracle.gemv_dense(q2, s2, z2, Xd, along="n")
+        _check(yd.cpu().numpy(), y_ref, B, f"ng dense M={M}", True)
