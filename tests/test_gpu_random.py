@@ -1,6 +1,6 @@
 """Seeded random combinations through the C ABI on MI355X: every entry point
 (fused with and without the list, gather + run, a given list with and
-without thresholds, every column), both layout versions, fp16 and fp32
+without thresholds, every column), every layout version, fp16 and fp32
 outputs, 1..16 rows, K from one group to 72 groups (ragged against every
 segment size), N from one tile to eight, sparsity from dense to empty.
 Lists and counts are compared bit for bit with the oracle, y on sampled
@@ -19,6 +19,7 @@ torch = pytest.importorskip("torch")
 
 ENTRIES = ("fused_list", "fused", "split", "given_list", "every_column")
 CASES = 80
+CASES_NG = 40      # groups along N (layout version 3), seeds of their own
 
 
 def _case(i):
@@ -29,7 +30,13 @@ def _case(i):
     p = float(rng.choice([0.0, 0.25, 0.5, 0.7, 0.9, 0.97, 1.0]))
     return dict(seed=9000 + i, N=N, K=K, M=M, p=p, z4=bool(rng.integers(2)),
                 f32=bool(rng.integers(2)), gauss=bool(rng.integers(2)),
-                entry=ENTRIES[i % len(ENTRIES)], masked=bool(rng.integers(2)))
+                entry=ENTRIES[i % len(ENTRIES)], masked=bool(rng.integers(2)), ng=False)
+
+
+def _case_ng(i):
+    c = _case(500 + i)
+    c["ng"], c["z4"] = True, False
+    return c
 
 
 def _thresholds(X, p):
@@ -40,15 +47,26 @@ def _thresholds(X, p):
 
 @pytest.mark.parametrize("i", range(CASES))
 def test_random_combination(i):
+    _run(_case(i))
+
+
+@pytest.mark.parametrize("i", range(CASES_NG))
+def test_random_combination_groups_along_n(i):
+    _run(_case_ng(i))
+
+
+def _run(c):
     from activation_sparse_bit_amd import sgemv
-    c = _case(i)
     print("case", c, flush=True)
     N, K, M, dev = c["N"], c["K"], c["M"], G.torch_dev()
-    if c["gauss"]:
+    if c["ng"]:
+        q, s, z = (synth.quantized_weights_ng(c["seed"] % 7, N, K, 0.02) if c["gauss"]
+                   else synth.random_int4_problem_ng(c["seed"], N, K))
+    elif c["gauss"]:
         q, s, z = synth.quantized_weights(c["seed"] % 7, N, K, 0.02)
     else:
         q, s, z = synth.random_int4_problem(c["seed"], N, K)
-    pm = sgemv.PackedMatrix(q, s, z, device=dev, z4=c["z4"])
+    pm = sgemv.PackedMatrix(q, s, z, device=dev, z4=c["z4"], ng=c["ng"])
     X = np.stack([synth.glu_activation(c["seed"] + m, K) for m in range(M)])
     ts = _thresholds(X, c["p"])
     xd = G.to_dev(X)
@@ -96,14 +114,19 @@ def test_random_combination(i):
         assert np.array_equal(ii[:len(U)], U)
         assert np.all(ii[len(U):] == -7)
 
-    qs, ss, zs = q[rows], s[rows], z[rows]
+    # groups along N: the oracle on every row (a row's group is n // 128),
+    # then the sample; groups along K: the oracle on the sampled rows only
+    along = "n" if c["ng"] else "k"
+    qs, ss, zs = (q, s, z) if c["ng"] else (q[rows], s[rows], z[rows])
     if entry == "given_list":
         Xe = X if thr is None else np.where(oracle.active_mask(X, thr), X, np.float16(0))
-        y_ref, B = oracle.gemv_listed(qs, ss, zs, Xe, listed)
+        y_ref, B = oracle.gemv_listed(qs, ss, zs, Xe, listed, along)
     elif entry == "every_column" and thr is None:
-        y_ref, B = oracle.gemv_dense(qs, ss, zs, X)
+        y_ref, B = oracle.gemv_dense(qs, ss, zs, X, along)
     elif thr is None:    # one row over the list of its own active columns
-        y_ref, B = oracle.gemv_listed(qs, ss, zs, X, U)
+        y_ref, B = oracle.gemv_listed(qs, ss, zs, X, U, along)
     else:
-        y_ref, B, _ = oracle.gemv_masked(qs, ss, zs, X, thr)
+        y_ref, B, _ = oracle.gemv_masked(qs, ss, zs, X, thr, along)
+    if c["ng"]:
+        y_ref, B = y_ref[:, rows], B[:, rows]
     G.check_y(y.float().cpu().numpy()[:, rows], y_ref, B, str(c))
