@@ -42,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_FP16_PEAK_TFLOPS = 2500.0   # dense fp16 matrix-core peak of MI355X
 ROTATE_BYTES = 1 << 30          # other weight bytes read between two uses of one copy
 FLUSH_BYTES = 1 << 30           # scratch read before every timed replay
 STREAM_BYTES = 2 << 30          # the sequential read ceiling's buffer
@@ -375,8 +376,15 @@ def main():
         res = {"M": M, "active_union": A, "us_per_step": step_us, "run_us": run_us,
                "run_GBps": rb / (run_us * 1e-6) / 1e9}
         # the fused call: one or two rows on the vector units, 3 to 16 on the matrix cores
-        res["fused_us_per_step"] = graph_time(
+        fus = graph_time(
             [lambda i: sgemv.sgemv_run_fused(desc, copies[i % R], Xd, ts, Y, ws, idx, cnt)], steps, warmup)
+        fb = fused_bytes(A, Ag, N_DOWN, K_DOWN, M=M)
+        flops = 2.0 * M * A * N_DOWN        # one multiply-add per row, union column and output
+        res.update({"fused_us_per_step": fus, "fused_bytes": fb,
+                    "fused_GBps": fb / (fus * 1e-6) / 1e9,
+                    "fused_frac_hbm_peak": fb / (fus * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                    "fused_TFLOPs": flops / (fus * 1e-6) / 1e12,
+                    "fused_frac_fp16_mfma_peak": flops / (fus * 1e-6) / 1e12 / MFMA_FP16_PEAK_TFLOPS})
         return res
 
     def measure_layer(steps, warmup):
@@ -577,6 +585,16 @@ def main():
         for p in (0.5, 0.9):
             sweep[f"listed_read_p{int(p * 100)}"] = listed_read_ceiling(p, args.steps, args.warmup)
         dense_us = sweep["dense_int4"]["us_per_step"]
+        # time against the active fraction (1 - p): least-squares line through
+        # the 50 / 70 / 90 % steps; the intercept is the fixed cost of a step
+        dens = np.array([1 - sweep[f"fused_p{q}"]["p"] for q in (50, 70, 90)])
+        tus = np.array([sweep[f"fused_p{q}"]["us_per_step"] for q in (50, 70, 90)])
+        slope, icpt = np.polyfit(dens, tus, 1)
+        sweep["time_vs_active_fraction"] = {
+            "points": [[float(a), float(b)] for a, b in zip(dens, tus)],
+            "slope_us_per_unit": float(slope), "intercept_us": float(icpt),
+            "p90_over_p50": float(tus[2] / tus[0]), "bytes_p90_over_p50":
+                float(sweep["fused_p90"]["bytes"] / sweep["fused_p50"]["bytes"])}
         for k in ("fused_p50", "fused_p70", "fused_p90", "split_p50", "split_p70", "split_p90"):
             sweep[k]["speedup_vs_dense_int4"] = dense_us / sweep[k]["us_per_step"]
         for M in (1, 2, 4, 8, 16):
