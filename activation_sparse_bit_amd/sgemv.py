@@ -424,11 +424,14 @@ class PackedMatrix:
         self.N, self.K = self.desc.N, self.desc.K
 
     @classmethod
-    def from_parts(cls, parts, device="cuda", max_batch: int = SGEMV_MAX_BATCH, z4: bool = False):
+    def from_parts(cls, parts, device="cuda", max_batch: int = SGEMV_MAX_BATCH, z4: bool = False,
+                   ng: bool = False):
         """Several projections sharing their input as one matrix (rows
-        stacked in order), packed by sgemv_pack_layout_parts."""
-        packed = sgemv_pack_layout_parts(parts, version=SGEMV_LAYOUT_Z4 if z4 else SGEMV_LAYOUT_PAIRS)
-        return cls(None, None, None, device=device, max_batch=max_batch, z4=z4, _packed=packed)
+        stacked in order), packed by sgemv_pack_layout_parts (ng: parts
+        quantized with groups along N, layout version 3)."""
+        version = SGEMV_LAYOUT_NG if ng else SGEMV_LAYOUT_Z4 if z4 else SGEMV_LAYOUT_PAIRS
+        packed = sgemv_pack_layout_parts(parts, version=version)
+        return cls(None, None, None, device=device, max_batch=max_batch, z4=z4, _packed=packed, ng=ng)
 
 
 class FusedProjections:
@@ -439,7 +442,7 @@ class FusedProjections:
     tile belongs to one projection.  `split(y)` returns the per-projection
     views of the concatenated output."""
 
-    def __init__(self, parts, device="cuda", max_batch: int = 2, z4: bool = False):
+    def __init__(self, parts, device="cuda", max_batch: int = 2, z4: bool = False, ng: bool = False):
         names = [p[0] for p in parts]
         if len(set(names)) != len(names):
             raise ValueError("projection names must be unique")
@@ -454,7 +457,8 @@ class FusedProjections:
                 raise ValueError(f"{name}: N = {n} is not a multiple of {SGEMV_TILE_N}")
             self.offsets[name] = (start, n)
             start += n
-        self.matrix = PackedMatrix.from_parts([p[1:] for p in parts], device=device, max_batch=max_batch, z4=z4)
+        self.matrix = PackedMatrix.from_parts([p[1:] for p in parts], device=device, max_batch=max_batch, z4=z4,
+                                              ng=ng)
         self.N, self.K = self.matrix.N, self.matrix.K
 
     def split(self, y):
