@@ -60,7 +60,7 @@ struct Codes {
 
 struct RunArgs {
     const uint8_t* w;        // weight region of the blob
-    const uint8_t* md;       // metadata region (layout version 1 or 2)
+    const uint8_t* md;       // metadata region (layout version 1, 2 or 3)
     uint32_t md_z4;          // version 2: fp16 scales, then 4-bit zero-points
     const uint16_t* x;       // fp16 bits [M][ldx]
     void* y;
@@ -373,15 +373,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // (kTileN * 5 / 2 bytes).  md_raw4 loads the 16 bytes per lane of outputs
 // o .. o + 3 (o a multiple of 4) and md_cook4 turns them into the version-1
 // words (s bits | z bits << 16) either way, so the kernels after it are the
-// same for both.
+// same for both.  (Version 3, groups along the outputs, has per-column
+// metadata and its own loads: fs_block_ng, fs_dense_ng and k_fm<3>.)
 struct MdHalf {
     const uint8_t* tile;   // the tile's metadata (group 0)
     uint32_t h;            // which half of the tile
     uint32_t z4;           // version 2
 };
 
-// The version is a template parameter of every kernel: the handle's z4 is
-// then a constant, and the branches below fold away after inlining.
+// The layout version is a template parameter of every kernel: the handle's
+// z4 is then a constant, and the branches below fold away after inlining.
 template <bool Z4>
 __device__ __forceinline__ MdHalf md_half(const RunArgs& a, int t, int h) {
     const size_t run = Z4 ? (size_t)kTileN * 5 / 2 : (size_t)kTileN * 4;   // bytes per group
