@@ -118,3 +118,24 @@ def test_static_scratch_refuses_sizes_beyond_the_array():
     # the same matrix with two rows fits the array; argument checks still apply
     r = L.sgemv_run_fused_static(ctypes.byref(d), FAKE, FAKE, 2, K, None, None, None, FAKE, N, 0, None)
     assert r == sgemv.SGEMV_EINVAL      # thresholds are required
+
+
+@pytest.mark.gpu
+def test_static_scratch_groups_along_n():
+    """Layout version 3 through both entry points: four rows (matrix cores)
+    then one row (vector kernel), bit for bit the workspace call, within the
+    bar of the groups-along-N oracle."""
+    from activation_sparse_bit_amd import sgemv
+    K, N = 4096, 4096
+    q, s, z = synth.quantized_weights_ng(1, N, K, 0.02)
+    pm = sgemv.PackedMatrix(q, s, z, device=G.torch_dev(), ng=True)
+    for M, p in ((4, 0.7), (1, 0.5)):
+        X = np.stack([synth.plain_activation(50 + m, K) for m in range(M)])
+        ts = [synth.percentile_threshold(X[m], p) for m in range(M)]
+        print(f"static scratch: groups along N, {M} rows", flush=True)
+        yw, iw, cw, ys, is_, cs = _both(pm, X, ts, torch.float32)
+        U = oracle.active_indices(X, ts)
+        assert cw == cs == len(U) and np.array_equal(is_[:cs], U) and np.array_equal(is_, iw)
+        assert np.array_equal(ys.view(np.uint32), yw.view(np.uint32)), "static and workspace outputs differ"
+        y_ref, B, _ = oracle.gemv_masked(q, s, z, X, ts, along="n")
+        G.check_y(ys.astype(np.float64), y_ref, B, f"static ng M={M}")
