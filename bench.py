@@ -385,6 +385,18 @@ def main():
                     "fused_frac_hbm_peak": fb / (fus * 1e-6) / 1e9 / HBM_PEAK_GBPS,
                     "fused_TFLOPs": flops / (fus * 1e-6) / 1e12,
                     "fused_frac_fp16_mfma_peak": flops / (fus * 1e-6) / 1e12 / MFMA_FP16_PEAK_TFLOPS})
+        if M == 16:   # the same call on the groups-along-N layout (version 3)
+            q3, s3, z3 = synth.quantized_weights_ng(0, N_DOWN, K_DOWN, 0.02)
+            d3, b3 = sgemv.sgemv_pack_layout_ng(q3, s3, z3)
+            R3 = rotation(fused_bytes(A, Ag, N_DOWN, K_DOWN, M=M, ng=True))
+            bd = torch.from_numpy(b3).to(dev)
+            c3 = [bd] + [bd.clone() for _ in range(R3 - 1)]
+            f3 = graph_time([lambda i: sgemv.sgemv_run_fused(d3, c3[i % R3], Xd, ts, Y, ws, idx, cnt)],
+                            steps, warmup)
+            fb3 = fused_bytes(A, Ag, N_DOWN, K_DOWN, M=M, ng=True)
+            res.update({"fused_ng_us_per_step": f3, "fused_ng_bytes": fb3,
+                        "fused_ng_frac_hbm_peak": fb3 / (f3 * 1e-6) / 1e9 / HBM_PEAK_GBPS})
+            del c3, bd
         return res
 
     def measure_layer(steps, warmup):
