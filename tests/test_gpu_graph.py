@@ -149,3 +149,47 @@ def test_calls_on_a_side_stream_match_the_default_stream():
     got = run(side)
     for a, b in zip(got, ref):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_graph_replays_groups_along_n(M):
+    """Layout version 3 in a captured graph: one row (vector kernel) and four
+    rows (matrix cores, with the list workgroups), replays bitwise equal to
+    the eager call, with an eager call on other inputs between replays."""
+    from activation_sparse_bit_amd import sgemv
+    K, N = 14336, 4096
+    q, s, z = synth.quantized_weights_ng(0, N, K, 0.02)
+    pm = sgemv.PackedMatrix(q, s, z, device=G.torch_dev(), ng=True)
+    dev = G.torch_dev()
+    X1 = np.stack([synth.glu_activation(m, K) for m in range(M)])
+    X2 = np.stack([synth.glu_activation(10 + m, K) for m in range(M)])
+    t1 = [synth.percentile_threshold(X1[m], 0.5) for m in range(M)]
+    t2 = [synth.percentile_threshold(X2[m], 0.8) for m in range(M)]
+    x1, x2 = (G.to_dev(X1), G.to_dev(X2)) if M > 1 else (G.to_dev(X1[0]), G.to_dev(X2[0]))
+    idx = torch.zeros(K, dtype=torch.int32, device=dev)
+    cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+    y = torch.zeros((M, N) if M > 1 else (N,), dtype=torch.float32, device=dev)
+
+    def step(x, t):
+        sgemv.sgemv_run_fused(pm.desc, pm.blob, x, t, y, pm.workspace, idx, cnt)
+
+    def snap():
+        torch.cuda.synchronize()
+        return y.cpu().numpy().view(np.uint32).copy(), idx.cpu().numpy().copy(), int(cnt.item())
+
+    step(x1, t1)
+    ref = snap()
+    step(x2, t2)
+    other = snap()
+    assert not np.array_equal(ref[0], other[0])
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step(x1, t1)
+    for rep in range(4):
+        g.replay()
+        for a, b in zip(snap(), ref):
+            assert np.array_equal(a, b), f"replay {rep}"
+        step(x2, t2)
+        for a, b in zip(snap(), other):
+            assert np.array_equal(a, b), f"eager after replay {rep}"
