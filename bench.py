@@ -385,6 +385,11 @@ def main():
                     "fused_frac_hbm_peak": fb / (fus * 1e-6) / 1e9 / HBM_PEAK_GBPS,
                     "fused_TFLOPs": flops / (fus * 1e-6) / 1e12,
                     "fused_frac_fp16_mfma_peak": flops / (fus * 1e-6) / 1e12 / MFMA_FP16_PEAK_TFLOPS})
+        if M >= 3:    # the union's weight runs read alone, with the one-row grid
+            lst = idx[:A].cpu().numpy().astype(np.int32)
+            lus = listed_read_us(lst, K_DOWN, N_DOWN, copies, R, desc.w_off, steps, warmup)
+            res.update({"union_listed_read_us": lus,
+                        "union_listed_read_frac_hbm_peak": (A * N_DOWN // 2) / (lus * 1e-6) / 1e9 / HBM_PEAK_GBPS})
         if M == 16:   # the same call on the groups-along-N layout (version 3)
             q3, s3, z3 = synth.quantized_weights_ng(0, N_DOWN, K_DOWN, 0.02)
             d3, b3 = sgemv.sgemv_pack_layout_ng(q3, s3, z3)
@@ -496,6 +501,18 @@ def main():
                              "frac_hbm_peak": db / (dus * 1e-6) / 1e9 / HBM_PEAK_GBPS}
         for pp in ps:
             res[f"fused_p{int(pp * 100)}"]["speedup_vs_dense_int4"] = dus / res[f"fused_p{int(pp * 100)}"]["us_per_step"]
+        # each call's own ceiling: the same weight runs read and nothing else
+        for pp in ps + (0.0,):
+            if pp > 0.0:
+                t = synth.percentile_threshold(xv, pp)
+                lst = np.flatnonzero(np.abs(xv.astype(np.float32)) >= np.float32(t)).astype(np.int32)
+                r = res[f"fused_p{int(pp * 100)}"]
+            else:
+                lst, r = np.arange(K, dtype=np.int32), res["dense_int4"]
+            lus = listed_read_us(lst, K, N, cps, RR, dsc.w_off, steps, warmup)
+            r["listed_read_us"] = lus
+            r["listed_read_frac_hbm_peak"] = (len(lst) * N // 2) / (lus * 1e-6) / 1e9 / HBM_PEAK_GBPS
+            r["listed_read_over_call"] = lus / r["us_per_step"]
         del cps, bd
         torch.cuda.empty_cache()
         return res
@@ -534,27 +551,34 @@ def main():
         return {"GBps": STREAM_BYTES / best / 1e9, "bytes": STREAM_BYTES, "us": best * 1e6,
                 "kernel": "sequential 16-byte non-temporal loads, 4096 x 512 threads, best of %d" % reps}
 
-    def listed_read_ceiling(p, steps, warmup):
-        """The step's weight reads alone: for every half tile the 128-byte run
-        of each column in the step's list, with the GEMV's lanes and grid, no
-        activations, scales, arithmetic or sums (measurement-only kernel),
-        graph-timed over the same rotated copies as the step."""
+    def listed_read_us(lst, K, N, cps, RR, w_off, steps, warmup):
+        """Graph-timed microseconds per launch of the weight reads alone of a
+        one-row call over the ascending list `lst`: for every half tile the
+        128-byte run of each listed column, with the GEMV's lanes and grid of
+        half tiles x 1024-column segments, and no activations, scales,
+        arithmetic or sums (measurement-only kernel), over the same rotated
+        copies `cps` as the call it bounds."""
         import ctypes
         bl = ctypes.CDLL(os.path.join(ROOT, "activation_sparse_bit_amd", "lib", "libsgemv_bench.so"))
         bl.sgemv_bench_listed_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
-        t = synth.percentile_threshold(x, p)
-        lst = np.flatnonzero(np.abs(x.astype(np.float32)) >= np.float32(t)).astype(np.int32)
-        starts = np.searchsorted(lst, np.arange(0, K_DOWN + 1, 128)).astype(np.int32)
-        ld, sd = torch.from_numpy(lst).to(dev), torch.from_numpy(starts).to(dev)
+        starts = np.searchsorted(lst, np.arange(0, K + 1, 128)).astype(np.int32)
+        ld = torch.from_numpy(np.ascontiguousarray(lst, dtype=np.int32)).to(dev)
+        sd = torch.from_numpy(starts).to(dev)
         sink = torch.zeros(1024, dtype=torch.int32, device=dev)
 
         def f(i):
             st = torch.cuda.current_stream().cuda_stream
-            if bl.sgemv_bench_listed_read(copies[i % R].data_ptr() + desc.w_off, sd.data_ptr(), ld.data_ptr(),
-                                          K_DOWN, N_DOWN, sink.data_ptr(), st) != 0:
+            if bl.sgemv_bench_listed_read(cps[i % RR].data_ptr() + w_off, sd.data_ptr(), ld.data_ptr(),
+                                          K, N, sink.data_ptr(), st) != 0:
                 raise RuntimeError("sgemv_bench_listed_read failed")
-        us = graph_time([f], steps, warmup)
+        return graph_time([f], steps, warmup)
+
+    def listed_read_ceiling(p, steps, warmup):
+        """The step's weight reads alone (see listed_read_us)."""
+        t = synth.percentile_threshold(x, p)
+        lst = np.flatnonzero(np.abs(x.astype(np.float32)) >= np.float32(t)).astype(np.int32)
+        us = listed_read_us(lst, K_DOWN, N_DOWN, copies, R, desc.w_off, steps, warmup)
         wb = len(lst) * N_DOWN // 2
         return {"p": p, "active": int(len(lst)), "us_per_launch": us, "weight_bytes": wb,
                 "GBps": wb / (us * 1e-6) / 1e9}
