@@ -100,16 +100,6 @@ __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast
 // ---------------------------------------------------------------------------
 // index gathering
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t mask8_of(uint4 v, uint32_t code) {
-    uint32_t m = 0;
-    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m |= (uint32_t)is_active(wv[i] & 0xFFFFu, code) << (2 * i);
-        m |= (uint32_t)is_active(wv[i] >> 16, code) << (2 * i + 1);
-    }
-    return m;
-}
 
 // Exclusive prefix (over lower lanes) and wave total of a per-lane count in
 // 0..15, from four bit-plane ballots.
@@ -138,11 +128,19 @@ struct GatherShared {
 
 // Union over rows 0..M-1 of the 8-column masks at column col: the rows are
 // loaded RB at a time, all in flight together (rows past M repeat row M - 1,
-// whose mask is already in).
+// whose mask is already in).  Two fp16 values per 32-bit word, decided in
+// packed 16-bit arithmetic: with mag = bits & 0x7FFF, a value is inactive
+// for its row's code c exactly when mag - c or 0x7C00 - mag is negative as a
+// signed 16-bit number (mag < c, or a NaN; both differences lie in
+// [-0x7C00, 0x7FFF]), that is the is_active rule; the sign bits are ANDed
+// over the rows, and a column is in the union when its bit ends clear.
+typedef short s2_t __attribute__((ext_vector_type(2)));
+
 template <int RB>
 __device__ __forceinline__ uint32_t union_mask8(const uint16_t* __restrict__ x, int M, int ldx, int col,
                                                 const Codes& tc) {
-    uint32_t m8 = 0;
+    uint32_t none[4] = {~0u, ~0u, ~0u, ~0u};   // bits 15 and 31: inactive in every row so far
+    const s2_t kInf = __builtin_bit_cast(s2_t, 0x7C007C00u);
     for (int m0 = 0; m0 < M; m0 += RB) {
         uint4 v[RB];
 #pragma unroll
@@ -153,10 +151,20 @@ __device__ __forceinline__ uint32_t union_mask8(const uint16_t* __restrict__ x, 
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             const int mr = m0 + r < M ? m0 + r : M - 1;
-            m8 |= mask8_of(v[r], code_of(tc, mr));
+            const uint32_t c = code_of(tc, mr);
+            const s2_t c2 = __builtin_bit_cast(s2_t, c | (c << 16));
+            const uint32_t wv[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const s2_t mag = __builtin_bit_cast(s2_t, wv[i] & 0x7FFF7FFFu);
+                none[i] &= __builtin_bit_cast(uint32_t, mag - c2) | __builtin_bit_cast(uint32_t, kInf - mag);
+            }
         }
     }
-    return m8;
+    uint32_t m8 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m8 |= (((none[i] >> 15) & 1u) | ((none[i] >> 30) & 2u)) << (2 * i);
+    return ~m8 & 0xFFu;
 }
 
 // Wavefronts W and above of the workgroup only join the barrier.  The
