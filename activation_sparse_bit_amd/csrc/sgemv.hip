@@ -12,9 +12,10 @@
 //   k_gather   the standalone gathering step: a few workgroups, each over
 //              its own column range, with no scratch and no communication
 //              (each recounts the active columns below its range from x);
-//              per-lane 8-element masks from 16-byte loads, bit-plane
-//              ballots and mbcnt for in-wave ranks, an LDS scan across the
-//              wavefronts, ordered index writes.
+//              per-lane 8-element masks from 16-byte loads (two entries per
+//              packed 16-bit instruction), bit-plane ballots and mbcnt for
+//              in-wave ranks, an LDS scan across the wavefronts, ordered
+//              index writes.
 //   k_fs, k_fs4  one or two rows, fused: threshold, compaction and GEMV in
 //              one launch, one quantization group per wavefront, 8 or (one
 //              row, small or short-K matrices) 4 wavefronts per workgroup

@@ -231,6 +231,23 @@ def test_fused_batched_ragged(K, N):
     G.check_y(y, y_ref, B, f"fused M=7 {K}x{N}")
 
 
+@pytest.mark.parametrize("M,K,p", [(16, 65536, 0.9), (5, 40960, 0.6), (3, 65536, 0.999)])
+def test_fused_batched_long_rows(M, K, p):
+    """Long rows: the list is built by the most list workgroups (8 ranges of
+    up to 8192 columns, joined by the last to finish) while the matrix-core
+    workgroups compute; list bit-exact, every output within the bar."""
+    from activation_sparse_bit_amd import sgemv
+    N = 512
+    q, s, z = synth.random_int4_problem(K + M, N, K)
+    pm = sgemv.PackedMatrix(q, s, z, device=G.torch_dev())
+    X = np.stack([synth.glu_activation(30 + m, K) for m in range(M)])
+    ts = [synth.percentile_threshold(X[m], p) for m in range(M)]
+    y, idx, c = _fused(pm, X, ts)
+    _check_list(idx, c, X, ts)
+    y_ref, B, _ = oracle.gemv_masked(q, s, z, X, ts)
+    G.check_y(y, y_ref, B, f"fused M={M} K={K} p={p}")
+
+
 def test_fused_batched_dense_fp32_and_empty():
     K, N = 4096, 4096
     q, s, z = G.weights(1, N, K, 0.02)
