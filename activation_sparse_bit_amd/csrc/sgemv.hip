@@ -1653,31 +1653,40 @@ __global__ __launch_bounds__(fm::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     if (last_flag == 0u) return;
     if (last_flag == 1u) acquire_slices();
 
-    // last to arrive: thread t adds row t / 32, storage 8 (t % 32) .. + 7 of
-    // every slot, in segment order, 16 slots in flight (past the CU's L1)
-    const int om = t >> 5, os = 8 * (t & 31);
-    if (om < a.M) {
-        const uint32_t my = ((uint32_t)om * kVTile + os) * 4u;
-        float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // last to arrive: a slot's M x 256 sums are M KiB; thread t adds its
+    // 16-byte pieces t and t + 512 (row c / 64, storage 4 (c % 64) .. + 3 for
+    // piece c) of every slot, in segment order, 16 slots in flight (past the
+    // CU's L1).  Each load instruction reads 1 KiB of a slot contiguously,
+    // so no line is fetched from L2 twice.
+    const int np = a.M * (kVTile / 4);   // pieces per slot
+    const int c1 = t, c2 = t + fm::kWaves * 64;
+    const bool h1 = c1 < np, h2 = c2 < np;
+    float tot1[4] = {0.f, 0.f, 0.f, 0.f}, tot2[4] = {0.f, 0.f, 0.f, 0.f};
+    if (h1) {
         for (int sb = 0; sb < S; sb += 16) {
             u32x4 u[16][2];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int sl = sb + i < S ? sb + i : sb;
-                const uint32_t off = tile_base + (uint32_t)sl * slot_bytes + my;
-                u[i][0] = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, kCacheSC0);
-                u[i][1] = __builtin_amdgcn_raw_buffer_load_b128(prs, off + 16u, 0, kCacheSC0);
+                const uint32_t off = tile_base + (uint32_t)sl * slot_bytes;
+                u[i][0] = __builtin_amdgcn_raw_buffer_load_b128(prs, off + (uint32_t)c1 * 16u, 0, kCacheSC0);
+                u[i][1] = h2 ? __builtin_amdgcn_raw_buffer_load_b128(prs, off + (uint32_t)c2 * 16u, 0, kCacheSC0)
+                             : (u32x4){0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 if (sb + i < S) {
-                    tot[0] += u2f(u[i][0].x); tot[1] += u2f(u[i][0].y); tot[2] += u2f(u[i][0].z); tot[3] += u2f(u[i][0].w);
-                    tot[4] += u2f(u[i][1].x); tot[5] += u2f(u[i][1].y); tot[6] += u2f(u[i][1].z); tot[7] += u2f(u[i][1].w);
+                    tot1[0] += u2f(u[i][0].x); tot1[1] += u2f(u[i][0].y); tot1[2] += u2f(u[i][0].z); tot1[3] += u2f(u[i][0].w);
+                    tot2[0] += u2f(u[i][1].x); tot2[1] += u2f(u[i][1].y); tot2[2] += u2f(u[i][1].z); tot2[3] += u2f(u[i][1].w);
                 }
             }
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) put_y(om, os + j, tot[j]);
+        for (int j = 0; j < 4; ++j) put_y(c1 / 64, 4 * (c1 % 64) + j, tot1[j]);
+        if (h2) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) put_y(c2 / 64, 4 * (c2 % 64) + j, tot2[j]);
+        }
     }
     if (t == 0) reset_arrivals(a.counters, vt);
 }
