@@ -162,6 +162,22 @@ def test_run_mlp_70b_sampled(K, N, glu, p):
     G.check_y(y[rows][None, :], y_ref, B, f"70b {K}->{N} p={p}")
 
 
+@pytest.mark.parametrize("K,N,glu", [(8192, 28672, False), (28672, 8192, True)])
+def test_run_mlp_70b_dense_sampled(K, N, glu):
+    """Every column (no list, no threshold) at the full 70B shapes, the
+    multi-round grids of the dense GEMV: sampled rows within the bar, and
+    with fp32 output only fp32 accumulation error."""
+    q, s, z = G.weights(2, N, K, 0.015)
+    x = synth.glu_activation(0, K) if glu else synth.plain_activation(0, K)
+    rows = G.sample_rows(N, 384)
+    y_ref, B = oracle.gemv_dense(q[rows], s[rows], z[rows], x)
+    y, _ = _run_single(2, N, K, 0.015, x, 0.0, dense=True)
+    G.check_y(y[rows][None, :], y_ref, B, f"70b dense {K}->{N}")
+    y32, _ = _run_single(2, N, K, 0.015, x, 0.0, dtype=torch.float32, dense=True)
+    rel = G.check_y(y32[rows][None, :], y_ref, B, f"70b dense fp32 {K}->{N}")
+    assert rel < 2e-6
+
+
 @pytest.mark.parametrize("K,N", [(128, 512), (384, 1536), (1152, 512), (2176, 2560)])
 def test_run_ragged_shapes(K, N):
     """K not a multiple of the 1024- (or 512-) column workgroup segment, tiny K, several tiles."""
